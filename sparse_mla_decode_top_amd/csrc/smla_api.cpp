@@ -1,0 +1,155 @@
+// C ABI of the split-KV sparse MLA decode library: argument checks, the split
+// count heuristic and the launch sequence.  The kernels live in
+// smla_kernels.hip.  Nothing here allocates memory or synchronises.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "smla.h"
+#include "smla_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t n_blocks_of(int32_t topk) { return (topk + SMLA_SPLIT_BLOCK - 1) / SMLA_SPLIT_BLOCK; }
+
+// Checks shared by both entry points: the shape fields that the combine uses.
+smla_status check_common_shape(const smla_params* p, int32_t num_splits) {
+  if (p == nullptr) return SMLA_ERR_INVALID_ARG;
+  if (p->s_q < 1 || p->s_q > (1 << 22)) return p->s_q < 1 ? SMLA_ERR_INVALID_ARG : SMLA_ERR_UNSUPPORTED;
+  if (p->h_q != 16 && p->h_q != 32 && p->h_q != 64) return SMLA_ERR_UNSUPPORTED;
+  if (num_splits < 1) return SMLA_ERR_INVALID_ARG;
+  if (num_splits > SMLA_MAX_SPLITS) return SMLA_ERR_UNSUPPORTED;
+  if ((int64_t)p->s_q * num_splits > INT32_MAX) return SMLA_ERR_UNSUPPORTED;
+  if (p->out_dtype != SMLA_OUT_BF16 && p->out_dtype != SMLA_OUT_FP32 && p->out_dtype != SMLA_OUT_FP8_E4M3)
+    return SMLA_ERR_INVALID_ARG;
+  return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* smla_status_string(smla_status s) {
+  switch (s) {
+    case SMLA_OK: return "SMLA_OK";
+    case SMLA_ERR_INVALID_ARG: return "SMLA_ERR_INVALID_ARG";
+    case SMLA_ERR_UNSUPPORTED: return "SMLA_ERR_UNSUPPORTED";
+    case SMLA_ERR_MISSING_WORKSPACE: return "SMLA_ERR_MISSING_WORKSPACE";
+    case SMLA_ERR_MISALIGNED: return "SMLA_ERR_MISALIGNED";
+    case SMLA_ERR_HIP: return "SMLA_ERR_HIP";
+  }
+  return "SMLA_ERR_UNKNOWN";
+}
+
+size_t smla_partial_bytes(int32_t s_q, int32_t h_q, int32_t num_splits) {
+  if (s_q < 1 || h_q < 1 || num_splits < 1) return 0;
+  return (size_t)num_splits * (size_t)s_q * (size_t)h_q * (size_t)(SMLA_D_V * 4 + 4);
+}
+
+int32_t smla_choose_num_splits(int32_t s_q, int32_t h_q, int32_t topk, int32_t num_cus) {
+  if (s_q < 1 || h_q < 1 || topk < 1 || num_cus < 1) return 0;
+  const int32_t n_blk = n_blocks_of(topk);
+  // Enough (token, split) jobs for one workgroup per compute unit; batches
+  // that already give at least half the compute units a token stay unsplit,
+  // since the partials would add traffic there without adding parallelism.
+  if (2 * (int64_t)s_q >= num_cus) return 1;
+  int32_t s = (num_cus + s_q - 1) / s_q;
+  if (s > n_blk) s = n_blk;
+  if (s > SMLA_MAX_SPLITS) s = SMLA_MAX_SPLITS;
+  return s < 1 ? 1 : s;
+}
+
+smla_status smla_validate(const smla_params* p, const void* q, const void* kv_pool, const float* kv_scale,
+                          const int32_t* indices, int32_t num_splits, const float* o_accum,
+                          const float* lse_accum, const void* out, const float* out_scale) {
+  smla_status st = check_common_shape(p, num_splits);
+  if (st != SMLA_OK) return st;
+  if (p->topk < 1 || p->n_pool < 1) return SMLA_ERR_INVALID_ARG;
+  if (p->split_block != SMLA_SPLIT_BLOCK) return SMLA_ERR_UNSUPPORTED;
+  if (p->kv_dtype != SMLA_KV_BF16 && p->kv_dtype != SMLA_KV_FP8_E4M3) return SMLA_ERR_INVALID_ARG;
+  if (!isfinite(p->softmax_scale)) return SMLA_ERR_INVALID_ARG;
+  if (p->kv_row_stride < SMLA_D_QK) return SMLA_ERR_INVALID_ARG;
+  const int64_t elem = p->kv_dtype == SMLA_KV_BF16 ? 2 : 1;
+  if (p->kv_row_stride > (INT64_MAX / 4) / elem) return SMLA_ERR_UNSUPPORTED;
+  if ((p->kv_row_stride * elem) % 16 != 0) return SMLA_ERR_MISALIGNED;
+  if (q == nullptr || kv_pool == nullptr || indices == nullptr) return SMLA_ERR_INVALID_ARG;
+  if (p->kv_dtype == SMLA_KV_FP8_E4M3 && kv_scale == nullptr) return SMLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_pool)) return SMLA_ERR_MISALIGNED;
+  if ((reinterpret_cast<uintptr_t>(indices) & 3u) != 0) return SMLA_ERR_MISALIGNED;
+  if (kv_scale != nullptr && (reinterpret_cast<uintptr_t>(kv_scale) & 3u) != 0) return SMLA_ERR_MISALIGNED;
+  const bool has_o = o_accum != nullptr, has_l = lse_accum != nullptr;
+  if (has_o != has_l) return SMLA_ERR_MISSING_WORKSPACE;
+  if (num_splits > 1 && !has_o) return SMLA_ERR_MISSING_WORKSPACE;
+  if (!has_o && out == nullptr) return SMLA_ERR_INVALID_ARG;     // direct path needs an output
+  if (has_o && !aligned16(o_accum)) return SMLA_ERR_MISALIGNED;
+  if (has_l && (reinterpret_cast<uintptr_t>(lse_accum) & 3u) != 0) return SMLA_ERR_MISALIGNED;
+  if (out != nullptr) {
+    if (!aligned16(out)) return SMLA_ERR_MISALIGNED;
+    if (p->out_dtype == SMLA_OUT_FP8_E4M3 && out_scale == nullptr) return SMLA_ERR_INVALID_ARG;
+  }
+  return SMLA_OK;
+}
+
+smla_status combine_splits(const smla_params* p, int32_t num_splits, const float* o_accum,
+                           const float* lse_accum, const float* sink, void* out, float* out_scale,
+                           float* lse_out, void* stream) {
+  smla_status st = check_common_shape(p, num_splits);
+  if (st != SMLA_OK) return st;
+  if (o_accum == nullptr || lse_accum == nullptr) return SMLA_ERR_MISSING_WORKSPACE;
+  if (out == nullptr) return SMLA_ERR_INVALID_ARG;
+  if (p->out_dtype == SMLA_OUT_FP8_E4M3 && out_scale == nullptr) return SMLA_ERR_INVALID_ARG;
+  if (!aligned16(o_accum) || !aligned16(out)) return SMLA_ERR_MISALIGNED;
+  if ((reinterpret_cast<uintptr_t>(lse_accum) & 3u) != 0) return SMLA_ERR_MISALIGNED;
+  smla::CombineArgs a;
+  a.o_accum = o_accum;
+  a.lse_accum = lse_accum;
+  a.sink = sink;
+  a.out = out;
+  a.out_scale = out_scale;
+  a.lse_out = lse_out;
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.num_splits = num_splits;
+  a.out_dtype = p->out_dtype;
+  return smla::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
+smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* kv_pool, const float* kv_scale,
+                              const int32_t* indices, int32_t num_splits, const float* sink, float* o_accum,
+                              float* lse_accum, void* out, float* out_scale, float* lse_out, void* stream) {
+  smla_status st = smla_validate(p, q, kv_pool, kv_scale, indices, num_splits, o_accum, lse_accum, out, out_scale);
+  if (st != SMLA_OK) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool fp8 = p->kv_dtype == SMLA_KV_FP8_E4M3;
+  smla::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv_pool);
+  a.kv_scale = kv_scale;
+  a.indices = indices;
+  a.sink = sink;
+  a.o_accum = o_accum;
+  a.lse_accum = lse_accum;
+  a.out = out;
+  a.out_scale = out_scale;
+  a.lse_out = lse_out;
+  a.n_pool = p->n_pool;
+  a.row_stride_bytes = p->kv_row_stride * (fp8 ? 1 : 2);
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.topk = p->topk;
+  a.num_splits = num_splits;
+  a.n_blocks = n_blocks_of(p->topk);
+  a.out_dtype = p->out_dtype;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+
+  if (o_accum == nullptr) {        // direct path: one job per token, fused epilogue
+    return smla::launch_decode_direct(a, fp8, hs) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+  }
+  if (smla::launch_decode_partial(a, fp8, hs) != hipSuccess) return SMLA_ERR_HIP;
+  if (out == nullptr) return SMLA_OK;   // partial-only: the caller combines
+  return combine_splits(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream);
+}
+
+}  // extern "C"

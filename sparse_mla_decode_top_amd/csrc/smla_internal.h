@@ -1,0 +1,45 @@
+// Internal interface between the C-ABI layer (smla_api.cpp) and the HIP
+// kernels (smla_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+// Everything one launch of the attention kernel needs.  Device pointers only.
+struct DecodeArgs {
+  const uint16_t* q;          // [s_q][h_q][576] bf16 bits
+  const uint8_t* kv;          // pool base address (bytes)
+  const float* kv_scale;      // [n_pool] (FP8 pool) or nullptr
+  const int32_t* indices;     // [s_q][topk]
+  const float* sink;          // [h_q] or nullptr
+  float* o_accum;             // [S][s_q][h_q][512]   (partial mode)
+  float* lse_accum;           // [S][s_q][h_q]        (partial mode)
+  void* out;                  // [s_q][h_q][512]      (direct mode)
+  float* out_scale;           // [s_q]                (direct mode, FP8 out)
+  float* lse_out;             // [s_q][h_q] or nullptr (direct mode)
+  int64_t n_pool;
+  int64_t row_stride_bytes;
+  int32_t s_q, h_q, topk, num_splits, n_blocks;
+  int32_t out_dtype;          // smla_out_dtype (direct mode)
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* o_accum;
+  const float* lse_accum;
+  const float* sink;
+  void* out;
+  float* out_scale;
+  float* lse_out;
+  int32_t s_q, h_q, num_splits;
+  int32_t out_dtype;
+};
+
+// Each returns the launch status (hipSuccess or the runtime's error).
+hipError_t launch_decode_partial(const DecodeArgs& a, bool kv_fp8, hipStream_t stream);
+hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,135 @@
+"""Shared helpers of the GPU parity tests: upload seeded inputs, call the
+library through its binding, and evaluate the float64 oracle on the same
+inputs (the oracle only ever sees generator output, never GPU results)."""
+import functools
+
+import numpy as np
+
+import oracle
+from sparse_mla_decode_top_amd import workloads as W
+
+TOL_O = 2e-3          # max-abs on O for bf16 inputs
+TOL_LSE = 1e-5        # max-abs on the log2 LSE
+TOL_SPLIT = 1e-5      # combined fp32 O between split counts
+
+
+class Bf16PoolView:
+    """Row-indexable float32 view of a bf16 pool that converts only the rows asked for."""
+
+    def __init__(self, bits):
+        self.bits = bits
+
+    def __getitem__(self, rows):
+        return W.bf16_bits_to_f32(self.bits[rows])
+
+
+def oracle_pool(inp):
+    if inp.kv_dtype == "bf16":
+        return Bf16PoolView(inp.kv_bits)
+    return oracle.Fp8Pool(inp.kv_codes, inp.kv_scale)
+
+
+@functools.lru_cache(maxsize=4)
+def inputs_for(name, seed):
+    return W.make_workload_inputs(W.WORKLOADS[name], seed)
+
+
+@functools.lru_cache(maxsize=8)
+def oracle_direct(name, seed):
+    """(O without sink, LSE) of every token by the plain definition."""
+    inp = inputs_for(name, seed)
+    return oracle.attend(inp.q.astype(np.float64), oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+
+
+def oracle_final(inp, O, lse):
+    return oracle.apply_sink(O, lse, None if inp.sink is None else inp.sink.astype(np.float64))
+
+
+class DeviceInputs:
+    def __init__(self, inp, device="cuda"):
+        import torch
+        self.inp = inp
+        self.q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(device)
+        if inp.kv_dtype == "bf16":
+            self.kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(device)
+            self.kv_scale = None
+        else:
+            self.kv = torch.from_numpy(inp.kv_codes).to(device)
+            self.kv_scale = torch.from_numpy(inp.kv_scale).to(device)
+        self.indices = torch.from_numpy(inp.indices).to(device)
+        self.sink = None if inp.sink is None else torch.from_numpy(inp.sink).to(device)
+
+
+def run(dev, num_splits, out_dtype="f32", path="split", use_sink=True, want_lse=True, indices=None,
+        kv=None):
+    """One decode through the C ABI.  path: "split" (partials + combine), "direct"
+    (S = 1, fused epilogue) or "partial" (partials only).  Buffers start poisoned
+    (NaN / 0x7F) so unwritten elements show up."""
+    import torch
+    import sparse_mla_decode_top_amd as smla
+    inp = dev.inp
+    s_q, h_q = inp.s_q, inp.h_q
+    d = dev.q.device
+    o_acc = lse_acc = None
+    if path in ("split", "partial"):
+        o_acc = torch.full((num_splits, s_q, h_q, 512), float("nan"), device=d)
+        lse_acc = torch.full((num_splits, s_q, h_q), float("nan"), device=d)
+    out = out_scale = None
+    if path != "partial":
+        if out_dtype == "f32":
+            out = torch.full((s_q, h_q, 512), float("nan"), device=d)
+        elif out_dtype == "bf16":
+            out = torch.full((s_q, h_q, 512), float("nan"), device=d, dtype=torch.bfloat16)
+        else:
+            out = torch.full((s_q, h_q, 512), 0x7F, device=d, dtype=torch.uint8)
+            out_scale = torch.full((s_q,), float("nan"), device=d)
+    lse_out = torch.full((s_q, h_q), float("nan"), device=d) if (want_lse and out is not None) else None
+    smla.sparse_mla_decode(dev.q, dev.kv if kv is None else kv, dev.indices if indices is None else indices,
+                           num_splits, inp.scale, kv_scale=dev.kv_scale,
+                           sink=dev.sink if use_sink else None, o_accum=o_acc, lse_accum=lse_acc, out=out,
+                           out_scale=out_scale, lse_out=lse_out)
+    torch.cuda.synchronize()
+    res = {}
+    if out is not None:
+        if out_dtype == "fp8":
+            res["codes"] = out.cpu().numpy()
+            res["scale"] = out_scale.cpu().numpy().astype(np.float64)
+        else:
+            res["O"] = out.float().cpu().numpy().astype(np.float64)
+    if lse_out is not None:
+        res["lse"] = lse_out.cpu().numpy().astype(np.float64)
+    if o_acc is not None:
+        res["o_acc"] = o_acc.cpu().numpy()
+        res["lse_acc"] = lse_acc.cpu().numpy()
+    return res
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def assert_lse_close(got, ref, tol=TOL_LSE):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert not np.any(np.isnan(got)), "unwritten or NaN LSE"
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "-inf pattern differs"
+    if fin.any():
+        err = max_abs(got[fin], ref[fin])
+        assert err <= tol, f"LSE max-abs error {err:.3g} > {tol}"
+
+
+def assert_o_close(got, ref, tol=TOL_O, rel=0.0):
+    got = np.asarray(got, np.float64)
+    assert not np.any(np.isnan(got)), "unwritten or NaN output"
+    bound = tol + rel * np.abs(ref)
+    err = np.abs(got - ref)
+    worst = float(np.max(err - bound)) if err.size else -1.0
+    assert worst <= 0, f"O error exceeds bound by {worst:.3g} (max-abs {float(np.max(err)):.3g})"
+
+
+def e4m3_half_ulp(x):
+    """Half the spacing of e4m3fn values around |x| (saturating range included)."""
+    a = np.maximum(np.abs(x), 2.0 ** -6)
+    e = np.floor(np.log2(a))
+    return np.exp2(e - 4)

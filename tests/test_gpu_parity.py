@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on the
+same seeded inputs, for every workload family, split count and path.
+
+Bars: O max-abs <= 2e-3 (fp32 output; bf16 output adds its own rounding,
+2^-8 |O|), LSE max-abs <= 1e-5, combined fp32 O between split counts <= 1e-5,
+index handling and empty splits bit-exact (+0.0 and -inf).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mla_decode_top_amd import workloads as W
+from tests import _harness as H
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SEEDS = (0, 1, 2)
+FAMILIES = ["tiny", "single", "single_nosink", "small6", "small16", "small16_trailing", "degenerate"]
+
+
+def _dev(name, seed):
+    print(f"[case] {name} seed={seed}", flush=True)
+    return H.DeviceInputs(H.inputs_for(name, seed))
+
+
+_DEV_CACHE = {}
+
+
+def dev_for(name, seed):
+    key = (name, seed)
+    if key not in _DEV_CACHE:
+        _DEV_CACHE.clear()
+        torch.cuda.empty_cache()
+        _DEV_CACHE[key] = _dev(name, seed)
+    return _DEV_CACHE[key]
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("name", FAMILIES)
+def test_split_path_matches_oracle(name, seed):
+    w = W.WORKLOADS[name]
+    dev = dev_for(name, seed)
+    O_ref, L_ref = H.oracle_direct(name, seed)
+    O_fin = H.oracle_final(dev.inp, O_ref, L_ref)
+    for S in w.num_splits:
+        res = H.run(dev, S, "f32", "split")
+        H.assert_o_close(res["O"], O_fin)
+        H.assert_lse_close(res["lse"], L_ref)
+    res = H.run(dev, w.num_splits[-1], "bf16", "split")
+    H.assert_o_close(res["O"], O_fin, rel=2.0 ** -8)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("name", ["tiny", "single", "single_nosink", "small16", "small16_trailing"])
+def test_direct_path_matches_oracle(name, seed):
+    dev = dev_for(name, seed)
+    O_ref, L_ref = H.oracle_direct(name, seed)
+    O_fin = H.oracle_final(dev.inp, O_ref, L_ref)
+    res = H.run(dev, 1, "f32", "direct")
+    H.assert_o_close(res["O"], O_fin)
+    H.assert_lse_close(res["lse"], L_ref)
+    res = H.run(dev, 1, "bf16", "direct", want_lse=False)
+    H.assert_o_close(res["O"], O_fin, rel=2.0 ** -8)
+
+
+@pytest.mark.parametrize("name", ["tiny", "single", "small6", "small16"])
+def test_split_count_invariance(name):
+    """Combined fp32 O and LSE agree across split counts (and with the direct path) to 1e-5."""
+    w = W.WORKLOADS[name]
+    dev = dev_for(name, 0)
+    base = H.run(dev, 1, "f32", "split")
+    direct = H.run(dev, 1, "f32", "direct")
+    assert H.max_abs(direct["O"], base["O"]) <= H.TOL_SPLIT
+    H.assert_lse_close(direct["lse"], base["lse"], H.TOL_SPLIT)
+    for S in sorted(set(w.num_splits) | {3, 5, 7, 10, 16}):
+        res = H.run(dev, S, "f32", "split")
+        err = H.max_abs(res["O"], base["O"])
+        assert err <= H.TOL_SPLIT, f"S={S}: O differs from S=1 by {err:.3g}"
+        H.assert_lse_close(res["lse"], base["lse"], H.TOL_SPLIT)
+
+
+@pytest.mark.parametrize("name", ["tiny", "single", "small16", "degenerate"])
+def test_partials_match_oracle(name):
+    """Every split's partial (O_s normalised by its own l, LSE_s) against the oracle's."""
+    w = W.WORKLOADS[name]
+    dev = dev_for(name, 1)
+    inp = dev.inp
+    for S in sorted(set(w.num_splits) | {3}):
+        res = H.run(dev, S, "f32", "partial")
+        o_ref, l_ref = oracle.split_partials(inp.q.astype(np.float64), H.oracle_pool(inp), inp.indices,
+                                             inp.n_pool, inp.scale, S, 64)
+        empty = np.isneginf(l_ref)
+        # an empty or fully masked split is exactly O = +0.0, LSE = -inf
+        assert np.all(res["o_acc"][empty] == 0.0) and not np.any(np.signbit(res["o_acc"][empty]))
+        assert np.all(np.isneginf(res["lse_acc"][empty]))
+        H.assert_o_close(res["o_acc"][~empty], o_ref[~empty])
+        H.assert_lse_close(res["lse_acc"], l_ref)
+
+
+def test_more_splits_than_blocks_is_exact():
+    """topk = 64 is one block: with 16 splits, splits 1..15 are empty."""
+    dev = dev_for("degenerate", 0)
+    res = H.run(dev, 16, "f32", "split")
+    o = res["o_acc"]
+    assert np.all(o[1:] == 0.0) and not np.any(np.signbit(o[1:]))
+    assert np.all(np.isneginf(res["lse_acc"][1:]))
+    assert np.all(np.isfinite(res["lse_acc"][0]))
+    one = H.run(dev, 1, "f32", "split")
+    assert H.max_abs(res["O"], one["O"]) <= H.TOL_SPLIT
+
+
+@pytest.mark.parametrize("path", ["split", "direct"])
+def test_out_of_range_and_fully_masked_tokens(path):
+    inp = W.make_inputs(4, 64, 4096, 640, seed=7, sink=True, pad="oob")
+    inp.indices[2, :] = -1                       # a token with nothing to attend to
+    inp.indices[3, 64:] = -1                     # a token whose later blocks are all masked
+    dev = H.DeviceInputs(inp)
+    O_ref, L_ref = oracle.attend(inp.q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    res = H.run(dev, 1 if path == "direct" else 4, "f32", path)
+    H.assert_o_close(res["O"], O_fin)
+    H.assert_lse_close(res["lse"], L_ref)
+    assert np.all(res["O"][2] == 0.0) and not np.any(np.signbit(res["O"][2]))
+    assert np.all(np.isneginf(res["lse"][2]))
+
+
+@pytest.mark.parametrize("h_q", [16, 32])
+def test_fewer_heads(h_q):
+    inp = W.make_inputs(3, h_q, 8192, 200, seed=11, sink=True, pad="random")
+    dev = H.DeviceInputs(inp)
+    O_ref, L_ref = oracle.attend(inp.q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    for S, path in ((1, "direct"), (1, "split"), (3, "split"), (4, "split")):
+        res = H.run(dev, S, "f32", path)
+        H.assert_o_close(res["O"], O_fin)
+        H.assert_lse_close(res["lse"], L_ref)
+
+
+def test_ragged_topk_and_row_stride():
+    """topk not a multiple of 64, and pool rows embedded in a wider buffer (row stride 640)."""
+    inp = W.make_inputs(5, 64, 3000, 333, seed=12, sink=True, pad="random")
+    dev = H.DeviceInputs(inp)
+    wide = torch.zeros((inp.n_pool, 640), dtype=torch.bfloat16, device="cuda")
+    wide[:, :576] = dev.kv
+    wide[:, 576:] = float("nan")                 # never read
+    O_ref, L_ref = oracle.attend(inp.q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    for S, path in ((1, "direct"), (2, "split"), (6, "split"), (8, "split")):
+        res = H.run(dev, S, "f32", path, kv=wide)
+        H.assert_o_close(res["O"], O_fin)
+        H.assert_lse_close(res["lse"], L_ref)
+
+
+@pytest.mark.parametrize("name", ["large96", "large384"])
+def test_large_batches_adaptive_splits(name):
+    import sparse_mla_decode_top_amd as smla
+    w = W.WORKLOADS[name]
+    dev = dev_for(name, 0)
+    inp = dev.inp
+    S = smla.smla_choose_num_splits(w.s_q, w.h_q, w.topk, 256)
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(w.s_q, 24, replace=False))
+    O_ref, L_ref = oracle.attend(inp.q[sample].astype(np.float64), H.oracle_pool(inp), inp.indices[sample],
+                                 inp.n_pool, inp.scale)
+    O_fin = oracle.apply_sink(O_ref, L_ref, inp.sink.astype(np.float64))
+    results = {}
+    for s in sorted({1, 2, S}):
+        res = H.run(dev, s, "f32", "split")
+        H.assert_o_close(res["O"][sample], O_fin)
+        H.assert_lse_close(res["lse"][sample], L_ref)
+        results[s] = res
+    for s in results:            # every token, across split counts
+        assert H.max_abs(results[s]["O"], results[1]["O"]) <= H.TOL_SPLIT
+    direct = H.run(dev, 1, "bf16", "direct", want_lse=False)
+    H.assert_o_close(direct["O"][sample], O_fin, rel=2.0 ** -8)
+
+
+@pytest.mark.parametrize("name", ["fp8_1", "fp8_16"])
+def test_fp8_pool_and_fp8_output(name):
+    w = W.WORKLOADS[name]
+    dev = dev_for(name, 0)
+    inp = dev.inp
+    O_ref, L_ref = H.oracle_direct(name, 0)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    # fp32 output through the FP8 pool
+    res = H.run(dev, 8, "f32", "split")
+    H.assert_o_close(res["O"], O_fin)
+    H.assert_lse_close(res["lse"], L_ref)
+    direct = H.run(dev, 1, "f32", "direct")
+    H.assert_o_close(direct["O"], O_fin)
+    # FP8 output (per-token scale = amax / 448), from the combine and from the direct epilogue
+    amax_ref = np.abs(O_fin).reshape(w.s_q, -1).max(axis=1)
+    for path, S in (("split", 8), ("direct", 1)):
+        r = H.run(dev, S, "fp8", path)
+        scale = r["scale"]
+        assert np.all(np.abs(scale - amax_ref / 448.0) <= H.TOL_O / 448.0 + 1e-7 * scale)
+        dec = oracle.e4m3_decode(r["codes"]) * scale[:, None, None]
+        x_bound = np.abs(O_fin) / scale[:, None, None] + H.TOL_O / scale[:, None, None]
+        bound = H.e4m3_half_ulp(x_bound) * scale[:, None, None] + H.TOL_O
+        assert not np.any(np.isnan(dec))
+        assert np.all(np.abs(dec - O_fin) <= bound), f"{path}: fp8 value error beyond bound"
+
+
+def test_partial_only_then_combine_matches_fused():
+    import sparse_mla_decode_top_amd as smla
+    dev = dev_for("small16", 0)
+    fused = H.run(dev, 4, "f32", "split")
+    part = H.run(dev, 4, "f32", "partial")
+    o = torch.from_numpy(part["o_acc"]).cuda()
+    l = torch.from_numpy(part["lse_acc"]).cuda()
+    out = torch.empty((16, 64, 512), device="cuda")
+    lse = torch.empty((16, 64), device="cuda")
+    smla.combine_splits(o, l, 4, out, sink=dev.sink, lse_out=lse)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), fused["O"].astype(np.float32))
+    assert np.array_equal(lse.cpu().numpy(), fused["lse"].astype(np.float32))
+
+
+def test_combine_against_oracle_combine():
+    """combine_splits on generator-made partials (random O_s, LSE_s with -inf splits) vs the oracle's."""
+    import sparse_mla_decode_top_amd as smla
+    rng = np.random.default_rng(21)
+    S, s_q, h_q = 6, 5, 64
+    o = rng.standard_normal((S, s_q, h_q, 512)).astype(np.float32)
+    l = (rng.standard_normal((S, s_q, h_q)) * 4).astype(np.float32)
+    l[2, 1, :] = -np.inf
+    o[2, 1, :] = 0.0
+    l[:, 3, 5] = -np.inf                      # one (token, head) with no split at all
+    o[:, 3, 5] = 0.0
+    sink = rng.standard_normal(h_q).astype(np.float32)
+    O_ref, L_ref = oracle.combine_partials(o.astype(np.float64), l.astype(np.float64))
+    O_fin = oracle.apply_sink(O_ref, L_ref, sink.astype(np.float64))
+    out = torch.empty((s_q, h_q, 512), device="cuda")
+    lse = torch.empty((s_q, h_q), device="cuda")
+    smla.combine_splits(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(), S, out,
+                        sink=torch.from_numpy(sink).cuda(), lse_out=lse)
+    torch.cuda.synchronize()
+    H.assert_o_close(out.cpu().numpy(), O_fin, tol=1e-5, rel=1e-5)
+    H.assert_lse_close(lse.cpu().numpy(), L_ref)
+    assert np.all(out.cpu().numpy()[3, 5] == 0.0)
+
+
+def test_fp8_encoder_is_bit_exact():
+    """Single split, LSE 0: the combine's e4m3 codes equal the oracle's float32-decided codes,
+    including exact ties (token 0 has amax 448, so its scale is exactly 1)."""
+    import sparse_mla_decode_top_amd as smla
+    rng = np.random.default_rng(22)
+    s_q, h_q = 5, 64
+    o = rng.standard_normal((1, s_q, h_q, 512)).astype(np.float32)
+    vals = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)          # exact ties in float32
+    t0 = np.concatenate([mids, -mids, vals.astype(np.float32), -vals.astype(np.float32)])
+    o[0, 0].reshape(-1)[: t0.size] = t0
+    o[0, 0, 0, 0] = 448.0
+    o[0, 1] *= 1e-3                                                  # small magnitudes
+    o[0, 2] = 0.0                                                    # amax 0 -> scale 1, all codes 0
+    o[0, 3, :, ::7] = -0.0
+    o[0, 4] *= 1000.0
+    l = np.zeros((1, s_q, h_q), dtype=np.float32)
+    codes_ref, scale_ref = oracle.fp8_quantize_per_token_f32(o[0])
+    out = torch.empty((s_q, h_q, 512), device="cuda", dtype=torch.uint8)
+    scale = torch.empty((s_q,), device="cuda")
+    smla.combine_splits(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(), 1, out, out_scale=scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(scale.cpu().numpy(), scale_ref)
+    got = out.cpu().numpy()
+    bad = np.argwhere(got != codes_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+
+
+def test_graph_capture_replays_match_eager():
+    """The decode step (attention + combine) captured into a HIP graph: every replay equals eager."""
+    import sparse_mla_decode_top_amd as smla
+    dev = dev_for("small6", 0)
+    inp = dev.inp
+    S = 4
+    o_acc = torch.empty((S, inp.s_q, 64, 512), device="cuda")
+    lse_acc = torch.empty((S, inp.s_q, 64), device="cuda")
+    out = torch.empty((inp.s_q, 64, 512), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((inp.s_q, 64), device="cuda")
+
+    def step():
+        smla.sparse_mla_decode(dev.q, dev.kv, dev.indices, S, inp.scale, sink=dev.sink, o_accum=o_acc,
+                               lse_accum=lse_acc, out=out, lse_out=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
