@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the split-KV sparse MLA decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the attention kernel
+over every (token, split) job plus the combine, on inputs already resident in
+HBM.  Steps are replayed from a HIP graph (the pages time their kernels under
+CUDA graphs) and cycle through L distinct "layers" -- independent pools,
+queries and index lists whose pools together exceed the 256 MB last-level
+cache -- so the gathered rows come from HBM as in a multi-layer decode.
+
+Prints ONE JSON line (rank 0, N = 1):
+  value        microseconds per step (lower is better) at the single-token
+               workload: s_q=1, h_q=64, topk=640, pool 65536 bf16 rows, sink on,
+               num_splits from smla_choose_num_splits
+  roofline     the attention kernel's algorithmic bytes per launch over its mean
+               duration (HIP events on its launch stream), against 8 TB/s
+  cpu_baseline the float64 oracle timed on the host cores on the same inputs
+  sweep        the same measurement at s_q = 6, 16, 96, 384 (context)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+_CORES = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(_CORES))
+
+import numpy as np  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA split-KV decode µs/step + HBM TB/s (h_q=64, topk=640, s_q=1..384)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+# Algorithmic bytes per query token (h_q = 64, topk = 640, bf16 pool):
+KV_BYTES = 640 * 1152          # gathered rows (576 bf16 each)
+Q_BYTES = 64 * 576 * 2
+IDX_BYTES = 640 * 4
+OUT_BYTES = 64 * 512 * 2       # bf16 output
+MAIN_BYTES_PER_TOKEN = KV_BYTES + Q_BYTES + IDX_BYTES     # 813,568: the attention kernel's share
+STEP_BYTES_PER_TOKEN = MAIN_BYTES_PER_TOKEN + OUT_BYTES   # 879,104
+FLOPS_PER_TOKEN = 2 * 64 * 640 * (576 + 512)              # 89,128,960
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_mla_decode_top_amd", "csrc", "smla_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_kernel_single_token.json")
+
+WORKLOADS = {   # name -> (s_q, n_pool)
+    "single": (1, 65536),
+    "small6": (6, 131072),
+    "small16": (16, 131072),
+    "large96": (96, 262144),
+    "large384": (384, 262144),
+}
+LLC_BYTES = 256 << 20
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="single", choices=sorted(WORKLOADS))
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = smla_choose_num_splits")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-reps", type=int, default=100)
+    ap.add_argument("--copy-only", action="store_true",
+                    help="run only a plain 256 MiB device copy (calibrates the HBM byte counters)")
+    return ap.parse_args()
+
+
+def source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Layer:
+    """Device-resident inputs of one independent decode layer."""
+
+    def __init__(self, s_q, n_pool, seed, torch, W):
+        inp = W.make_inputs(s_q, 64, n_pool, 640, seed, kv_dtype="bf16", sink=True)
+        self.inp = inp
+        self.q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        self.kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        self.indices = torch.from_numpy(inp.indices).cuda()
+        self.sink = torch.from_numpy(inp.sink).cuda()
+        self.out = torch.empty((s_q, 64, 512), dtype=torch.bfloat16, device="cuda")
+
+
+def build_layers(s_q, n_pool, torch, W, seed0=1000):
+    per_pool = n_pool * 576 * 2
+    n_layers = max(2, -(-2 * LLC_BYTES // per_pool))       # pools total >= 2x the last-level cache
+    log(f"s_q={s_q}: generating {n_layers} layers of {per_pool / 1e6:.0f} MB pools")
+    return [Layer(s_q, n_pool, seed0 + i, torch, W) for i in range(n_layers)]
+
+
+def time_steps(layers, S, steps, warmup, torch, smla):
+    """Step time from graph replays; returns (us_per_step, event_us_per_step)."""
+    s_q = layers[0].inp.s_q
+    scale = layers[0].inp.scale
+    o_acc = torch.empty((S, s_q, 64, 512), device="cuda") if S > 1 else None
+    lse_acc = torch.empty((S, s_q, 64), device="cuda") if S > 1 else None
+
+    def step(L):
+        smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, sink=L.sink, o_accum=o_acc,
+                               lse_accum=lse_acc, out=L.out)
+
+    for L in layers:                  # eager warm-up (also loads the library)
+        step(L)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for L in layers:
+            step(L)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for L in layers:
+            step(L)
+    n = len(layers)
+    reps_w = max(1, -(-warmup // n))
+    reps = max(1, -(-steps // n))
+    for _ in range(reps_w):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k = reps * n
+    return (t1 - t0) * 1e6 / k, e0.elapsed_time(e1) * 1e3 / k, k, reps_w * n
+
+
+def sleep_cycles_for(ms, torch):
+    """torch.cuda._sleep argument that keeps the GPU busy about `ms` milliseconds."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cyc = 1_000_000
+    e0.record()
+    torch.cuda._sleep(cyc)
+    e1.record()
+    torch.cuda.synchronize()
+    per_ms = cyc / max(e0.elapsed_time(e1), 1e-3)
+    return int(per_ms * ms)
+
+
+def kernel_durations(layers, S, reps, torch, smla):
+    """Mean duration (us) of the attention kernel and of the combine, each bracketed by HIP
+    events on the stream it is launched on.  A GPU sleep queued first keeps the stream
+    backed up, so every event pair brackets its kernel alone."""
+    s_q = layers[0].inp.s_q
+    scale = layers[0].inp.scale
+    o_acc = torch.empty((S, s_q, 64, 512), device="cuda")
+    lse_acc = torch.empty((S, s_q, 64), device="cuda")
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    cyc = sleep_cycles_for(5 + reps * 0.25, torch)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(cyc)
+    for i in range(reps):
+        L = layers[i % len(layers)]
+        evs[i][0].record(stream)
+        smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, sink=L.sink, o_accum=o_acc, lse_accum=lse_acc)
+        evs[i][1].record(stream)
+        smla.combine_splits(o_acc, lse_acc, S, L.out, sink=L.sink)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    main = np.array([a.elapsed_time(b) * 1e3 for a, b, _ in evs])
+    comb = np.array([b.elapsed_time(c) * 1e3 for _, b, c in evs])
+    gaps = np.array([evs[i][2].elapsed_time(evs[i + 1][0]) * 1e3 for i in range(reps - 1)])
+    return float(main.mean()), float(comb.mean()), float(np.median(gaps)) if gaps.size else 0.0
+
+
+def traffic_for(S):
+    """HBM bytes per launch of the attention kernel from the committed PMC summary,
+    or None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != source_hash() or t.get("num_splits") != S:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(layer, seconds):
+    import oracle
+    from threadpoolctl import threadpool_info
+    inp = layer.inp
+
+    class Pool:
+        def __getitem__(self, rows):
+            from sparse_mla_decode_top_amd.workloads import bf16_bits_to_f32
+            return bf16_bits_to_f32(inp.kv_bits[rows])
+
+    q64 = inp.q.astype(np.float64)
+    sink = inp.sink.astype(np.float64)
+    times = []
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or len(times) < 3:
+        t0 = time.perf_counter()
+        O, L = oracle.attend(q64, Pool(), inp.indices, inp.n_pool, inp.scale)
+        oracle.apply_sink(O, L, sink)
+        times.append(time.perf_counter() - t0)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(float(np.median(times)) * 1e6, 1), "unit": "us/step", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"whole step ({inp.s_q} token x 64 heads x 640 slots, float64), median of "
+                      f"{len(times)} runs in {seconds:.0f} s on {_CORES} host cores"}
+
+
+def measure(name, S_arg, steps, warmup, reps, torch, smla, W):
+    s_q, n_pool = WORKLOADS[name]
+    S = S_arg or smla.smla_choose_num_splits(s_q, 64, 640, 256)
+    layers = build_layers(s_q, n_pool, torch, W)
+    us, ev_us, k, w = time_steps(layers, S, steps, warmup, torch, smla)
+    main_us, comb_us, gap = kernel_durations(layers, S, reps, torch, smla) if S > 1 else (None, None, None)
+    if S == 1:
+        # direct path: one kernel per step
+        main_us, comb_us, gap = _direct_durations(layers, reps, torch, smla)
+    step_gbs = STEP_BYTES_PER_TOKEN * s_q / (ev_us * 1e-6) / 1e9
+    return dict(name=name, s_q=s_q, n_pool=n_pool, S=S, us=us, ev_us=ev_us, steps=k, warmup=w,
+                main_us=main_us, comb_us=comb_us, gap_us=gap, step_tbps=step_gbs / 1e3,
+                layers=len(layers)), layers
+
+
+def _direct_durations(layers, reps, torch, smla):
+    scale = layers[0].inp.scale
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    cyc = sleep_cycles_for(5 + reps * 0.15, torch)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(cyc)
+    for i in range(reps):
+        L = layers[i % len(layers)]
+        evs[i][0].record(stream)
+        smla.sparse_mla_decode(L.q, L.kv, L.indices, 1, scale, sink=L.sink, out=L.out)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    main = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return float(main.mean()), 0.0, 0.0
+
+
+def copy_only(torch):
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n}), flush=True)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+    import sparse_mla_decode_top_amd as smla
+    from sparse_mla_decode_top_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    smla.load_library()
+    if args.copy_only:
+        copy_only(torch)
+        return
+
+    head, layers = measure(args.workload, args.num_splits, args.steps, args.warmup, args.kernel_reps,
+                           torch, smla, W)
+    s_q, S = head["s_q"], head["S"]
+    log(f"{args.workload}: {head['us']:.2f} us/step (events {head['ev_us']:.2f}), attention kernel "
+        f"{head['main_us']:.2f} us, combine {head['comb_us']:.2f} us, S={S}")
+    main_bytes = MAIN_BYTES_PER_TOKEN * s_q
+    achieved = main_bytes / (head["main_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(S),
+                "kernel": "decode_kernel<bf16 pool, partial>" if S > 1 else "decode_kernel<bf16 pool, direct>",
+                "bytes_per_launch": main_bytes, "mean_launch_us": round(head["main_us"], 3),
+                "mfma_frac": round(FLOPS_PER_TOKEN * s_q / (head["main_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host cores")
+        cpu = cpu_baseline(layers[0], args.cpu_seconds)
+    del layers
+    torch.cuda.empty_cache()
+
+    sweep = {}
+    if not args.no_sweep:
+        for name in ("small6", "small16", "large96", "large384"):
+            if name == args.workload:
+                continue
+            r, ls = measure(name, 0, max(20, args.steps // 4), args.warmup, max(20, args.kernel_reps // 4),
+                            torch, smla, W)
+            del ls
+            torch.cuda.empty_cache()
+            mb = MAIN_BYTES_PER_TOKEN * r["s_q"]
+            sweep[name] = {"s_q": r["s_q"], "num_splits": r["S"], "us_per_step": round(r["ev_us"], 2),
+                           "attention_kernel_us": round(r["main_us"], 2), "combine_us": round(r["comb_us"], 2),
+                           "step_hbm_tbps": round(r["step_tbps"], 3),
+                           "kernel_hbm_frac": round(mb / (r["main_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "kernel_mfma_frac": round(FLOPS_PER_TOKEN * r["s_q"] / (r["main_us"] * 1e-6) / 1e12
+                                                     / BF16_PEAK_TFLOPS, 4)}
+            log(f"{name}: {r['ev_us']:.2f} us/step, kernel {r['main_us']:.2f} us, S={r['S']}")
+
+    line = {
+        "metric": METRIC, "value": round(head["ev_us"], 3), "unit": "us/step", "n_gpus": 1,
+        "steps": head["steps"], "warmup": head["warmup"], "ms_per_step": round(head["ev_us"] / 1e3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 pools, uniform unique top-k indices)",
+        "config": {"workload": f"single-token decode: s_q={s_q}, h_q=64, d_qk=576, d_v=512, topk=640, "
+                               f"pool {head['n_pool']} bf16 rows x {head['layers']} layers, sink on, "
+                               f"num_splits={S}",
+                   "global_batch": s_q, "num_splits": S, "timing": "HIP graph replay, cold layer rotation"},
+        "hbm_tbps": round(head["step_tbps"], 4),
+        "wall_us_per_step": round(head["us"], 3),
+        "attention_kernel_us": round(head["main_us"], 3),
+        "combine_kernel_us": round(head["comb_us"], 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+        "context": {"b200_fused_kernel_us_s_q1": {"unsplit": 26.6, "split8": 14.4, "split16": 14.3}},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,35 +8,38 @@
 // the remainder on the leading splits; an empty split is O = 0, LSE = -inf).
 //
 // decode kernel: one workgroup of 4 wave64s per (token, split) job.
-//   * The 64 slots of a KV block share one tile: the index-driven gather copies
-//     each selected 1152-byte row into LDS with 16-byte direct-to-LDS loads
-//     (global_load_lds_dwordx4), double-buffered so block b+1 streams in while
-//     block b is computed.  Masked slots are never read; their tile rows are
-//     zero-filled.
-//   * Wave w = 2*hg + x owns heads [32hg, 32hg+32).  For QK^T it takes slots
-//     [32x, 32x+32) of the block: S^T[slot][head] = K . Q^T with
-//     v_mfma_f32_32x32x16_bf16 (K from LDS, Q resident in VGPRs), so every lane
-//     holds scores of exactly one head.  For PV it takes value columns
-//     [256x, 256x+256): O^T[col][head] = V^T . P^T, the V^T operand read with
-//     the gfx950 LDS transpose load ds_read_b64_tr_b16 from the same row-major
-//     tile, so again every accumulator lane belongs to one head.
-//   * Online softmax in log2 units with an integer running maximum M: each
-//     weight is p = 2^(t - floor t) * 2^(floor t - M).  Its bf16 rounding does
-//     not depend on M, and every rescale is an exact power of two, so the
-//     partials of different split counts combine to the same value up to fp32
-//     summation order.  The denominator sums the unrounded fp32 weights.
+//   * The 64 slots of a KV block share one LDS tile, gathered by index with
+//     16-byte direct-to-LDS loads (global_load_lds_dwordx4) in which 8 lanes
+//     fetch one contiguous 128-byte segment of a row; two tiles double-buffer
+//     the gather of block b+1 behind the compute of block b.  Masked slots are
+//     never read; their tile rows are zero-filled.
+//   * Wave w owns heads [16w, 16w+16) end to end, so the waves share nothing
+//     but the tile (one barrier per block).  S^T[slot][head] = K . Q^T and
+//     O^T[col][head] = V^T . P^T use v_mfma_f32_16x16x32_bf16; every lane
+//     holds one head's scores and accumulators.  Q stays in VGPRs (72 per
+//     lane); V^T is read from the row-major tile with the gfx950 transpose
+//     load ds_read_b64_tr_b16.
+//   * Softmax in log2 units against an integer frame M per head: each weight
+//     is p = 2^(t - floor t) * 2^(floor t - M).  Its bf16 rounding does not
+//     depend on M, so the partials of different split counts combine to the
+//     same value up to fp32 summation order.  M is the floor of the head's
+//     first non-empty block maximum and never moves inside a pass, so the
+//     accumulators are touched by MFMAs only (they stay in AGPRs).  A later
+//     score above M + 64 would risk overflow: the job then runs once more
+//     with M = floor of the largest score seen, which bounds every p by 2.
+//     The denominator sums the unrounded fp32 weights.
 //   * P enters the PV product as two bf16 terms, hi = bf16(p) and
 //     lo = bf16(p - hi), sharing each V^T operand: a bf16-rounded P alone
 //     leaves O errors near 4e-3 when a few slots dominate (one 64-slot block);
 //     hi + lo carries p to about 2^-17 relative.
 //
-// combine kernel: one thread per 4 output columns of a (token, head), reading
-// the split-major partials.
+// combine kernel: split-major partials -> final output (+ sink, cast).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
+#include "smla.h"
 #include "smla_internal.h"
 
 namespace smla {
@@ -44,7 +47,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef short i16x4 __attribute__((__vector_size__(8)));
-typedef float f32x16 __attribute__((__vector_size__(64)));
 typedef float f32x4 __attribute__((__vector_size__(16)));
 typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
@@ -52,87 +54,89 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 64;                         // slots per KV block
-constexpr int kRowChunks = 72;                   // 16-byte chunks per bf16 row (576 x 2 B)
-constexpr int kTileChunks = kBlk * kRowChunks;   // 4608
-constexpr int kTileBytes = kTileChunks * 16;     // 73728
-constexpr int kCodeRowChunks = 36;               // 16-byte chunks per FP8 row (576 B)
-constexpr int kCodeTileBytes = kBlk * kCodeRowChunks * 16;   // 36864
+constexpr int kTileBytes = kBlk * 1152;          // 64 bf16 rows of 576
+constexpr int kCodeTileBytes = kBlk * 576;       // 64 e4m3 rows of 576
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kFrameSlack = 64.0f;     // scores may exceed a head's frame M by this much
 
 enum OutDtype { kOutBf16 = 0, kOutF32 = 1, kOutFp8 = 2 };
 
 // ---------------------------------------------------------------------------
-// LDS tile layout ("chunk-major").  A bf16 KV row is 72 chunks of 16 bytes
-// (8 elements).  Chunk c of tile row r lives at chunk position
-//     c * 64 + (r ^ 4 * (c & 3)),
-// i.e. the 64 rows of one chunk column are contiguous.  Consequences:
-//   * gather: one direct-to-LDS load instruction fills one chunk column, lane l
-//     loading row l ^ 4(c & 3); wave w owns the columns c = w (mod 4), so each
-//     lane gathers from ONE pool row at immediate offsets 16c;
-//   * QK^T reads (32 rows x one chunk per 32 lanes) hit 32 consecutive
-//     positions: conflict-free;
-//   * PV transpose reads (4 rows x 2 adjacent chunks per 16 lanes): the XOR on
-//     row bits 2..3 moves the two chunks to different bank halves.
-// The FP8 code tile uses the same formula over its 36 chunks per row.
+// LDS tile layout ("octet-major").  A bf16 row is 72 chunks of 16 bytes (8
+// elements), grouped in 9 octets of 8 chunks (128 bytes).  Chunk c of tile row
+// r sits at 16-byte position
+//     (c >> 3) * 512 + r * 8 + ((c & 7) ^ (r & 7)).
+// * Gather: one load instruction fills one octet of 8 rows; lanes 8k..8k+7
+//   fetch the 128 contiguous bytes of one row (in swizzled order).
+// * The XOR of the chunk slot with the low row bits makes both operand read
+//   streams bank-conflict free on the gfx950 LDS (64 banks, 256 B/clk): the
+//   QK^T reads (16 B per lane, 16 rows x 4 chunks per instruction) and the PV
+//   transpose reads (8 B per lane, 16 rows x 2 chunks).  This was measured
+//   with the LDS bank-conflict counter over the kernel's exact address
+//   streams; several XOR patterns that look conflict free on paper are 2-way
+//   conflicted there.
+// The FP8 code tile is "quartet-major": code chunk c of row r at position
+//     (c >> 2) * 256 + r * 4 + (c & 3),
+// so 4 lanes fetch 64 contiguous bytes of a row.
 // ---------------------------------------------------------------------------
-constexpr int kLoadsBf16 = kRowChunks / kWaves;          // 18 chunk columns per wave
-constexpr int kLoadsFp8 = kCodeRowChunks / kWaves;       // 9
-constexpr float kRescaleSlack = 8.0f;    // the running max only moves when exceeded by this
+// Chunk-slot XOR of tile row r.
+__host__ __device__ constexpr int rsw(int r) { return r & 7; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Direct-to-LDS gather of one lane's row: N loads of 16 bytes at global offsets
-// 64j (chunk columns w, w+4, ...) into LDS bytes base + 4096j + 16*lane (4 chunk
-// columns apart).  The hardware adds the instruction offset to BOTH addresses
-// (LDS address = m0 + offset + 16*lane), so m0 steps by 4096 - 64 = 4032 to
-// land each load 4096 bytes after the previous one.  Issued as one inline-assembly
-// block so that the compiler neither interleaves other m0 users nor inserts a
-// vmcnt wait in front of the LDS reads of the other buffer (it cannot tell the
-// prefetch buffer from the one being read); the kernel waits explicitly.  m0
-// is saved and restored; one wait state follows each m0 write.
-#define SMLA_DMA_STEP(OFF) \
-  "s_add_u32 m0, m0, 4032\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:" #OFF "\n\t"
-template <int N>
-__device__ __forceinline__ void dma_row(const void* gptr, uint32_t lds_base_uniform);
-template <>
-__device__ __forceinline__ void dma_row<18>(const void* gptr, uint32_t lds_base_uniform) {
+// Nine 16-byte direct-to-LDS loads from one row per lane.  The hardware adds
+// the instruction offset to BOTH addresses (LDS address = m0 + offset +
+// 16*lane), so m0 advances by (LDS step - global step).  Issued as one inline
+// assembly block so that the compiler neither touches m0 in between nor
+// inserts a vmcnt wait in front of the LDS reads of the other tile buffer (it
+// cannot tell the prefetch buffer from the one being read); the kernel waits
+// explicitly.  m0 is saved and restored; one wait state follows each m0 write.
+#define SMLA_DMA(M0STEP, OFF) \
+  "s_add_u32 m0, m0, " #M0STEP "\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:" #OFF "\n\t"
+// bf16 tile: octet o of a row -> global +128o, LDS +8192o  (m0 step 8064)
+__device__ __forceinline__ void dma_octets(const void* gptr, uint32_t lds_base_uniform) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off\n\t"
-      SMLA_DMA_STEP(64) SMLA_DMA_STEP(128) SMLA_DMA_STEP(192) SMLA_DMA_STEP(256)
-      SMLA_DMA_STEP(320) SMLA_DMA_STEP(384) SMLA_DMA_STEP(448) SMLA_DMA_STEP(512)
-      SMLA_DMA_STEP(576) SMLA_DMA_STEP(640) SMLA_DMA_STEP(704) SMLA_DMA_STEP(768)
-      SMLA_DMA_STEP(832) SMLA_DMA_STEP(896) SMLA_DMA_STEP(960) SMLA_DMA_STEP(1024)
-      SMLA_DMA_STEP(1088)
+      SMLA_DMA(8064, 128) SMLA_DMA(8064, 256) SMLA_DMA(8064, 384) SMLA_DMA(8064, 512)
+      SMLA_DMA(8064, 640) SMLA_DMA(8064, 768) SMLA_DMA(8064, 896) SMLA_DMA(8064, 1024)
       "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(gptr), "s"(lds_base_uniform)
       : "memory");
 }
-template <>
-__device__ __forceinline__ void dma_row<9>(const void* gptr, uint32_t lds_base_uniform) {
+// FP8 code tile: quartet q of a row -> global +64q, LDS +4096q  (m0 step 4032)
+__device__ __forceinline__ void dma_quartets(const void* gptr, uint32_t lds_base_uniform) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off\n\t"
-      SMLA_DMA_STEP(64) SMLA_DMA_STEP(128) SMLA_DMA_STEP(192) SMLA_DMA_STEP(256)
-      SMLA_DMA_STEP(320) SMLA_DMA_STEP(384) SMLA_DMA_STEP(448) SMLA_DMA_STEP(512)
+      SMLA_DMA(4032, 64) SMLA_DMA(4032, 128) SMLA_DMA(4032, 192) SMLA_DMA(4032, 256)
+      SMLA_DMA(4032, 320) SMLA_DMA(4032, 384) SMLA_DMA(4032, 448) SMLA_DMA(4032, 512)
       "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(gptr), "s"(lds_base_uniform)
       : "memory");
 }
-#undef SMLA_DMA_STEP
+#undef SMLA_DMA
+
+// Hides a value from the optimiser, so that an address computed from it inside
+// the loop keeps its constant parts as instruction offsets instead of being
+// hoisted as many loop-invariant registers.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Workgroup barrier that only drains LDS traffic (in-flight tile prefetches
@@ -145,14 +149,6 @@ __device__ __forceinline__ float warp_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
-}
-
-// Bit s of the result = bit (s ^ 4w) of m: undoes the lane <-> slot XOR of
-// the gather assignment (xor 4 swaps nibbles, xor 8 swaps bytes).
-__device__ __forceinline__ uint64_t unswizzle_mask(uint64_t m, int w) {
-  if (w & 1) m = ((m & 0x0F0F0F0F0F0F0F0Full) << 4) | ((m >> 4) & 0x0F0F0F0F0F0F0F0Full);
-  if (w & 2) m = ((m & 0x00FF00FF00FF00FFull) << 8) | ((m >> 8) & 0x00FF00FF00FF00FFull);
-  return m;
 }
 
 // e4m3fn code of a finite fp32 value, round to nearest even, saturating at
@@ -203,55 +199,50 @@ __device__ __forceinline__ Job decode_job(int num_splits, int n_blocks) {
 // DIRECT: single-split job writing the final output (sink + cast fused).
 // ---------------------------------------------------------------------------
 template <bool KV_FP8, bool DIRECT>
-__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
-  // LDS: two bf16 tiles (bf16 pool) or two code tiles + one bf16 tile (FP8
-  // pool), the P exchange area and small reduction arrays.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeArgs a) {
+  // bf16 pool: two tiles.  FP8 pool: two code tiles + one bf16 tile.
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_p[kWaves * 2 * 64 * 16];
-  __shared__ float s_max[2][64];
-  __shared__ float s_l[2][64];
   __shared__ float s_scale[2][kBlk];
   __shared__ float s_red[kWaves];
+  __shared__ int s_restart;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int g = lane >> 5;            // k-group of the MFMA operand layout
-  const int hg = wave >> 1;           // head tile: heads [32hg, 32hg + 32)
-  const int x = wave & 1;             // QK slot half / PV column half
-  const int hh = 32 * hg + (lane & 31);   // this lane's head (MFMA column)
-  const int partner = wave ^ 1;
-  const int gslot = lane ^ (4 * wave);    // slot of the block whose row this lane gathers
+  const int hl = lane & 15;               // head within the wave (MFMA column)
+  const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
+  const int head = 16 * wave + hl;
 
   const Job job = decode_job(a.num_splits, a.n_blocks);
   const int t = job.t;
   const int32_t* idx_row = a.indices + (int64_t)t * a.topk;
 
-  float M_run = kNegInf;              // integer-valued running max (log2 units)
+  float M_run = kNegInf;              // integer frame of this lane's head (log2 units)
+  float m_seen = kNegInf;             // largest score seen so far
   float l_run = 0.f;                  // this lane's share of the denominator
-  f32x16 acc[8];
+  if (tid == 0) s_restart = 0;        // ordered before its readers by the loop barriers
+  f32x4 acc[32];                      // O^T: column tile ct -> columns 16ct + 4G + i
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[ct][i] = 0.f;
+  for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (job.b0 < job.b1) {
     auto load_idx = [&](int b) -> int {
-      const int slot = b * kBlk + gslot;
+      const int slot = b * kBlk + lane;
       return (b < job.b1 && slot < a.topk) ? __builtin_nontemporal_load(idx_row + slot) : -1;
     };
     auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
-    int idx_cur = load_idx(job.b0);
+    int idx_cur = load_idx(job.b0);          // lane l: slot l of the block
     int idx_nxt = load_idx(job.b0 + 1);
+    const float scale_log2 = a.scale_log2;
 
-    // Q fragments of this lane's head: B operand of S^T = K . Q^T.
-    bf16x8 qf[36];
+    // Q fragments (B operand of S^T = K . Q^T): head, dims 32ks + 8G .. +8.
+    bf16x8 qf[18];
     {
-      const bool hv = hh < a.h_q;
-      const uint16_t* qrow = a.q + ((int64_t)t * a.h_q + (hv ? hh : 0)) * 576 + 8 * g;
+      const bool hv = head < a.h_q;
+      const uint16_t* qrow = a.q + ((int64_t)t * a.h_q + (hv ? head : 0)) * 576 + 8 * G;
 #pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        u32x4 v = *(const u32x4*)(qrow + 16 * ks);
+      for (int ks = 0; ks < 18; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + 32 * ks);
         if (!hv) v = u32x4{0u, 0u, 0u, 0u};
         qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
@@ -259,37 +250,74 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
     const uint32_t tile_lds0 = lds_addr(s_tile);
     constexpr int kBufBytes = KV_FP8 ? kCodeTileBytes : kTileBytes;
-    constexpr int kLoads = KV_FP8 ? kLoadsFp8 : kLoadsBf16;
 
-    // Gather of one block into buffer `buf`: this lane's row, chunk columns
-    // c = wave + 4j.  Masked slots are zero-filled, never read.
+    // Gather one block into buffer `buf`.  bf16: wave w fills rows
+    // [16w, 16w+16) as two groups of 8 rows; lane l gathers rows
+    // 16w + (l >> 3) and 16w + 8 + (l >> 3), chunk (l & 7) ^ swz of each octet.
+    // FP8: wave w fills rows [16w, 16w+16); lane l gathers row 16w + (l >> 2),
+    // chunk l & 3 of each quartet.  Masked rows are zero-filled.
     auto issue_gather = [&](int idx_lane, int buf) {
-      if (valid_of(idx_lane)) {
-        const uint8_t* src = a.kv + (int64_t)idx_lane * a.row_stride_bytes + 16 * wave;
-        dma_row<kLoads>(src, __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kBufBytes + wave * 1024));
-      } else {
-        uint8_t* dst = s_tile + buf * kBufBytes + wave * 1024 + lane * 16;
+      if (!KV_FP8) {
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) *(u32x4*)(dst + 4096 * j) = u32x4{0u, 0u, 0u, 0u};
+        for (int hgrp = 0; hgrp < 2; ++hgrp) {
+          const int rg = 2 * wave + hgrp;                  // group of 8 rows
+          const int row_idx = __shfl(idx_lane, 8 * rg + (lane >> 3));
+          const uint32_t lds_base = tile_lds0 + buf * kBufBytes + rg * 1024;
+          if (valid_of(row_idx)) {
+            const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + (((lane & 7) ^ rsw(lane >> 3)) * 16);
+            dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
+          } else {
+            uint8_t* dst = s_tile + buf * kBufBytes + rg * 1024 + lane * 16;
+#pragma unroll
+            for (int o = 0; o < 9; ++o) *(u32x4*)(dst + 8192 * o) = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      } else {
+        const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
+        const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
+        if (valid_of(row_idx)) {
+          const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + (lane & 3) * 16;
+          dma_quartets(src, __builtin_amdgcn_readfirstlane(lds_base));
+        } else {
+          uint8_t* dst = s_tile + buf * kBufBytes + wave * 1024 + lane * 16;
+#pragma unroll
+          for (int q = 0; q < 9; ++q) *(u32x4*)(dst + 4096 * q) = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     };
 
+    // per-lane LDS byte offsets of the operand reads (see the layout above)
+    const int sw_k = rsw(hl);
+    const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
+    const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
+    const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
+    const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
+    int vb[4];                                                  // column tile ct & 3
+#pragma unroll
+    for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
+
+    for (int pass = 0; pass < 2; ++pass) {
+    bool overflow = false;
+    if (pass > 0) {
+      idx_cur = load_idx(job.b0);
+      idx_nxt = load_idx(job.b0 + 1);
+    }
     // ---- prologue: block b0 in flight ------------------------------------
-    uint64_t vmask_cur = unswizzle_mask(__ballot(valid_of(idx_cur)), wave);
+    uint64_t vmask_cur = __ballot(valid_of(idx_cur));
     issue_gather(idx_cur, 0);
-    float sc_cur = (KV_FP8 && wave == 0 && valid_of(idx_cur)) ? a.kv_scale[idx_cur] : 0.f;
-    const float scale_log2 = a.scale_log2;
+    float sc_cur = (KV_FP8 && valid_of(idx_cur)) ? a.kv_scale[idx_cur] : 0.f;
 
     for (int b = job.b0; b < job.b1; ++b) {
       const int cur = (b - job.b0) & 1;
       wait_vmem_all();          // this wave's share of block b has landed
-      lds_barrier();            // ... and every other wave's; block b-1 fully consumed
+      if (KV_FP8 && wave == 0) s_scale[cur][lane] = sc_cur;
+      lds_barrier();            // ... and every wave's; block b-1 fully consumed
 
       // Prefetch block b+1 (its indices were loaded one block ahead).
       uint64_t vmask_nxt = 0;
       float sc_nxt = 0.f;
       if (b + 1 < job.b1) {
-        vmask_nxt = unswizzle_mask(__ballot(valid_of(idx_nxt)), wave);
+        vmask_nxt = __ballot(valid_of(idx_nxt));
         issue_gather(idx_nxt, cur ^ 1);
         if (KV_FP8 && wave == 0 && valid_of(idx_nxt)) sc_nxt = a.kv_scale[idx_nxt];
       }
@@ -299,201 +327,193 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       if (!KV_FP8) {
         tile = s_tile + cur * kTileBytes;
       } else {
-        // Expand block b's e4m3 codes into the bf16 tile (exact) and publish
-        // the row scales.  Wave w converts bf16 chunk columns c = w + 4j.
+        // Expand block b's e4m3 codes into the bf16 tile (exact conversion).
         uint8_t* btile = s_tile + 2 * kCodeTileBytes;
         const uint8_t* ctile = s_tile + cur * kCodeTileBytes;
-        if (wave == 0) s_scale[cur][lane] = sc_cur;
-        const int r = gslot;                       // row of bf16 position c*64 + lane
 #pragma unroll 6
-        for (int j = 0; j < kLoadsBf16; ++j) {
-          const int c = wave + 4 * j;
-          const int cc = c >> 1;                   // code chunk holding bf16 chunk c
+        for (int j = 0; j < 18; ++j) {
+          const int p = j * kThreads + tid;           // bf16 chunk position
+          const int o = p >> 9, r = (p >> 3) & 63;
+          const int c = 8 * o + ((p & 7) ^ rsw(r));   // bf16 chunk of row r
+          const int cc = c >> 1;                      // code chunk holding it
           const u32x2 codes =
-              *(const u32x2*)(ctile + (cc * 64 + (r ^ (4 * (cc & 3)))) * 16 + (c & 1) * 8);
+              *(const u32x2*)(ctile + ((cc >> 2) * 256 + r * 4 + (cc & 3)) * 16 + (c & 1) * 8);
           // v_cvt_scalef32_pk_bf16_fp8 with scale 1 is exact for every e4m3fn code.
-          u32x4 o;
-          o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
-          o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
-          o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
-          o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
-          *(u32x4*)(btile + (c * 64 + lane) * 16) = o;
+          u32x4 ov;
+          ov[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
+          ov[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
+          ov[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
+          ov[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
+          *(u32x4*)(btile + p * 16) = ov;
         }
         lds_barrier();
         tile = btile;
       }
 
-      // ---- S^T = K . Q^T over this wave's 32 slots --------------------------
-      f32x16 sacc;
+      // ---- S^T = K . Q^T: 4 slot tiles x 18 k-steps ------------------------
+      f32x4 sacc[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      for (int st = 0; st < 4; ++st) sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
       {
-        const int r = 32 * x + (lane & 31);
-        // chunk c = 2ks + g sits at c*64 + (r ^ 4(c & 3)), c & 3 = 2(ks & 1) + g
-        const uint8_t* kb0 = tile + g * 1024 + ((r ^ (4 * g)) * 16);
-        const uint8_t* kb1 = tile + g * 1024 + ((r ^ (8 + 4 * g)) * 16);
+        // four bases keep every offset within the 16-bit ds_read field
+        const uint32_t tl = lds_addr(tile);
+        const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
+                                   opaque(tl + kb1 + 65536)};
+        // Software pipeline: the K fragments of k-step ks+2 are requested
+        // before the MFMAs of k-step ks are issued.
+        auto kfrag = [&](int ks, int st) -> bf16x8 {
+          const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
+          return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
+        };
+        bf16x8 kf[3][4];
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
-          const bf16x8 kf = *(const bf16x8*)(((ks & 1) ? kb1 : kb0) + 2048 * ks);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+        for (int st = 0; st < 4; ++st) { kf[0][st] = kfrag(0, st); kf[1][st] = kfrag(1, st); }
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          if (ks + 2 < 18) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) kf[(ks + 2) % 3][st] = kfrag(ks + 2, st);
+          }
+          __builtin_amdgcn_sched_barrier(0);     // keep the reads two k-steps ahead
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % 3][st], qf[ks], sacc[st], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
 
       // ---- online softmax (log2 units, integer running max) -----------------
+      // lane holds head hl, slots 16st + 4G + i
       float tv[16];
       float mloc = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int slot = 32 * x + 8 * (i >> 2) + 4 * g + (i & 3);
-        const bool v = (vmask_cur >> slot) & 1ull;
-        float sv = sacc[i] * scale_log2;
-        if (KV_FP8) sv *= s_scale[cur][slot];
-        tv[i] = v ? sv : kNegInf;
-        mloc = fmaxf(mloc, tv[i]);
-      }
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = 16 * st + 4 * G + i;
+          float sv = sacc[st][i] * scale_log2;
+          if (KV_FP8) sv *= s_scale[cur][slot];
+          const bool v = (vmask_cur >> slot) & 1ull;
+          tv[4 * st + i] = v ? sv : kNegInf;
+          mloc = fmaxf(mloc, tv[4 * st + i]);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      if (lane < 32) s_max[x][hh] = mloc;
-      lds_barrier();
-      const float mblk = fmaxf(s_max[0][hh], s_max[1][hh]);
-      float M_new = M_run;
-      if (mblk != kNegInf && (M_run == kNegInf || mblk > M_run + kRescaleSlack)) M_new = floorf(mblk);
-      const bool moved = (M_run != kNegInf) && (M_new != M_run);
-      if (__any(moved)) {       // rare: rescale by an exact power of two
-        const float alpha = moved ? __builtin_amdgcn_ldexpf(1.0f, (int)fmaxf(M_run - M_new, -200.f)) : 1.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[ct][i] *= alpha;
-      }
-      M_run = M_new;
+      m_seen = fmaxf(m_seen, mloc);
+      // The first contributing block fixes the frame (nothing is accumulated yet).
+      if (M_run == kNegInf && mloc != kNegInf) M_run = floorf(mloc);
+      overflow |= mloc > M_run + kFrameSlack;
+      const float M_new = M_run;
 
-      uint32_t pk[8], pl[8];      // bf16 pairs of p: high part, low part
+      // P as bf16 hi + lo.  B operand of k-step kk: slots 32kk + 16(e/4) + 4G + (e%4),
+      // i.e. this lane's own values of slot tiles 2kk and 2kk+1.
+      uint32_t ph[8], pl[8];
       float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
+      for (int e = 0; e < 16; e += 2) {
         float pv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const float tt = tv[i + u];
+          const float tt = tv[e + u];
           float p = 0.f;
           if (tt != kNegInf) {
             const float fl = floorf(tt);
-            p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)fmaxf(fl - M_new, -200.f));
+            p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)fminf(fmaxf(fl - M_new, -200.f), 200.f));
           }
           psum += p;
-          if (KV_FP8) {
-            const int slot = 32 * x + 8 * ((i + u) >> 2) + 4 * g + ((i + u) & 3);
-            p *= s_scale[cur][slot];
-          }
+          if (KV_FP8) p *= s_scale[cur][16 * ((e + u) >> 2) + 4 * G + ((e + u) & 3)];
           pv[u] = p;
         }
-        pk[i >> 1] = pack_bf16x2(pv[0], pv[1]);
-        const float h0 = __uint_as_float(pk[i >> 1] << 16), h1 = __uint_as_float(pk[i >> 1] & 0xFFFF0000u);
-        pl[i >> 1] = pack_bf16x2(pv[0] - h0, pv[1] - h1);
+        ph[e >> 1] = pack_bf16x2(pv[0], pv[1]);
+        const float h0 = __uint_as_float(ph[e >> 1] << 16), h1 = __uint_as_float(ph[e >> 1] & 0xFFFF0000u);
+        pl[e >> 1] = pack_bf16x2(pv[0] - h0, pv[1] - h1);
       }
       l_run += psum;
+      const bf16x8 pf0 = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+      const bf16x8 pf1 = __builtin_bit_cast(bf16x8, u32x4{ph[4], ph[5], ph[6], ph[7]});
+      const bf16x8 pg0 = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+      const bf16x8 pg1 = __builtin_bit_cast(bf16x8, u32x4{pl[4], pl[5], pl[6], pl[7]});
 
-      // ---- exchange P with the partner wave (same heads, other 32 slots) ----
-      // The high parts go through s_p; the low parts through the RoPE chunk
-      // columns 64..71 of the current tile, which PV does not read and every
-      // wave has finished reading for QK (the s_max barrier above).
-      uint8_t* s_plo = const_cast<uint8_t*>(tile) + 64 * 1024;
-      *(u32x4*)(s_p + ((wave * 2 + 0) * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-      *(u32x4*)(s_p + ((wave * 2 + 1) * 64 + lane) * 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
-      *(u32x4*)(s_plo + ((wave * 2 + 0) * 64 + lane) * 16) = u32x4{pl[0], pl[1], pl[2], pl[3]};
-      *(u32x4*)(s_plo + ((wave * 2 + 1) * 64 + lane) * 16) = u32x4{pl[4], pl[5], pl[6], pl[7]};
-      lds_barrier();
-      bf16x8 pf[4], pg[4];        // B operands per k-step: hi, lo
-      {
-        const u32x4 o0 = *(const u32x4*)(s_p + ((partner * 2 + 0) * 64 + lane) * 16);
-        const u32x4 o1 = *(const u32x4*)(s_p + ((partner * 2 + 1) * 64 + lane) * 16);
-        const u32x4 m0 = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        const u32x4 m1 = u32x4{pk[4], pk[5], pk[6], pk[7]};
-        // k-step kst covers slots [16kst, 16kst+16), owned by wave half kst/2.
-        pf[0] = __builtin_bit_cast(bf16x8, x == 0 ? m0 : o0);
-        pf[1] = __builtin_bit_cast(bf16x8, x == 0 ? m1 : o1);
-        pf[2] = __builtin_bit_cast(bf16x8, x == 1 ? m0 : o0);
-        pf[3] = __builtin_bit_cast(bf16x8, x == 1 ? m1 : o1);
-        const u32x4 q0 = *(const u32x4*)(s_plo + ((partner * 2 + 0) * 64 + lane) * 16);
-        const u32x4 q1 = *(const u32x4*)(s_plo + ((partner * 2 + 1) * 64 + lane) * 16);
-        const u32x4 n0 = u32x4{pl[0], pl[1], pl[2], pl[3]};
-        const u32x4 n1 = u32x4{pl[4], pl[5], pl[6], pl[7]};
-        pg[0] = __builtin_bit_cast(bf16x8, x == 0 ? n0 : q0);
-        pg[1] = __builtin_bit_cast(bf16x8, x == 0 ? n1 : q1);
-        pg[2] = __builtin_bit_cast(bf16x8, x == 1 ? n0 : q0);
-        pg[3] = __builtin_bit_cast(bf16x8, x == 1 ? n1 : q1);
-      }
-
-      // ---- O^T += V^T . P^T over this wave's 256 columns ---------------------
-      {
-        const int i16 = lane & 15;
-        const int nhalf = (lane >> 4) & 1;
-        const int cb = 2 * nhalf + ((i16 & 3) >> 1);   // chunk & 3 of this lane's reads
-        const int half8 = (i16 & 1) * 8;
-        const uint8_t* vb0 = tile + (32 * x + cb) * 1024 + (((4 * g + (i16 >> 2)) ^ (4 * cb)) * 16) + half8;
-        const uint8_t* vb1 = tile + (32 * x + cb) * 1024 + (((8 + 4 * g + (i16 >> 2)) ^ (4 * cb)) * 16) + half8;
+      // ---- O^T += V^T . P^T: 32 column tiles x 2 k-steps x (hi, lo) ----------
+      const uint32_t tlv = lds_addr(tile);
+      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]),
+                                 opaque(tlv + vb[3])};
+      // Software pipeline: the V^T fragments of column tile ct+2 are requested
+      // before the MFMAs of ct are issued.
+      auto vfrag = [&](int ct, int kk) -> bf16x8 {
+        const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
+        const i16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)(vp + 2048));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, v1);
+        return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+      };
+      bf16x8 vf[3][2];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
+      for (int kk = 0; kk < 2; ++kk) { vf[0][kk] = vfrag(0, kk); vf[1][kk] = vfrag(1, kk); }
 #pragma unroll
-          for (int kst = 0; kst < 4; ++kst) {
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(vb0 + 4096 * ct + 256 * kst));
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(vb1 + 4096 * ct + 256 * kst));
-            const u32x2 w0 = __builtin_bit_cast(u32x2, v0);
-            const u32x2 w1 = __builtin_bit_cast(u32x2, v1);
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kst], acc[ct], 0, 0, 0);
-            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pg[kst], acc[ct], 0, 0, 0);
-          }
+      for (int ct = 0; ct < 32; ++ct) {
+        if (ct + 2 < 32) {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) vf[(ct + 2) % 3][kk] = vfrag(ct + 2, kk);
         }
+        __builtin_amdgcn_sched_barrier(0);       // keep the reads two column tiles ahead
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % 3][kk], kk ? pf1 : pf0, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % 3][kk], kk ? pg1 : pg0, acc[ct], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       vmask_cur = vmask_nxt;
       sc_cur = sc_nxt;
       idx_nxt = idx_after;
     }
+    // A score beyond the frame anywhere in the workgroup: run the job again
+    // from zero with every head's frame at the largest score it has seen.
+    if (pass == 0) {
+      if (__any(overflow) && lane == 0) s_restart = 1;
+      lds_barrier();
+      if (s_restart == 0) break;
+      M_run = floorf(m_seen);
+      l_run = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    }
   }
 
   // ---- epilogue: full denominator of this lane's head -----------------------
-  const float l_wave = l_run + __shfl_xor(l_run, 32);
-  if (lane < 32) s_l[x][hh] = l_wave;
-  lds_barrier();
-  const float l_head = s_l[0][hh] + s_l[1][hh];
+  float l_head = l_run + __shfl_xor(l_run, 16);
+  l_head += __shfl_xor(l_head, 32);
   const bool any = l_head > 0.f;
   const float lse = any ? M_run + __builtin_amdgcn_logf(l_head) : kNegInf;
   float oscale = any ? 1.0f / l_head : 0.f;
-  const bool head_ok = hh < a.h_q;
+  const bool head_ok = head < a.h_q;
 
   if (!DIRECT) {
-    const int64_t row = ((int64_t)job.s * a.s_q + t) * a.h_q + hh;
+    const int64_t row = ((int64_t)job.s * a.s_q + t) * a.h_q + head;
     if (head_ok) {
-      float* orow = a.o_accum + row * 512;
+      float* orow = a.o_accum + row * 512 + 4 * G;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = 256 * x + 32 * ct + 8 * q4 + 4 * g;
-          f32x4 v = {acc[ct][4 * q4 + 0] * oscale, acc[ct][4 * q4 + 1] * oscale,
-                     acc[ct][4 * q4 + 2] * oscale, acc[ct][4 * q4 + 3] * oscale};
-          *(f32x4*)(orow + col) = v;
-        }
-      if (x == 0 && g == 0) a.lse_accum[row] = lse;
+      for (int ct = 0; ct < 32; ++ct) *(f32x4*)(orow + 16 * ct) = acc[ct] * oscale;
+      if (G == 0) a.lse_accum[row] = lse;
     }
   } else {
     if (a.sink != nullptr && any && head_ok) {
-      const float z = a.sink[hh] * kLog2e - lse;
+      const float z = a.sink[head] * kLog2e - lse;
       oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
     }
-    const int64_t row = (int64_t)t * a.h_q + hh;
+    const int64_t row = (int64_t)t * a.h_q + head;
     if (a.out_dtype == kOutFp8) {
       float amax = 0.f;
       if (head_ok)
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 32; ++ct)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[ct][i] * oscale));
+          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[ct][i] * oscale));
       amax = warp_max(amax);
       if (lane == 0) s_red[wave] = amax;
       lds_barrier();
@@ -501,139 +521,152 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       const float qscale = amax > 0.f ? amax / 448.0f : 1.0f;
       if (tid == 0) a.out_scale[t] = qscale;
       if (head_ok) {
-        uint8_t* orow = (uint8_t*)a.out + row * 512;
+        uint8_t* orow = (uint8_t*)a.out + row * 512 + 4 * G;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 32; ++ct) {
+          uint32_t w = 0;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int col = 256 * x + 32 * ct + 8 * q4 + 4 * g;
-            uint32_t w = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w |= e4m3_encode((acc[ct][4 * q4 + e] * oscale) / qscale) << (8 * e);
-            *(uint32_t*)(orow + col) = w;
-          }
+          for (int i = 0; i < 4; ++i) w |= e4m3_encode((acc[ct][i] * oscale) / qscale) << (8 * i);
+          *(uint32_t*)(orow + 16 * ct) = w;
+        }
       }
     } else if (head_ok) {
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = 256 * x + 32 * ct + 8 * q4 + 4 * g;
-          const float v0 = acc[ct][4 * q4 + 0] * oscale, v1 = acc[ct][4 * q4 + 1] * oscale;
-          const float v2 = acc[ct][4 * q4 + 2] * oscale, v3 = acc[ct][4 * q4 + 3] * oscale;
-          if (a.out_dtype == kOutF32) {
-            *(f32x4*)((float*)a.out + row * 512 + col) = f32x4{v0, v1, v2, v3};
-          } else {
-            *(u32x2*)((uint16_t*)a.out + row * 512 + col) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          }
+      for (int ct = 0; ct < 32; ++ct) {
+        const f32x4 v = acc[ct] * oscale;
+        if (a.out_dtype == kOutF32) {
+          *(f32x4*)((float*)a.out + row * 512 + 16 * ct + 4 * G) = v;
+        } else {
+          *(u32x2*)((uint16_t*)a.out + row * 512 + 16 * ct + 4 * G) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
+      }
     }
-    if (a.lse_out != nullptr && head_ok && x == 0 && g == 0) a.lse_out[row] = lse;
+    if (a.lse_out != nullptr && head_ok && G == 0) a.lse_out[row] = lse;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Combine: O = sum_s 2^(LSE_s - M) O_s / sum_s 2^(LSE_s - M), then the sink and
-// the cast.  bf16 / fp32 outputs: 128 threads per (token, head), 4 columns
-// each.  FP8 output: one workgroup per token so the amax is a local reduction.
+// the cast.  The per-split weights of a (token, head) are computed once into
+// LDS; every thread then issues its split loads back to back.
 // ---------------------------------------------------------------------------
-struct Merged {
-  float lse, M, inv_w;
-  bool any;
-};
+constexpr int kMaxSplits = SMLA_MAX_SPLITS;
 
-__device__ __forceinline__ Merged merge_weights(const CombineArgs& a, int t, int h) {
+// Weights of head h of token t into w[0..S), plus the merged LSE and 1/sum.
+// Called by the 64 lanes of one wave; lane s loads split s (S <= 64).
+__device__ __forceinline__ void head_weights(const CombineArgs& a, int t, int h, float* w, float& lse,
+                                             float& inv_w) {
+  const int lane = threadIdx.x & 63;
   const int64_t stride = (int64_t)a.s_q * a.h_q;
-  const float* lp = a.lse_accum + (int64_t)t * a.h_q + h;
-  float M = kNegInf;
-  for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, lp[s * stride]);
-  Merged m;
-  m.M = M;
-  m.any = M != kNegInf;
-  float wsum = 0.f;
-  if (m.any)
-    for (int s = 0; s < a.num_splits; ++s) {
-      const float ls = lp[s * stride];
-      wsum += (ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls - M);
-    }
-  m.lse = m.any ? M + __builtin_amdgcn_logf(wsum) : kNegInf;
-  m.inv_w = m.any ? 1.0f / wsum : 0.f;
-  return m;
+  const float ls = lane < a.num_splits ? a.lse_accum[lane * stride + (int64_t)t * a.h_q + h] : kNegInf;
+  const float M = warp_max(ls);
+  const float wl = (M == kNegInf || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls - M);
+  float ws = wl;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
+  if (lane < a.num_splits) w[lane] = wl;
+  lse = M == kNegInf ? kNegInf : M + __builtin_amdgcn_logf(ws);
+  inv_w = M == kNegInf ? 0.f : 1.0f / ws;
 }
 
-__device__ __forceinline__ f32x4 merge_columns(const CombineArgs& a, const Merged& m, int t, int h, int col) {
-  const int64_t stride = (int64_t)a.s_q * a.h_q;
-  const float* lp = a.lse_accum + (int64_t)t * a.h_q + h;
+__device__ __forceinline__ f32x4 merge_columns(const CombineArgs& a, const float* w, float inv_w, float lse,
+                                               int t, int h, int col) {
+  const int64_t stride = (int64_t)a.s_q * a.h_q * 512;
   const float* op = a.o_accum + ((int64_t)t * a.h_q + h) * 512 + col;
-  if (!m.any) return f32x4{0.f, 0.f, 0.f, 0.f};
+  if (inv_w == 0.f) return f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 o = {-0.f, -0.f, -0.f, -0.f};     // IEEE additive identity: keeps the sign of -0 terms
-  for (int s = 0; s < a.num_splits; ++s) {
-    const float ls = lp[s * stride];
-    if (ls == kNegInf) continue;
-    const float w = __builtin_amdgcn_exp2f(ls - m.M);
-    const f32x4 v = *(const f32x4*)(op + s * stride * 512);
-    o += w * v;
+  int s = 0;
+  for (; s + 4 <= a.num_splits; s += 4) {
+    const f32x4 v0 = *(const f32x4*)(op + (s + 0) * stride);
+    const f32x4 v1 = *(const f32x4*)(op + (s + 1) * stride);
+    const f32x4 v2 = *(const f32x4*)(op + (s + 2) * stride);
+    const f32x4 v3 = *(const f32x4*)(op + (s + 3) * stride);
+    o += w[s + 0] * v0;
+    o += w[s + 1] * v1;
+    o += w[s + 2] * v2;
+    o += w[s + 3] * v3;
   }
-  float f = m.inv_w;
-  if (a.sink != nullptr) f = f / (1.0f + __builtin_amdgcn_exp2f(a.sink[h] * kLog2e - m.lse));
+  for (; s < a.num_splits; ++s) o += w[s] * *(const f32x4*)(op + s * stride);
+  float f = inv_w;
+  if (a.sink != nullptr) f = f / (1.0f + __builtin_amdgcn_exp2f(a.sink[h] * kLog2e - lse));
   return o * f;
 }
 
+// bf16 / fp32 output: 4 heads per block, one wave per head, 8 columns per lane.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const int hpb = 2;                               // heads per block
-  const int blocks_per_token = (a.h_q + hpb - 1) / hpb;
-  const int t = blockIdx.x / blocks_per_token;
-  const int h = (blockIdx.x - t * blocks_per_token) * hpb + (threadIdx.x >> 7);
+  __shared__ float s_w[4][kMaxSplits];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bpt = (a.h_q + 3) / 4;
+  const int t = blockIdx.x / bpt;
+  const int h = (blockIdx.x - t * bpt) * 4 + wave;
   if (h >= a.h_q) return;
-  const int col = (threadIdx.x & 127) * 4;
-  const Merged m = merge_weights(a, t, h);
-  const f32x4 o = merge_columns(a, m, t, h, col);
+  float lse, inv_w;
+  head_weights(a, t, h, s_w[wave], lse, inv_w);    // the same wave reads the weights back
+  __builtin_amdgcn_wave_barrier();
   const int64_t row = (int64_t)t * a.h_q + h;
-  if (a.out_dtype == kOutF32) {
-    *(f32x4*)((float*)a.out + row * 512 + col) = o;
-  } else {
-    *(u32x2*)((uint16_t*)a.out + row * 512 + col) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int col = 256 * half + 4 * lane;
+    const f32x4 o = merge_columns(a, s_w[wave], inv_w, lse, t, h, col);
+    if (a.out_dtype == kOutF32) {
+      *(f32x4*)((float*)a.out + row * 512 + col) = o;
+    } else {
+      *(u32x2*)((uint16_t*)a.out + row * 512 + col) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
   }
-  if (a.lse_out != nullptr && (threadIdx.x & 127) == 0) a.lse_out[row] = m.lse;
+  if (a.lse_out != nullptr && lane == 0) a.lse_out[row] = lse;
 }
 
-// FP8 output: 1024 threads per token; 16 threads per head, 32 columns each.
+// FP8 output: one workgroup (16 waves) per token so the amax is a local
+// reduction; wave w merges heads w, w+16, ...
 __global__ __launch_bounds__(1024) void combine_fp8_kernel(CombineArgs a) {
+  __shared__ float s_w[16][kMaxSplits];
   __shared__ float s_red[16];
   const int t = blockIdx.x;
-  const int h = threadIdx.x >> 4;
-  const int sub = threadIdx.x & 15;
-  const bool hv = h < a.h_q;
-  f32x4 o[8];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  f32x4 o[4][2];
   float amax = 0.f;
-  Merged m = {kNegInf, kNegInf, 0.f, false};
-  if (hv) {
-    m = merge_weights(a, t, h);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      o[k] = merge_columns(a, m, t, h, (k * 16 + sub) * 4);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[k][0]), fabsf(o[k][1])), fmaxf(fabsf(o[k][2]), fabsf(o[k][3]))));
+  for (int k = 0; k < 4; ++k) {
+    const int h = wave + 16 * k;
+    o[k][0] = o[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (h < a.h_q) {
+      float lse, inv_w;
+      head_weights(a, t, h, s_w[wave], lse, inv_w);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        o[k][half] = merge_columns(a, s_w[wave], inv_w, lse, t, h, 256 * half + 4 * lane);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[k][half][0]), fabsf(o[k][half][1])),
+                                 fmaxf(fabsf(o[k][half][2]), fabsf(o[k][half][3]))));
+      }
+      if (a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)t * a.h_q + h] = lse;
+      __builtin_amdgcn_wave_barrier();
     }
   }
   amax = warp_max(amax);
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = amax;
+  if (lane == 0) s_red[wave] = amax;
   __syncthreads();
   amax = 0.f;
 #pragma unroll
   for (int w = 0; w < 16; ++w) amax = fmaxf(amax, s_red[w]);
   const float qscale = amax > 0.f ? amax / 448.0f : 1.0f;
   if (threadIdx.x == 0) a.out_scale[t] = qscale;
-  if (!hv) return;
-  const int64_t row = (int64_t)t * a.h_q + h;
-  uint8_t* orow = (uint8_t*)a.out + row * 512;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    uint32_t w = 0;
+  for (int k = 0; k < 4; ++k) {
+    const int h = wave + 16 * k;
+    if (h < a.h_q) {
+      uint8_t* orow = (uint8_t*)a.out + ((int64_t)t * a.h_q + h) * 512;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w |= e4m3_encode(o[k][e] / qscale) << (8 * e);
-    *(uint32_t*)(orow + (k * 16 + sub) * 4) = w;
+      for (int half = 0; half < 2; ++half) {
+        uint32_t wd = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wd |= e4m3_encode(o[k][half][e] / qscale) << (8 * e);
+        *(uint32_t*)(orow + 256 * half + 4 * lane) = wd;
+      }
+    }
   }
-  if (a.lse_out != nullptr && sub == 0) a.lse_out[row] = m.lse;
 }
 
 }  // namespace
@@ -660,7 +693,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.out_dtype == kOutFp8) {
     hipLaunchKernelGGL(combine_fp8_kernel, dim3((unsigned)a.s_q), dim3(1024), 0, stream, a);
   } else {
-    const unsigned blocks = (unsigned)(a.s_q * ((a.h_q + 1) / 2));
+    const unsigned blocks = (unsigned)(a.s_q * ((a.h_q + 3) / 4));
     hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
