@@ -74,6 +74,12 @@ def parse_args():
     ap.add_argument("--kernel-reps", type=int, default=100)
     ap.add_argument("--copy-only", action="store_true",
                     help="run only a plain 256 MiB device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--kernel-stats", metavar="DIR",
+                    help="print a summary of a rocprofv3 --kernel-trace --stats output directory and exit")
+    ap.add_argument("--hbm-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output directories of this bench "
+                         "(--no-sweep) and of --copy-only: print the calibrated HBM bytes per launch of the "
+                         "attention kernel, write them to the traffic record, and exit")
     return ap.parse_args()
 
 
@@ -160,30 +166,36 @@ def sleep_cycles_for(ms, torch):
 
 
 def kernel_durations(layers, S, reps, torch, smla):
-    """Mean duration (us) of the attention kernel and of the combine, each bracketed by HIP
-    events on the stream it is launched on.  A GPU sleep queued first keeps the stream
-    backed up, so every event pair brackets its kernel alone."""
+    """Mean duration (us) of the attention kernel and of the combine, from HIP events on
+    the stream they are launched on.  Each kernel is timed as a batch of `reps`
+    back-to-back launches bracketed by one event pair; a GPU sleep queued first keeps
+    the stream backed up so the launches run without host gaps.  S == 1 times the
+    direct path (one kernel per step)."""
     s_q = layers[0].inp.s_q
     scale = layers[0].inp.scale
-    o_acc = torch.empty((S, s_q, 64, 512), device="cuda")
-    lse_acc = torch.empty((S, s_q, 64), device="cuda")
     stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
-    cyc = sleep_cycles_for(5 + reps * 0.25, torch)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(cyc)
-    for i in range(reps):
-        L = layers[i % len(layers)]
-        evs[i][0].record(stream)
-        smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, sink=L.sink, o_accum=o_acc, lse_accum=lse_acc)
-        evs[i][1].record(stream)
-        smla.combine_splits(o_acc, lse_acc, S, L.out, sink=L.sink)
-        evs[i][2].record(stream)
-    torch.cuda.synchronize()
-    main = np.array([a.elapsed_time(b) * 1e3 for a, b, _ in evs])
-    comb = np.array([b.elapsed_time(c) * 1e3 for _, b, c in evs])
-    gaps = np.array([evs[i][2].elapsed_time(evs[i + 1][0]) * 1e3 for i in range(reps - 1)])
-    return float(main.mean()), float(comb.mean()), float(np.median(gaps)) if gaps.size else 0.0
+    o_acc = torch.empty((S, s_q, 64, 512), device="cuda") if S > 1 else None
+    lse_acc = torch.empty((S, s_q, 64), device="cuda") if S > 1 else None
+
+    def batch(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cyc = sleep_cycles_for(5 + reps * 0.1, torch)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(cyc)
+        e0.record(stream)
+        for i in range(reps):
+            fn(layers[i % len(layers)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    if S == 1:
+        main = batch(lambda L: smla.sparse_mla_decode(L.q, L.kv, L.indices, 1, scale, sink=L.sink, out=L.out))
+        return main, 0.0
+    main = batch(lambda L: smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, sink=L.sink,
+                                                  o_accum=o_acc, lse_accum=lse_acc))
+    comb = batch(lambda L: smla.combine_splits(o_acc, lse_acc, S, L.out, sink=L.sink))
+    return main, comb
 
 
 def traffic_for(S):
@@ -230,31 +242,83 @@ def measure(name, S_arg, steps, warmup, reps, torch, smla, W):
     S = S_arg or smla.smla_choose_num_splits(s_q, 64, 640, 256)
     layers = build_layers(s_q, n_pool, torch, W)
     us, ev_us, k, w = time_steps(layers, S, steps, warmup, torch, smla)
-    main_us, comb_us, gap = kernel_durations(layers, S, reps, torch, smla) if S > 1 else (None, None, None)
-    if S == 1:
-        # direct path: one kernel per step
-        main_us, comb_us, gap = _direct_durations(layers, reps, torch, smla)
+    main_us, comb_us = kernel_durations(layers, S, reps, torch, smla)
     step_gbs = STEP_BYTES_PER_TOKEN * s_q / (ev_us * 1e-6) / 1e9
     return dict(name=name, s_q=s_q, n_pool=n_pool, S=S, us=us, ev_us=ev_us, steps=k, warmup=w,
-                main_us=main_us, comb_us=comb_us, gap_us=gap, step_tbps=step_gbs / 1e3,
+                main_us=main_us, comb_us=comb_us, step_tbps=step_gbs / 1e3,
                 layers=len(layers)), layers
 
 
-def _direct_durations(layers, reps, torch, smla):
-    scale = layers[0].inp.scale
-    stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-    cyc = sleep_cycles_for(5 + reps * 0.15, torch)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(cyc)
-    for i in range(reps):
-        L = layers[i % len(layers)]
-        evs[i][0].record(stream)
-        smla.sparse_mla_decode(L.q, L.kv, L.indices, 1, scale, sink=L.sink, out=L.out)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    main = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-    return float(main.mean()), 0.0, 0.0
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def summarize_kernel_stats(directory):
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+    for r in rows:
+        print(f"{r['Name'][:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.3f} "
+              f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
+
+
+def _counter_per_dispatch(directory, counter):
+    """{kernel name: mean counter value per dispatch} from a rocprofv3 --pmc run."""
+    tot, disp = {}, {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        k = r["Kernel_Name"]
+        tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+        disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def hbm_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, scaled by what the
+    same counters read for a plain copy of 256 MiB (read and written once)."""
+    copy_kib = (256 << 20) / 1024.0
+
+    def pick(d, key):
+        hits = [v for k, v in d.items() if key in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {key!r}, found {sorted(d)}")
+        return hits[0]
+
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    f_copy = pick(_counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE"), "copyBuffer")
+    w_copy = pick(_counter_per_dispatch(copy_write_dir, "WRITE_SIZE"), "copyBuffer")
+    rf, wf = copy_kib / f_copy, copy_kib / w_copy
+    print(f"copy calibration: 256 MiB copy reads FETCH_SIZE {f_copy:.1f} KiB -> read factor {rf:.3f}; "
+          f"WRITE_SIZE {w_copy:.1f} KiB -> write factor {wf:.3f}")
+    print(f"{'kernel':64s} {'FETCH_KiB':>10s} {'WRITE_KiB':>10s} {'HBM_bytes':>12s}")
+    for k in sorted(set(fetch) | set(write)):
+        b = (fetch.get(k, 0.0) * rf + write.get(k, 0.0) * wf) * 1024
+        print(f"{k[:64]:64s} {fetch.get(k, 0.0):10.1f} {write.get(k, 0.0):10.1f} {b:12.0f}")
+    kf, kw = pick(fetch, "decode_kernel"), pick(write, "decode_kernel")
+    rec = {"kernel": "decode_kernel<bf16 pool, partial>", "workload": "single",
+           "num_splits": _single_splits(),
+           "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kw, 1),
+           "read_factor": round(rf, 4), "write_factor": round(wf, 4),
+           "hbm_bytes_per_launch": int(round((kf * rf + kw * wf) * 1024)),
+           "kernel_source_sha256": source_hash()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def _single_splits():
+    from sparse_mla_decode_top_amd import binding
+    return binding.smla_choose_num_splits(WORKLOADS["single"][0], 64, 640, 256)
 
 
 def copy_only(torch):
@@ -270,6 +334,12 @@ def copy_only(torch):
 
 def main():
     args = parse_args()
+    if args.kernel_stats:
+        summarize_kernel_stats(args.kernel_stats)
+        return
+    if args.hbm_counters:
+        hbm_counters(*args.hbm_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
               file=sys.stderr, flush=True)
