@@ -56,9 +56,16 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 64;                         // slots per KV block
 constexpr int kTileBytes = kBlk * 1152;          // 64 bf16 rows of 576
 constexpr int kCodeTileBytes = kBlk * 576;       // 64 e4m3 rows of 576
+constexpr int kQOffset = kTileBytes;             // LDS byte offset of the staged Q rows
+constexpr int kStagePitch = 2064;                // LDS pitch of a staged fp32 output row (2048 + 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kFrameSlack = 64.0f;     // scores may exceed a head's frame M by this much
+// Score of a masked slot: finite, so that the branch-free weight below gives
+// exactly 0 for it (floor and fraction stay defined), and below any real score.
+constexpr float kMaskedScore = -3.0e38f;
+// Frame of a head that has not seen a valid slot yet: every weight is then 0.
+constexpr float kNoFrame = 3.0e38f;
 
 enum OutDtype { kOutBf16 = 0, kOutF32 = 1, kOutFp8 = 2 };
 
@@ -94,8 +101,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // inserts a vmcnt wait in front of the LDS reads of the other tile buffer (it
 // cannot tell the prefetch buffer from the one being read); the kernel waits
 // explicitly.  m0 is saved and restored; one wait state follows each m0 write.
-#define SMLA_DMA(M0STEP, OFF) \
-  "s_add_u32 m0, m0, " #M0STEP "\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:" #OFF "\n\t"
+#define SMLA_DMA_OP(OPND, M0STEP, OFF) \
+  "s_add_u32 m0, m0, " #M0STEP "\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %" #OPND ", off offset:" #OFF "\n\t"
+#define SMLA_DMA(M0STEP, OFF) SMLA_DMA_OP(1, M0STEP, OFF)
 // bf16 tile: octet o of a row -> global +128o, LDS +8192o  (m0 step 8064)
 __device__ __forceinline__ void dma_octets(const void* gptr, uint32_t lds_base_uniform) {
   uint32_t saved;
@@ -128,7 +136,39 @@ __device__ __forceinline__ void dma_quartets(const void* gptr, uint32_t lds_base
       : "v"(gptr), "s"(lds_base_uniform)
       : "memory");
 }
+// First index of a job and its Q rows in one block: the index load is issued,
+// then the 2 x 9 Q-row DMAs of this wave (two groups of 8 rows, as a KV
+// gather), and only the index is waited for (vmcnt counts completions in issue
+// order, so the 18 DMAs stay in flight).  One asm statement, so that the
+// compiler neither reads the index register before it has landed nor adds a
+// wait of its own that would cover the DMAs.
+__device__ __forceinline__ int load_idx_and_q(const int32_t* idx_ptr, const void* q0, const void* q1,
+                                              uint32_t lds0_uniform, uint32_t lds1_uniform) {
+  int idx;
+  uint32_t saved;
+  asm volatile(
+      "global_load_dword %0, %2, off nt\n\t"
+      "s_mov_b32 %1, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      SMLA_DMA_OP(3, 8064, 128) SMLA_DMA_OP(3, 8064, 256) SMLA_DMA_OP(3, 8064, 384) SMLA_DMA_OP(3, 8064, 512)
+      SMLA_DMA_OP(3, 8064, 640) SMLA_DMA_OP(3, 8064, 768) SMLA_DMA_OP(3, 8064, 896) SMLA_DMA_OP(3, 8064, 1024)
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, off\n\t"
+      SMLA_DMA_OP(4, 8064, 128) SMLA_DMA_OP(4, 8064, 256) SMLA_DMA_OP(4, 8064, 384) SMLA_DMA_OP(4, 8064, 512)
+      SMLA_DMA_OP(4, 8064, 640) SMLA_DMA_OP(4, 8064, 768) SMLA_DMA_OP(4, 8064, 896) SMLA_DMA_OP(4, 8064, 1024)
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_waitcnt vmcnt(18)"
+      : "=&v"(idx), "=&s"(saved)
+      : "v"(idx_ptr), "v"(q0), "v"(q1), "s"(lds0_uniform), "s"(lds1_uniform)
+      : "memory");
+  return idx;
+}
 #undef SMLA_DMA
+#undef SMLA_DMA_OP
 
 // Hides a value from the optimiser, so that an address computed from it inside
 // the loop keeps its constant parts as instruction offsets instead of being
@@ -149,6 +189,22 @@ __device__ __forceinline__ float warp_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
+}
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// with the gfx950 row-swap moves: each swap hands every lane the value of its
+// partner row, with no LDS round trip.
+__device__ __forceinline__ float rows_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // e4m3fn code of a finite fp32 value, round to nearest even, saturating at
@@ -202,7 +258,8 @@ template <bool KV_FP8, bool DIRECT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeArgs a) {
   // bf16 pool: two tiles.  FP8 pool: two code tiles + one bf16 tile.
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
-  __shared__ float s_scale[2][kBlk];
+  __shared__ __attribute__((aligned(16))) float s_scale[2][kBlk];
+  __shared__ __attribute__((aligned(16))) float s_bias[2][kBlk];   // 0: valid slot, kMaskedScore: masked
   __shared__ float s_red[kWaves];
   __shared__ int s_restart;
 
@@ -217,36 +274,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int t = job.t;
   const int32_t* idx_row = a.indices + (int64_t)t * a.topk;
 
-  float M_run = kNegInf;              // integer frame of this lane's head (log2 units)
-  float m_seen = kNegInf;             // largest score seen so far
+  float M_run = kNoFrame;             // integer frame of this lane's head (log2 units)
+  float m_seen = kMaskedScore;        // largest score seen so far
   float l_run = 0.f;                  // this lane's share of the denominator
   if (tid == 0) s_restart = 0;        // ordered before its readers by the loop barriers
+  bool restarted = false;
   f32x4 acc[32];                      // O^T: column tile ct -> columns 16ct + 4G + i
 #pragma unroll
   for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (job.b0 < job.b1) {
+    // Lane l holds the index of slot l of a block.  The load address is clamped
+    // into the token's list so that it is issued unconditionally (no divergent
+    // branch, hence no early wait on it); slots past the split or the list are
+    // masked where the index is used.
     auto load_idx = [&](int b) -> int {
-      const int slot = b * kBlk + lane;
-      return (b < job.b1 && slot < a.topk) ? __builtin_nontemporal_load(idx_row + slot) : -1;
+      return __builtin_nontemporal_load(idx_row + min(b * kBlk + lane, a.topk - 1));
     };
+    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < a.topk; };
     auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
-    int idx_cur = load_idx(job.b0);          // lane l: slot l of the block
-    int idx_nxt = load_idx(job.b0 + 1);
     const float scale_log2 = a.scale_log2;
-
     // Q fragments (B operand of S^T = K . Q^T): head, dims 32ks + 8G .. +8.
     bf16x8 qf[18];
-    {
-      const bool hv = head < a.h_q;
-      const uint16_t* qrow = a.q + ((int64_t)t * a.h_q + (hv ? head : 0)) * 576 + 8 * G;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        u32x4 v = *(const u32x4*)(qrow + 32 * ks);
-        if (!hv) v = u32x4{0u, 0u, 0u, 0u};
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
 
     const uint32_t tile_lds0 = lds_addr(s_tile);
     constexpr int kBufBytes = KV_FP8 ? kCodeTileBytes : kTileBytes;
@@ -296,30 +345,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
 
-    for (int pass = 0; pass < 2; ++pass) {
-    bool overflow = false;
-    if (pass > 0) {
-      idx_cur = load_idx(job.b0);
-      idx_nxt = load_idx(job.b0 + 1);
+    // ---- prologue -----------------------------------------------------------
+    // Q rows are copied into LDS (at kQOffset, a region the first block does not
+    // use) by the same 128-byte-per-row DMA as a KV gather, rows = heads, and
+    // read back in operand order: whole-line requests instead of 64-byte
+    // pieces of 16 rows per load.  Rows of heads >= h_q copy head 0 (their
+    // results are never stored).  The first block's index is waited for alone.
+    int idx_cur;
+    {
+      const int r0 = 16 * wave + (lane >> 3), r1 = r0 + 8;
+      const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
+      const uint8_t* qbase = (const uint8_t*)(a.q + (int64_t)t * a.h_q * 576);
+      idx_cur = load_idx_and_q(idx_row + min(job.b0 * kBlk + lane, a.topk - 1),
+                               qbase + (int64_t)(r0 < a.h_q ? r0 : 0) * 1152 + chunk,
+                               qbase + (int64_t)(r1 < a.h_q ? r1 : 0) * 1152 + chunk,
+                               __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + (2 * wave) * 1024),
+                               __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + (2 * wave + 1) * 1024));
     }
-    // ---- prologue: block b0 in flight ------------------------------------
-    uint64_t vmask_cur = __ballot(valid_of(idx_cur));
+
+    // One pass over the job's blocks; returns whether a score left the frame.
+    // Inlined twice (first pass, rare restart) rather than looped, so that the
+    // first pass's prologue shares no wait counts with a loop back edge.
+    auto run_pass = [&](const bool first) __attribute__((always_inline)) -> bool {
+    bool overflow = false;
+    if (!first) idx_cur = load_idx(job.b0);
+    // block b0 in flight; the next block's indices are requested behind it
+    idx_cur = slot_in(job.b0) ? idx_cur : -1;
     issue_gather(idx_cur, 0);
-    float sc_cur = (KV_FP8 && valid_of(idx_cur)) ? a.kv_scale[idx_cur] : 0.f;
+    int idx_nxt = load_idx(job.b0 + 1);
+    bool valid_cur = valid_of(idx_cur);
+    float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
+    if (first) {
+      wait_vmem_all();        // Q rows (and block b0) have landed
+      lds_barrier();
+      const uint32_t qt = lds_addr(s_tile) + kQOffset + wave * 2048;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
+        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
+      }
+      // The first iteration's barrier orders these reads before the block b0+1
+      // prefetch overwrites the Q rows.
+    }
 
     for (int b = job.b0; b < job.b1; ++b) {
       const int cur = (b - job.b0) & 1;
       wait_vmem_all();          // this wave's share of block b has landed
-      if (KV_FP8 && wave == 0) s_scale[cur][lane] = sc_cur;
+      if (wave == 0) {
+        s_bias[cur][lane] = valid_cur ? 0.f : kMaskedScore;
+        if (KV_FP8) s_scale[cur][lane] = sc_cur;
+      }
       lds_barrier();            // ... and every wave's; block b-1 fully consumed
 
       // Prefetch block b+1 (its indices were loaded one block ahead).
-      uint64_t vmask_nxt = 0;
+      bool valid_nxt = false;
       float sc_nxt = 0.f;
       if (b + 1 < job.b1) {
-        vmask_nxt = __ballot(valid_of(idx_nxt));
+        idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
         issue_gather(idx_nxt, cur ^ 1);
-        if (KV_FP8 && wave == 0 && valid_of(idx_nxt)) sc_nxt = a.kv_scale[idx_nxt];
+        valid_nxt = valid_of(idx_nxt);
+        if (KV_FP8 && wave == 0 && valid_nxt) sc_nxt = a.kv_scale[idx_nxt];
       }
       const int idx_after = load_idx(b + 2);
 
@@ -383,30 +468,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
 
       // ---- online softmax (log2 units, integer running max) -----------------
-      // lane holds head hl, slots 16st + 4G + i
+      // lane holds head hl, slots 16st + 4G + i.  A masked slot gets the score
+      // kMaskedScore from the block's bias row (its tile row is zero).
+      f32x4 bias[4], rsc[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bias[st] = *(const f32x4*)&s_bias[cur][16 * st + 4 * G];
+        if (KV_FP8) rsc[st] = *(const f32x4*)&s_scale[cur][16 * st + 4 * G];
+      }
       float tv[16];
-      float mloc = kNegInf;
+      float mloc = kMaskedScore;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int slot = 16 * st + 4 * G + i;
-          float sv = sacc[st][i] * scale_log2;
-          if (KV_FP8) sv *= s_scale[cur][slot];
-          const bool v = (vmask_cur >> slot) & 1ull;
-          tv[4 * st + i] = v ? sv : kNegInf;
-          mloc = fmaxf(mloc, tv[4 * st + i]);
+          float sv;
+          if (KV_FP8)
+            sv = fmaf(sacc[st][i] * scale_log2, rsc[st][i], bias[st][i]);
+          else
+            sv = fmaf(sacc[st][i], scale_log2, bias[st][i]);
+          tv[4 * st + i] = sv;
+          mloc = fmaxf(mloc, sv);
         }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      mloc = rows_max(mloc);
       m_seen = fmaxf(m_seen, mloc);
       // The first contributing block fixes the frame (nothing is accumulated yet).
-      if (M_run == kNegInf && mloc != kNegInf) M_run = floorf(mloc);
+      if (M_run == kNoFrame && mloc > kMaskedScore) M_run = floorf(mloc);
       overflow |= mloc > M_run + kFrameSlack;
       const float M_new = M_run;
 
       // P as bf16 hi + lo.  B operand of k-step kk: slots 32kk + 16(e/4) + 4G + (e%4),
       // i.e. this lane's own values of slot tiles 2kk and 2kk+1.
+      // p = 2^(t - floor t) * 2^(floor t - M), branch free: a masked slot or a
+      // head without a frame gets an exponent clamped to -256, i.e. p = 0.
       uint32_t ph[8], pl[8];
       float psum = 0.f;
 #pragma unroll
@@ -415,13 +509,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const float tt = tv[e + u];
-          float p = 0.f;
-          if (tt != kNegInf) {
-            const float fl = floorf(tt);
-            p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)fminf(fmaxf(fl - M_new, -200.f), 200.f));
-          }
+          const float fl = floorf(tt);
+          const float ex = __builtin_amdgcn_fmed3f(fl - M_new, -256.f, 256.f);
+          float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
           psum += p;
-          if (KV_FP8) p *= s_scale[cur][16 * ((e + u) >> 2) + 4 * G + ((e + u) & 3)];
+          if (KV_FP8) p *= rsc[(e + u) >> 2][(e + u) & 3];
           pv[u] = p;
         }
         ph[e >> 1] = pack_bf16x2(pv[0], pv[1]);
@@ -467,82 +559,104 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      vmask_cur = vmask_nxt;
+      valid_cur = valid_nxt;
       sc_cur = sc_nxt;
       idx_nxt = idx_after;
     }
+    return overflow;
+    };
+
+    const bool overflow = run_pass(true);
     // A score beyond the frame anywhere in the workgroup: run the job again
     // from zero with every head's frame at the largest score it has seen.
-    if (pass == 0) {
-      if (__any(overflow) && lane == 0) s_restart = 1;
-      lds_barrier();
-      if (s_restart == 0) break;
-      M_run = floorf(m_seen);
+    if (__any(overflow) && lane == 0) s_restart = 1;
+    lds_barrier();              // also: every wave is past its last tile read
+    if (s_restart != 0) {
+      restarted = true;
+      M_run = floorf(m_seen);   // a restart implies a valid score was seen
       l_run = 0.f;
 #pragma unroll
       for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      run_pass(false);
     }
   }
 
-  // ---- epilogue: full denominator of this lane's head -----------------------
-  float l_head = l_run + __shfl_xor(l_run, 16);
-  l_head += __shfl_xor(l_head, 32);
+  // ---- epilogue -------------------------------------------------------------
+  const float l_head = rows_sum(l_run);          // full denominator of this lane's head
   const bool any = l_head > 0.f;
   const float lse = any ? M_run + __builtin_amdgcn_logf(l_head) : kNegInf;
   float oscale = any ? 1.0f / l_head : 0.f;
-  const bool head_ok = head < a.h_q;
+  const bool wave_ok = 16 * wave < a.h_q;        // h_q is a multiple of 16
+  if (DIRECT && a.sink != nullptr && any && wave_ok) {
+    const float z = a.sink[head] * kLog2e - lse;
+    oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
+  }
 
-  if (!DIRECT) {
-    const int64_t row = ((int64_t)job.s * a.s_q + t) * a.h_q + head;
-    if (head_ok) {
-      float* orow = a.o_accum + row * 512 + 4 * G;
+  // The scaled rows go through LDS so that each global store instruction
+  // writes whole lines of one or two rows (a lane's accumulators hold 4
+  // columns of 32 column tiles, i.e. 64-byte pieces of 16 rows per store).
+  // Wave w stages its 16 heads x 512 fp32 at s_tile + w * 16 * kStagePitch;
+  // the 16-byte row padding keeps the 16-lane writes bank-conflict free.  A
+  // wave reads back only its own rows, and LDS keeps a wave's accesses in
+  // order, so no barrier is needed between the two.
+  if (restarted) lds_barrier();                  // a restarted pass ends with tiles in use
+  uint8_t* stg = s_tile + wave * 16 * kStagePitch;
+  float amax = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 32; ++ct) *(f32x4*)(orow + 16 * ct) = acc[ct] * oscale;
-      if (G == 0) a.lse_accum[row] = lse;
-    }
-  } else {
-    if (a.sink != nullptr && any && head_ok) {
-      const float z = a.sink[head] * kLog2e - lse;
-      oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
-    }
-    const int64_t row = (int64_t)t * a.h_q + head;
-    if (a.out_dtype == kOutFp8) {
-      float amax = 0.f;
-      if (head_ok)
+  for (int ct = 0; ct < 32; ++ct) {
+    const f32x4 v = acc[ct] * oscale;
+    if (DIRECT && wave_ok)
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    *(f32x4*)(stg + hl * kStagePitch + 64 * ct + 16 * G) = v;
+  }
+  float qscale = 1.0f;
+  if (DIRECT && a.out_dtype == kOutFp8) {        // per-token amax over every head
+    amax = warp_max(amax);
+    if (lane == 0) s_red[wave] = amax;
+    lds_barrier();
+    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    qscale = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (tid == 0) a.out_scale[t] = qscale;
+  }
+  if (wave_ok) {
+    const int64_t row0 = (DIRECT ? (int64_t)t * a.h_q : ((int64_t)job.s * a.s_q + t) * a.h_q) + 16 * wave;
+    if (!DIRECT || a.out_dtype == kOutF32) {     // one 1 KB half row per instruction
+      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + 4 * lane;
 #pragma unroll
-        for (int ct = 0; ct < 32; ++ct)
+      for (int j = 0; j < 32; ++j)
+        *(f32x4*)(dst + (j >> 1) * 512 + (j & 1) * 256) =
+            *(const f32x4*)(stg + (j >> 1) * kStagePitch + (j & 1) * 1024 + 16 * lane);
+    } else if (a.out_dtype == kOutBf16) {        // one 1 KB row per instruction
+      uint16_t* dst = (uint16_t*)a.out + row0 * 512 + 8 * lane;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[ct][i] * oscale));
-      amax = warp_max(amax);
-      if (lane == 0) s_red[wave] = amax;
-      lds_barrier();
-      amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-      const float qscale = amax > 0.f ? amax / 448.0f : 1.0f;
-      if (tid == 0) a.out_scale[t] = qscale;
-      if (head_ok) {
-        uint8_t* orow = (uint8_t*)a.out + row * 512 + 4 * G;
-#pragma unroll
-        for (int ct = 0; ct < 32; ++ct) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w |= e4m3_encode((acc[ct][i] * oscale) / qscale) << (8 * i);
-          *(uint32_t*)(orow + 16 * ct) = w;
-        }
+      for (int j = 0; j < 16; ++j) {
+        const f32x4 v0 = *(const f32x4*)(stg + j * kStagePitch + 32 * lane);
+        const f32x4 v1 = *(const f32x4*)(stg + j * kStagePitch + 32 * lane + 16);
+        *(u32x4*)(dst + j * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                         pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
       }
-    } else if (head_ok) {
+    } else {                                     // e4m3: two 512 B rows per instruction
+      uint8_t* dst = (uint8_t*)a.out + row0 * 512;
 #pragma unroll
-      for (int ct = 0; ct < 32; ++ct) {
-        const f32x4 v = acc[ct] * oscale;
-        if (a.out_dtype == kOutF32) {
-          *(f32x4*)((float*)a.out + row * 512 + 16 * ct + 4 * G) = v;
-        } else {
-          *(u32x2*)((uint16_t*)a.out + row * 512 + 16 * ct + 4 * G) =
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      for (int j = 0; j < 8; ++j) {
+        const int h = 2 * j + (lane >> 5);
+        const uint8_t* src = stg + h * kStagePitch + 64 * (lane & 31);
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x4 v = *(const f32x4*)(src + 16 * k);
+          w[k] = e4m3_encode(v[0] / qscale) | (e4m3_encode(v[1] / qscale) << 8) |
+                 (e4m3_encode(v[2] / qscale) << 16) | (e4m3_encode(v[3] / qscale) << 24);
         }
+        *(u32x4*)(dst + h * 512 + 16 * (lane & 31)) = w;
       }
     }
-    if (a.lse_out != nullptr && head_ok && G == 0) a.lse_out[row] = lse;
+    if (G == 0) {
+      if (!DIRECT)
+        a.lse_accum[row0 + hl] = lse;
+      else if (a.lse_out != nullptr)
+        a.lse_out[row0 + hl] = lse;
+    }
   }
 }
 
