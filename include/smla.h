@@ -128,9 +128,10 @@ smla_status combine_splits(const smla_params* p, int32_t num_splits, const float
  * smla_choose_num_splits -- a split count for the shape that gives small decode
  * batches enough (token, split) jobs to fill `num_cus` compute units and keeps
  * large batches unsplit ("The Split-K Dispatch", "The Reasoning Behind the
- * Design": the split count adapts to the batch).  Deterministic in its
- * arguments, so a captured graph stays valid.  Returns >= 1, or 0 when an
- * argument is non-positive.
+ * Design": the split count adapts to the batch): the largest S <= the block
+ * count with s_q * S <= num_cus, at least 1.  Deterministic in its arguments,
+ * so a captured graph stays valid.  Returns >= 1, or 0 when an argument is
+ * non-positive.
  */
 int32_t smla_choose_num_splits(int32_t s_q, int32_t h_q, int32_t topk, int32_t num_cus);
 

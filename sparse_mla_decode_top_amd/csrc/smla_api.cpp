@@ -51,11 +51,11 @@ size_t smla_partial_bytes(int32_t s_q, int32_t h_q, int32_t num_splits) {
 int32_t smla_choose_num_splits(int32_t s_q, int32_t h_q, int32_t topk, int32_t num_cus) {
   if (s_q < 1 || h_q < 1 || topk < 1 || num_cus < 1) return 0;
   const int32_t n_blk = n_blocks_of(topk);
-  // Enough (token, split) jobs for one workgroup per compute unit; batches
-  // that already give at least half the compute units a token stay unsplit,
-  // since the partials would add traffic there without adding parallelism.
-  if (2 * (int64_t)s_q >= num_cus) return 1;
-  int32_t s = (num_cus + s_q - 1) / s_q;
+  // As many splits as keep all s_q * S jobs within one round of one workgroup
+  // per compute unit.  A split count that spills into a second, partly
+  // filled round lengthens the step by a whole job; and once the tokens alone
+  // fill the compute units, splitting only adds partial traffic.
+  int32_t s = num_cus / s_q;
   if (s > n_blk) s = n_blk;
   if (s > SMLA_MAX_SPLITS) s = SMLA_MAX_SPLITS;
   return s < 1 ? 1 : s;

@@ -191,6 +191,15 @@ __device__ __forceinline__ float warp_max(float v) {
   return v;
 }
 
+// Butterfly reductions of a whole wave without LDS round trips: DPP swaps
+// inside each 16-lane row (lane ^ 1, ^ 2, then the 8- and 16-lane mirrors),
+// then the row swaps below.  Every lane ends with the same value: each step
+// combines two equal-shaped partial results with a commutative operation.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
 // with the gfx950 row-swap moves: each swap hands every lane the value of its
 // partner row, with no LDS round trip.
@@ -205,6 +214,20 @@ __device__ __forceinline__ float rows_sum(float v) {
   v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));        // quad_perm [1,0,3,2]: lane ^ 1
+  v = fmaxf(v, dpp<0x4E>(v));        // quad_perm [2,3,0,1]: lane ^ 2
+  v = fmaxf(v, dpp<0x141>(v));       // row_half_mirror: the other quad of the 8 lanes
+  v = fmaxf(v, dpp<0x140>(v));       // row_mirror: the other 8 lanes of the row
+  return rows_max(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = v + dpp<0xB1>(v);
+  v = v + dpp<0x4E>(v);
+  v = v + dpp<0x141>(v);
+  v = v + dpp<0x140>(v);
+  return rows_sum(v);
 }
 
 // e4m3fn code of a finite fp32 value, round to nearest even, saturating at
@@ -662,80 +685,97 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 // ---------------------------------------------------------------------------
 // Combine: O = sum_s 2^(LSE_s - M) O_s / sum_s 2^(LSE_s - M), then the sink and
-// the cast.  The per-split weights of a (token, head) are computed once into
-// LDS; every thread then issues its split loads back to back.
+// the cast.  One wave merges one (token, head) row: lane l owns columns
+// [4l, 4l+4) and [256+4l, 256+4l+4); lane s also loads split s's LSE.  The
+// partial rows of the first splits are requested together with the LSEs, so
+// the row loads do not wait for the weights.
 // ---------------------------------------------------------------------------
-constexpr int kMaxSplits = SMLA_MAX_SPLITS;
+constexpr int kMergeChunk = 8;       // partial rows in flight per lane: 8 splits x 2 x 16 B
 
-// Weights of head h of token t into w[0..S), plus the merged LSE and 1/sum.
-// Called by the 64 lanes of one wave; lane s loads split s (S <= 64).
-__device__ __forceinline__ void head_weights(const CombineArgs& a, int t, int h, float* w, float& lse,
-                                             float& inv_w) {
+struct Merged {
+  f32x4 lo, hi;                      // columns 4l.., 256+4l..
+  float lse;
+};
+
+__device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h) {
   const int lane = threadIdx.x & 63;
-  const int64_t stride = (int64_t)a.s_q * a.h_q;
-  const float ls = lane < a.num_splits ? a.lse_accum[lane * stride + (int64_t)t * a.h_q + h] : kNegInf;
-  const float M = warp_max(ls);
-  const float wl = (M == kNegInf || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls - M);
-  float ws = wl;
+  const int S = a.num_splits;
+  const int64_t row = (int64_t)t * a.h_q + h;
+  const int64_t ostride = (int64_t)a.s_q * a.h_q * 512;
+  const float* op = a.o_accum + row * 512 + 4 * lane;
+  const float ls = lane < S ? a.lse_accum[lane * (int64_t)a.s_q * a.h_q + row] : kNegInf;
+  // Split indices past S are clamped to S - 1 (an L1 hit on a row already
+  // requested) so the loads are unconditional and the LSE wait leaves them
+  // in flight; their terms are skipped below.
+  f32x4 v[kMergeChunk][2];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
-  if (lane < a.num_splits) w[lane] = wl;
-  lse = M == kNegInf ? kNegInf : M + __builtin_amdgcn_logf(ws);
-  inv_w = M == kNegInf ? 0.f : 1.0f / ws;
-}
-
-__device__ __forceinline__ f32x4 merge_columns(const CombineArgs& a, const float* w, float inv_w, float lse,
-                                               int t, int h, int col) {
-  const int64_t stride = (int64_t)a.s_q * a.h_q * 512;
-  const float* op = a.o_accum + ((int64_t)t * a.h_q + h) * 512 + col;
-  if (inv_w == 0.f) return f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 o = {-0.f, -0.f, -0.f, -0.f};     // IEEE additive identity: keeps the sign of -0 terms
-  int s = 0;
-  for (; s + 4 <= a.num_splits; s += 4) {
-    const f32x4 v0 = *(const f32x4*)(op + (s + 0) * stride);
-    const f32x4 v1 = *(const f32x4*)(op + (s + 1) * stride);
-    const f32x4 v2 = *(const f32x4*)(op + (s + 2) * stride);
-    const f32x4 v3 = *(const f32x4*)(op + (s + 3) * stride);
-    o += w[s + 0] * v0;
-    o += w[s + 1] * v1;
-    o += w[s + 2] * v2;
-    o += w[s + 3] * v3;
+  for (int c = 0; c < kMergeChunk; ++c) {
+    const float* src = op + min(c, S - 1) * ostride;
+    v[c][0] = *(const f32x4*)src;
+    v[c][1] = *(const f32x4*)(src + 256);
   }
-  for (; s < a.num_splits; ++s) o += w[s] * *(const f32x4*)(op + s * stride);
-  float f = inv_w;
-  if (a.sink != nullptr) f = f / (1.0f + __builtin_amdgcn_exp2f(a.sink[h] * kLog2e - lse));
-  return o * f;
+  const float M = wave_max(ls);
+  const float wl = (M == kNegInf || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls - M);
+  const float ws = wave_sum(wl);
+  Merged m;
+  const bool none = M == kNegInf;    // every split empty: O = 0, LSE = -inf
+  m.lse = none ? kNegInf : M + __builtin_amdgcn_logf(ws);
+  // Terms past S are dropped by a select, not a branch, so that the loads
+  // above are used on every path and stay where they are issued.
+  f32x4 lo = {-0.f, -0.f, -0.f, -0.f}, hi = lo;   // IEEE additive identity: keeps the sign of -0 terms
+#pragma unroll
+  for (int c = 0; c < kMergeChunk; ++c) {
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), c));
+    const f32x4 l2 = lo + w * v[c][0], h2 = hi + w * v[c][1];
+    lo = c < S ? l2 : lo;
+    hi = c < S ? h2 : hi;
+  }
+  for (int s0 = kMergeChunk; s0 < S; s0 += kMergeChunk) {
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c) {
+      const float* src = op + min(s0 + c, S - 1) * ostride;
+      v[c][0] = *(const f32x4*)src;
+      v[c][1] = *(const f32x4*)(src + 256);
+    }
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(s0 + c, 63)));
+      const f32x4 l2 = lo + w * v[c][0], h2 = hi + w * v[c][1];
+      lo = s0 + c < S ? l2 : lo;
+      hi = s0 + c < S ? h2 : hi;
+    }
+  }
+  float f = 1.0f / ws;
+  if (a.sink != nullptr) f = f / (1.0f + __builtin_amdgcn_exp2f(a.sink[h] * kLog2e - m.lse));
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  m.lo = none ? zero : lo * f;
+  m.hi = none ? zero : hi * f;
+  return m;
 }
 
-// bf16 / fp32 output: 4 heads per block, one wave per head, 8 columns per lane.
+// bf16 / fp32 output: 4 heads per workgroup, one wave per head.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  __shared__ float s_w[4][kMaxSplits];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bpt = (a.h_q + 3) / 4;
   const int t = blockIdx.x / bpt;
   const int h = (blockIdx.x - t * bpt) * 4 + wave;
   if (h >= a.h_q) return;
-  float lse, inv_w;
-  head_weights(a, t, h, s_w[wave], lse, inv_w);    // the same wave reads the weights back
-  __builtin_amdgcn_wave_barrier();
+  const Merged m = merge_head(a, t, h);
   const int64_t row = (int64_t)t * a.h_q + h;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int col = 256 * half + 4 * lane;
-    const f32x4 o = merge_columns(a, s_w[wave], inv_w, lse, t, h, col);
-    if (a.out_dtype == kOutF32) {
-      *(f32x4*)((float*)a.out + row * 512 + col) = o;
-    } else {
-      *(u32x2*)((uint16_t*)a.out + row * 512 + col) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-    }
+  if (a.out_dtype == kOutF32) {
+    *(f32x4*)((float*)a.out + row * 512 + 4 * lane) = m.lo;
+    *(f32x4*)((float*)a.out + row * 512 + 256 + 4 * lane) = m.hi;
+  } else {
+    uint16_t* o = (uint16_t*)a.out + row * 512 + 4 * lane;
+    *(u32x2*)o = u32x2{pack_bf16x2(m.lo[0], m.lo[1]), pack_bf16x2(m.lo[2], m.lo[3])};
+    *(u32x2*)(o + 256) = u32x2{pack_bf16x2(m.hi[0], m.hi[1]), pack_bf16x2(m.hi[2], m.hi[3])};
   }
-  if (a.lse_out != nullptr && lane == 0) a.lse_out[row] = lse;
+  if (a.lse_out != nullptr && lane == 0) a.lse_out[row] = m.lse;
 }
 
 // FP8 output: one workgroup (16 waves) per token so the amax is a local
 // reduction; wave w merges heads w, w+16, ...
 __global__ __launch_bounds__(1024) void combine_fp8_kernel(CombineArgs a) {
-  __shared__ float s_w[16][kMaxSplits];
   __shared__ float s_red[16];
   const int t = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -746,17 +786,14 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(CombineArgs a) {
     const int h = wave + 16 * k;
     o[k][0] = o[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (h < a.h_q) {
-      float lse, inv_w;
-      head_weights(a, t, h, s_w[wave], lse, inv_w);
-      __builtin_amdgcn_wave_barrier();
+      const Merged m = merge_head(a, t, h);
+      o[k][0] = m.lo;
+      o[k][1] = m.hi;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        o[k][half] = merge_columns(a, s_w[wave], inv_w, lse, t, h, 256 * half + 4 * lane);
+      for (int half = 0; half < 2; ++half)
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[k][half][0]), fabsf(o[k][half][1])),
                                  fmaxf(fabsf(o[k][half][2]), fabsf(o[k][half][3]))));
-      }
-      if (a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)t * a.h_q + h] = lse;
-      __builtin_amdgcn_wave_barrier();
+      if (a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)t * a.h_q + h] = m.lse;
     }
   }
   amax = warp_max(amax);

@@ -56,9 +56,13 @@ def test_choose_num_splits_properties():
             s = smla.smla_choose_num_splits(s_q, 64, topk, 256)
             n_blk = -(-topk // 64)
             assert 1 <= s <= max(1, min(n_blk, 64))
-            if s_q >= 128:
+            if s > 1:
+                assert s_q * s <= 256          # every job in one round of one workgroup per CU
+            if s_q > 128:
                 assert s == 1
     assert smla.smla_choose_num_splits(1, 64, 640, 256) == 10
+    assert smla.smla_choose_num_splits(96, 64, 640, 256) == 2
+    assert smla.smla_choose_num_splits(384, 64, 640, 256) == 1
     assert smla.smla_choose_num_splits(0, 64, 640, 256) == 0
     # deterministic
     assert smla.smla_choose_num_splits(16, 64, 640, 256) == smla.smla_choose_num_splits(16, 64, 640, 256)
