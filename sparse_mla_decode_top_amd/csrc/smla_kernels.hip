@@ -458,103 +458,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         tile = btile;
       }
 
-      // ---- S^T = K . Q^T: 4 slot tiles x 18 k-steps ------------------------
-      f32x4 sacc[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-      {
-        // four bases keep every offset within the 16-bit ds_read field
-        const uint32_t tl = lds_addr(tile);
-        const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
-                                   opaque(tl + kb1 + 65536)};
-        // Software pipeline: the K fragments of k-step ks+2 are requested
-        // before the MFMAs of k-step ks are issued.
-        auto kfrag = [&](int ks, int st) -> bf16x8 {
-          const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
-          return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
-        };
-        bf16x8 kf[3][4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) { kf[0][st] = kfrag(0, st); kf[1][st] = kfrag(1, st); }
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          if (ks + 2 < 18) {
-#pragma unroll
-            for (int st = 0; st < 4; ++st) kf[(ks + 2) % 3][st] = kfrag(ks + 2, st);
-          }
-          __builtin_amdgcn_sched_barrier(0);     // keep the reads two k-steps ahead
-#pragma unroll
-          for (int st = 0; st < 4; ++st)
-            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % 3][st], qf[ks], sacc[st], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      // ---- online softmax (log2 units, integer running max) -----------------
-      // lane holds head hl, slots 16st + 4G + i.  A masked slot gets the score
-      // kMaskedScore from the block's bias row (its tile row is zero).
-      f32x4 bias[4], rsc[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        bias[st] = *(const f32x4*)&s_bias[cur][16 * st + 4 * G];
-        if (KV_FP8) rsc[st] = *(const f32x4*)&s_scale[cur][16 * st + 4 * G];
-      }
-      float tv[16];
-      float mloc = kMaskedScore;
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sv;
-          if (KV_FP8)
-            sv = fmaf(sacc[st][i] * scale_log2, rsc[st][i], bias[st][i]);
-          else
-            sv = fmaf(sacc[st][i], scale_log2, bias[st][i]);
-          tv[4 * st + i] = sv;
-          mloc = fmaxf(mloc, sv);
-        }
-      mloc = rows_max(mloc);
-      m_seen = fmaxf(m_seen, mloc);
-      // The first contributing block fixes the frame (nothing is accumulated yet).
-      if (M_run == kNoFrame && mloc > kMaskedScore) M_run = floorf(mloc);
-      overflow |= mloc > M_run + kFrameSlack;
-      const float M_new = M_run;
-
-      // P as bf16 hi + lo.  B operand of k-step kk: slots 32kk + 16(e/4) + 4G + (e%4),
-      // i.e. this lane's own values of slot tiles 2kk and 2kk+1.
-      // p = 2^(t - floor t) * 2^(floor t - M), branch free: a masked slot or a
-      // head without a frame gets an exponent clamped to -256, i.e. p = 0.
-      uint32_t ph[8], pl[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        float pv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float tt = tv[e + u];
-          const float fl = floorf(tt);
-          const float ex = __builtin_amdgcn_fmed3f(fl - M_new, -256.f, 256.f);
-          float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
-          psum += p;
-          if (KV_FP8) p *= rsc[(e + u) >> 2][(e + u) & 3];
-          pv[u] = p;
-        }
-        ph[e >> 1] = pack_bf16x2(pv[0], pv[1]);
-        const float h0 = __uint_as_float(ph[e >> 1] << 16), h1 = __uint_as_float(ph[e >> 1] & 0xFFFF0000u);
-        pl[e >> 1] = pack_bf16x2(pv[0] - h0, pv[1] - h1);
-      }
-      l_run += psum;
-      const bf16x8 pf0 = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
-      const bf16x8 pf1 = __builtin_bit_cast(bf16x8, u32x4{ph[4], ph[5], ph[6], ph[7]});
-      const bf16x8 pg0 = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
-      const bf16x8 pg1 = __builtin_bit_cast(bf16x8, u32x4{pl[4], pl[5], pl[6], pl[7]});
-
-      // ---- O^T += V^T . P^T: 32 column tiles x 2 k-steps x (hi, lo) ----------
-      const uint32_t tlv = lds_addr(tile);
-      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]),
-                                 opaque(tlv + vb[3])};
-      // Software pipeline: the V^T fragments of column tile ct+2 are requested
-      // before the MFMAs of ct are issued.
+      // The block is processed as two halves of 32 slots (slot tiles 0-1 and
+      // 2-3).  The softmax of one half is independent of the MFMAs that run
+      // next to it, so its VALU work is issued in small steps between them:
+      //   QK(h0) | QK(h1) + softmax(h0) | PV(h0) + softmax(h1) | PV(h1)
+      // The first half with a valid slot fixes a head's frame.
+      const uint32_t tl = lds_addr(tile);
+      // four bases keep every offset within the 16-bit ds_read field
+      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
+                                 opaque(tl + kb1 + 65536)};
+      auto kfrag = [&](int ks, int st) -> bf16x8 {
+        const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
+        return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
+      };
+      const uint32_t vbase[4] = {opaque(tl + vb[0]), opaque(tl + vb[1]), opaque(tl + vb[2]), opaque(tl + vb[3])};
       auto vfrag = [&](int ct, int kk) -> bf16x8 {
         const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
@@ -564,23 +481,113 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const u32x2 w1 = __builtin_bit_cast(u32x2, v1);
         return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
       };
-      bf16x8 vf[3][2];
+
+      // bias (and FP8 row scale) of this lane's 16 slots: slots 16st + 4G + i
+      f32x4 bias[4], rsc[4];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) { vf[0][kk] = vfrag(0, kk); vf[1][kk] = vfrag(1, kk); }
-#pragma unroll
-      for (int ct = 0; ct < 32; ++ct) {
-        if (ct + 2 < 32) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) vf[(ct + 2) % 3][kk] = vfrag(ct + 2, kk);
-        }
-        __builtin_amdgcn_sched_barrier(0);       // keep the reads two column tiles ahead
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % 3][kk], kk ? pf1 : pf0, acc[ct], 0, 0, 0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % 3][kk], kk ? pg1 : pg0, acc[ct], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int st = 0; st < 4; ++st) {
+        bias[st] = *(const f32x4*)&s_bias[cur][16 * st + 4 * G];
+        if (KV_FP8) rsc[st] = *(const f32x4*)&s_scale[cur][16 * st + 4 * G];
       }
+
+      f32x4 sacc[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      // Softmax of half hh in 15 steps (called with constant hh and k):
+      //   0: scores (log2 units, masked slots at kMaskedScore)   1-2: head max, frame
+      //   3-10: one weight each (2^(t - floor t) * 2^(floor t - M), p = 0 for a
+      //   masked slot or a head without a frame)   11-14: one bf16 hi/lo pair each.
+      float tv[2][8], pv[2][8], mh[2];
+      uint32_t ph[2][4], pl[2][4];
+      auto sm_step = [&](const int hh, const int k) __attribute__((always_inline)) {
+        if (k == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int st = 2 * hh + (e >> 2), i = e & 3;
+            tv[hh][e] = KV_FP8 ? fmaf(sacc[st][i] * scale_log2, rsc[st][i], bias[st][i])
+                               : fmaf(sacc[st][i], scale_log2, bias[st][i]);
+          }
+        } else if (k == 1) {
+          float m = fmaxf(fmaxf(fmaxf(tv[hh][0], tv[hh][1]), fmaxf(tv[hh][2], tv[hh][3])),
+                          fmaxf(fmaxf(tv[hh][4], tv[hh][5]), fmaxf(tv[hh][6], tv[hh][7])));
+          auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          mh[hh] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        } else if (k == 2) {
+          auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mh[hh]), __float_as_uint(mh[hh]), false, false);
+          const float m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+          m_seen = fmaxf(m_seen, m);
+          if (M_run == kNoFrame && m > kMaskedScore) M_run = floorf(m);
+          overflow |= m > M_run + kFrameSlack;
+        } else if (k <= 10) {
+          const int e = k - 3;
+          const float tt = tv[hh][e];
+          const float fl = floorf(tt);
+          const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
+          float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+          l_run += p;
+          if (KV_FP8) p *= rsc[2 * hh + (e >> 2)][e & 3];
+          pv[hh][e] = p;
+        } else {
+          const int j = k - 11;
+          const uint32_t h2 = pack_bf16x2(pv[hh][2 * j], pv[hh][2 * j + 1]);
+          ph[hh][j] = h2;
+          pl[hh][j] = pack_bf16x2(pv[hh][2 * j] - __uint_as_float(h2 << 16),
+                                  pv[hh][2 * j + 1] - __uint_as_float(h2 & 0xFFFF0000u));
+        }
+      };
+      // step of the softmax placed after MFMA group g (-1: none)
+      auto sm_at = [](int g) -> int { return (g >= 1 && g <= 15) ? g - 1 : -1; };
+
+      // ---- QK^T of one half: 2 slot tiles x 18 k-steps; the K fragments of
+      // k-step ks+kAheadK are requested before the MFMAs of ks.  hh = 1
+      // carries the softmax of half 0.
+      constexpr int kAheadK = 4, kAheadV = 4;
+      auto qk_half = [&](const int hh) __attribute__((always_inline)) {
+        bf16x8 kf[kAheadK + 1][2];
+#pragma unroll
+        for (int a0 = 0; a0 < kAheadK; ++a0)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) kf[a0][u] = kfrag(a0, 2 * hh + u);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          if (ks + kAheadK < 18) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) kf[(ks + kAheadK) % (kAheadK + 1)][u] = kfrag(ks + kAheadK, 2 * hh + u);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            sacc[2 * hh + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % (kAheadK + 1)][u], qf[ks],
+                                                                       sacc[2 * hh + u], 0, 0, 0);
+          if (hh == 1 && sm_at(ks) >= 0) sm_step(0, sm_at(ks));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // ---- O^T += V^T . P^T over one half (k-step kk): 32 column tiles x
+      // (hi, lo); V^T fragments kAheadV column tiles ahead.  kk = 0 carries
+      // the softmax of half 1.
+      auto pv_half = [&](const int kk) __attribute__((always_inline)) {
+        const bf16x8 pfh = __builtin_bit_cast(bf16x8, u32x4{ph[kk][0], ph[kk][1], ph[kk][2], ph[kk][3]});
+        const bf16x8 pfl = __builtin_bit_cast(bf16x8, u32x4{pl[kk][0], pl[kk][1], pl[kk][2], pl[kk][3]});
+        bf16x8 vf[kAheadV + 1];
+#pragma unroll
+        for (int a0 = 0; a0 < kAheadV; ++a0) vf[a0] = vfrag(a0, kk);
+#pragma unroll
+        for (int ct = 0; ct < 32; ++ct) {
+          if (ct + kAheadV < 32) vf[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, kk);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfh, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfl, acc[ct], 0, 0, 0);
+          if (kk == 0 && sm_at(ct) >= 0) sm_step(1, sm_at(ct));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      qk_half(0);
+      qk_half(1);      // + softmax(h0)
+      pv_half(0);      // + softmax(h1)
+      pv_half(1);
 
       valid_cur = valid_nxt;
       sc_cur = sc_nxt;
