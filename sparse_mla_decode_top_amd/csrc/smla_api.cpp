@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "smla.h"
 #include "smla_internal.h"
 
@@ -13,6 +15,19 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int32_t n_blocks_of(int32_t topk) { return (topk + SMLA_SPLIT_BLOCK - 1) / SMLA_SPLIT_BLOCK; }
+
+// Compute units of the current device (cached per device; 256 if unknown).
+int32_t device_cus() {
+  static std::atomic<int32_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int32_t n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 // Checks shared by both entry points: the shape fields that the combine uses.
 smla_status check_common_shape(const smla_params* p, int32_t num_splits) {
@@ -143,8 +158,14 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   a.n_blocks = n_blocks_of(p->topk);
   a.out_dtype = p->out_dtype;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  // Few jobs leave most compute units idle: then two workgroups share each
+  // job, one per half of the 512 output columns (both compute the scores).
+  // Not for a direct FP8 output, whose scale needs every column of a token.
+  const bool direct = o_accum == nullptr;
+  const int64_t jobs = (int64_t)p->s_q * (direct ? 1 : num_splits);
+  a.col_parts = (direct && p->out_dtype == SMLA_OUT_FP8_E4M3) || 2 * jobs > device_cus() ? 1 : 2;
 
-  if (o_accum == nullptr) {        // direct path: one job per token, fused epilogue
+  if (direct) {        // direct path: one job per token, fused epilogue
     return smla::launch_decode_direct(a, fp8, hs) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
   }
   if (smla::launch_decode_partial(a, fp8, hs) != hipSuccess) return SMLA_ERR_HIP;

@@ -57,7 +57,6 @@ constexpr int kBlk = 64;                         // slots per KV block
 constexpr int kTileBytes = kBlk * 1152;          // 64 bf16 rows of 576
 constexpr int kCodeTileBytes = kBlk * 576;       // 64 e4m3 rows of 576
 constexpr int kQOffset = kTileBytes;             // LDS byte offset of the staged Q rows
-constexpr int kStagePitch = 2064;                // LDS pitch of a staged fp32 output row (2048 + 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kFrameSlack = 64.0f;     // scores may exceed a head's frame M by this much
@@ -257,16 +256,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Job decode shared by every wave: blockIdx.x = token * num_splits + split.
-// Blocks [b0, b1) of split s: near-equal ranges, the remainder on the leading
-// splits, empty past the end.
+// Job decode shared by every wave.  Job id = token * num_splits + split; with
+// CS = 2 column parts, the two workgroups of a job are 8 block ids apart in
+// groups of 16 (blocks are spread over the 8 XCDs round robin, so both land
+// on one XCD and share its L2 for the job's rows).  Blocks [b0, b1) of split
+// s: near-equal ranges, the remainder on the leading splits, empty past the
+// end.  part: which 512 / CS output columns this workgroup owns.
 struct Job {
-  int t, s, b0, b1;
+  int t, s, b0, b1, part;
+  bool live;
 };
-__device__ __forceinline__ Job decode_job(int num_splits, int n_blocks) {
+template <int CS>
+__device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int n_jobs) {
   Job j;
-  j.t = blockIdx.x / num_splits;
-  j.s = blockIdx.x - j.t * num_splits;
+  int id = blockIdx.x;
+  j.part = 0;
+  if (CS == 2) {
+    j.part = (id >> 3) & 1;
+    id = (id >> 4) * 8 + (id & 7);
+  }
+  j.live = id < n_jobs;
+  j.t = id / num_splits;
+  j.s = id - j.t * num_splits;
   const int base = n_blocks / num_splits, rem = n_blocks - base * num_splits;
   j.b0 = j.s * base + min(j.s, rem);
   j.b1 = j.b0 + base + (j.s < rem ? 1 : 0);
@@ -277,8 +288,11 @@ __device__ __forceinline__ Job decode_job(int num_splits, int n_blocks) {
 // The attention kernel.  KV_FP8: pool rows are e4m3 codes + a row scale.
 // DIRECT: single-split job writing the final output (sink + cast fused).
 // ---------------------------------------------------------------------------
-template <bool KV_FP8, bool DIRECT>
+template <bool KV_FP8, bool DIRECT, int CS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeArgs a) {
+  constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
+  constexpr int kCols = 512 / CS;
+  constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
   // bf16 pool: two tiles.  FP8 pool: two code tiles + one bf16 tile.
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
   __shared__ __attribute__((aligned(16))) float s_scale[2][kBlk];
@@ -293,7 +307,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
   const int head = 16 * wave + hl;
 
-  const Job job = decode_job(a.num_splits, a.n_blocks);
+  const Job job = decode_job<CS>(a.num_splits, a.n_blocks, a.s_q * a.num_splits);
+  if (!job.live) return;                          // padding of the CS = 2 grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = a.indices + (int64_t)t * a.topk;
 
@@ -302,9 +317,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   float l_run = 0.f;                  // this lane's share of the denominator
   if (tid == 0) s_restart = 0;        // ordered before its readers by the loop barriers
   bool restarted = false;
-  f32x4 acc[32];                      // O^T: column tile ct -> columns 16ct + 4G + i
+  f32x4 acc[kCt];                     // O^T: column tile ct -> columns kCols * part + 16ct + 4G + i
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (job.b0 < job.b1) {
     // Lane l holds the index of slot l of a block.  The load address is clamped
@@ -471,7 +486,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
         return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
       };
-      const uint32_t vbase[4] = {opaque(tl + vb[0]), opaque(tl + vb[1]), opaque(tl + vb[2]), opaque(tl + vb[3])};
+      // V^T of this workgroup's columns: column tile ct (local) is global
+      // tile kCt * part + ct; 4 column tiles per 128-byte octet
+      const uint32_t tlv = tl + job.part * (kCt / 4) * 8192;
+      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
       auto vfrag = [&](int ct, int kk) -> bf16x8 {
         const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
@@ -564,9 +582,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      // ---- O^T += V^T . P^T over one half (k-step kk): 32 column tiles x
-      // (hi, lo); V^T fragments kAheadV column tiles ahead.  kk = 0 carries
-      // the softmax of half 1.
+      // ---- O^T += V^T . P^T over one half (k-step kk): the kCt column tiles
+      // of this workgroup x (hi, lo); V^T fragments kAheadV column tiles
+      // ahead.  kk = 0 carries the softmax of half 1 (its 15 steps fit in the
+      // first 16 column tiles).
       auto pv_half = [&](const int kk) __attribute__((always_inline)) {
         const bf16x8 pfh = __builtin_bit_cast(bf16x8, u32x4{ph[kk][0], ph[kk][1], ph[kk][2], ph[kk][3]});
         const bf16x8 pfl = __builtin_bit_cast(bf16x8, u32x4{pl[kk][0], pl[kk][1], pl[kk][2], pl[kk][3]});
@@ -574,8 +593,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int a0 = 0; a0 < kAheadV; ++a0) vf[a0] = vfrag(a0, kk);
 #pragma unroll
-        for (int ct = 0; ct < 32; ++ct) {
-          if (ct + kAheadV < 32) vf[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, kk);
+        for (int ct = 0; ct < kCt; ++ct) {
+          if (ct + kAheadV < kCt) vf[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, kk);
           __builtin_amdgcn_sched_barrier(0);
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfh, acc[ct], 0, 0, 0);
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfl, acc[ct], 0, 0, 0);
@@ -606,7 +625,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       M_run = floorf(m_seen);   // a restart implies a valid score was seen
       l_run = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       run_pass(false);
     }
   }
@@ -624,8 +643,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // The scaled rows go through LDS so that each global store instruction
   // writes whole lines of one or two rows (a lane's accumulators hold 4
-  // columns of 32 column tiles, i.e. 64-byte pieces of 16 rows per store).
-  // Wave w stages its 16 heads x 512 fp32 at s_tile + w * 16 * kStagePitch;
+  // columns of each column tile, i.e. 64-byte pieces of 16 rows per store).
+  // Wave w stages its 16 heads x kCols fp32 at s_tile + w * 16 * kStagePitch;
   // the 16-byte row padding keeps the 16-lane writes bank-conflict free.  A
   // wave reads back only its own rows, and LDS keeps a wave's accesses in
   // order, so no barrier is needed between the two.
@@ -633,14 +652,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   uint8_t* stg = s_tile + wave * 16 * kStagePitch;
   float amax = 0.f;
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct) {
+  for (int ct = 0; ct < kCt; ++ct) {
     const f32x4 v = acc[ct] * oscale;
-    if (DIRECT && wave_ok)
+    if (DIRECT && CS == 1 && wave_ok)
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     *(f32x4*)(stg + hl * kStagePitch + 64 * ct + 16 * G) = v;
   }
   float qscale = 1.0f;
-  if (DIRECT && a.out_dtype == kOutFp8) {        // per-token amax over every head
+  if (DIRECT && CS == 1 && a.out_dtype == kOutFp8) {   // per-token amax over every head
     amax = warp_max(amax);
     if (lane == 0) s_red[wave] = amax;
     lds_barrier();
@@ -650,22 +669,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   if (wave_ok) {
     const int64_t row0 = (DIRECT ? (int64_t)t * a.h_q : ((int64_t)job.s * a.s_q + t) * a.h_q) + 16 * wave;
-    if (!DIRECT || a.out_dtype == kOutF32) {     // one 1 KB half row per instruction
-      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + 4 * lane;
+    const int col0 = job.part * kCols;
+    if (!DIRECT || a.out_dtype == kOutF32) {     // one 1 KB piece of a row per instruction
+      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + col0 + 4 * lane;
+      constexpr int kSeg = kCols / 256;
 #pragma unroll
-      for (int j = 0; j < 32; ++j)
-        *(f32x4*)(dst + (j >> 1) * 512 + (j & 1) * 256) =
-            *(const f32x4*)(stg + (j >> 1) * kStagePitch + (j & 1) * 1024 + 16 * lane);
-    } else if (a.out_dtype == kOutBf16) {        // one 1 KB row per instruction
-      uint16_t* dst = (uint16_t*)a.out + row0 * 512 + 8 * lane;
+      for (int j = 0; j < 16 * kSeg; ++j)
+        *(f32x4*)(dst + (j / kSeg) * 512 + (j % kSeg) * 256) =
+            *(const f32x4*)(stg + (j / kSeg) * kStagePitch + (j % kSeg) * 1024 + 16 * lane);
+    } else if (a.out_dtype == kOutBf16) {        // 1 KB (one or two row pieces) per instruction
+      constexpr int kLanesPerRow = kCols / 8, kRowsPer = 64 / kLanesPerRow;
+      const int rr = lane / kLanesPerRow, cc = 8 * (lane % kLanesPerRow);
+      uint16_t* dst = (uint16_t*)a.out + row0 * 512 + col0 + cc;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const f32x4 v0 = *(const f32x4*)(stg + j * kStagePitch + 32 * lane);
-        const f32x4 v1 = *(const f32x4*)(stg + j * kStagePitch + 32 * lane + 16);
-        *(u32x4*)(dst + j * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+      for (int j = 0; j < 16 / kRowsPer; ++j) {
+        const int r = kRowsPer * j + rr;
+        const f32x4 v0 = *(const f32x4*)(stg + r * kStagePitch + 4 * cc);
+        const f32x4 v1 = *(const f32x4*)(stg + r * kStagePitch + 4 * cc + 16);
+        *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
                                          pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
       }
-    } else {                                     // e4m3: two 512 B rows per instruction
+    } else if (CS == 1) {                        // e4m3: two 512 B rows per instruction
       uint8_t* dst = (uint8_t*)a.out + row0 * 512;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -681,7 +705,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         *(u32x4*)(dst + h * 512 + 16 * (lane & 31)) = w;
       }
     }
-    if (G == 0) {
+    if (G == 0 && job.part == 0) {               // both column parts hold the same LSE
       if (!DIRECT)
         a.lse_accum[row0 + hl] = lse;
       else if (a.lse_out != nullptr)
@@ -829,22 +853,34 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode_partial(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.s_q * a.num_splits));
-  if (kv_fp8)
-    hipLaunchKernelGGL((decode_kernel<true, false>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<false, false>), grid, dim3(kThreads), 0, stream, a);
+namespace {
+template <bool DIRECT>
+hipError_t launch_decode(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
+  const unsigned n_jobs = (unsigned)(a.s_q * (DIRECT ? 1 : a.num_splits));
+  const dim3 block(kThreads);
+  if (a.col_parts == 2) {
+    const dim3 grid((n_jobs + 7) / 8 * 16);
+    if (kv_fp8)
+      hipLaunchKernelGGL((decode_kernel<true, DIRECT, 2>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<false, DIRECT, 2>), grid, block, 0, stream, a);
+  } else {
+    const dim3 grid(n_jobs);
+    if (kv_fp8)
+      hipLaunchKernelGGL((decode_kernel<true, DIRECT, 1>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<false, DIRECT, 1>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_partial(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
+  return launch_decode<false>(a, kv_fp8, stream);
 }
 
 hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
-  const dim3 grid((unsigned)a.s_q);
-  if (kv_fp8)
-    hipLaunchKernelGGL((decode_kernel<true, true>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<false, true>), grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_decode<true>(a, kv_fp8, stream);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {

@@ -183,10 +183,12 @@ def test_fp8_pool_and_fp8_output(name):
     inp = dev.inp
     O_ref, L_ref = H.oracle_direct(name, 0)
     O_fin = H.oracle_final(inp, O_ref, L_ref)
-    # fp32 output through the FP8 pool
-    res = H.run(dev, 8, "f32", "split")
-    H.assert_o_close(res["O"], O_fin)
-    H.assert_lse_close(res["lse"], L_ref)
+    # fp32 output through the FP8 pool (at s_q = 16, 8 splits give 128 jobs and two
+    # workgroups per job; 16 splits give 256 jobs and one workgroup per job)
+    for S in (8, 16):
+        res = H.run(dev, S, "f32", "split")
+        H.assert_o_close(res["O"], O_fin)
+        H.assert_lse_close(res["lse"], L_ref)
     direct = H.run(dev, 1, "f32", "direct")
     H.assert_o_close(direct["O"], O_fin)
     # FP8 output (per-token scale = amax / 448), from the combine and from the direct epilogue
