@@ -257,9 +257,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Job decode shared by every wave.  Job id = token * num_splits + split; with
-// CS = 2 column parts, the two workgroups of a job are 8 block ids apart in
-// groups of 16 (blocks are spread over the 8 XCDs round robin, so both land
-// on one XCD and share its L2 for the job's rows).  Blocks [b0, b1) of split
+// CS > 1 column parts, the workgroups of a job are 8 block ids apart in
+// groups of 8 * CS (blocks are spread over the 8 XCDs round robin, so all of
+// them land on one XCD and share its L2 for the job's rows).  Blocks [b0, b1) of split
 // s: near-equal ranges, the remainder on the leading splits, empty past the
 // end.  part: which 512 / CS output columns this workgroup owns.
 struct Job {
@@ -271,9 +271,9 @@ __device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int n_jo
   Job j;
   int id = blockIdx.x;
   j.part = 0;
-  if (CS == 2) {
-    j.part = (id >> 3) & 1;
-    id = (id >> 4) * 8 + (id & 7);
+  if (CS > 1) {
+    j.part = (id >> 3) % CS;
+    id = (id / (8 * CS)) * 8 + (id & 7);
   }
   j.live = id < n_jobs;
   j.t = id / num_splits;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int head = 16 * wave + hl;
 
   const Job job = decode_job<CS>(a.num_splits, a.n_blocks, a.s_q * a.num_splits);
-  if (!job.live) return;                          // padding of the CS = 2 grid (whole workgroup)
+  if (!job.live) return;                          // padding of the CS > 1 grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = a.indices + (int64_t)t * a.topk;
 
@@ -601,6 +601,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           if (kk == 0 && sm_at(ct) >= 0) sm_step(1, sm_at(ct));
           __builtin_amdgcn_sched_barrier(0);
         }
+        if (kk == 0) {                                // steps that did not fit between the MFMAs
+#pragma unroll
+          for (int k = kCt - 1; k < 15; ++k) sm_step(1, k);
+        }
       };
 
       qk_half(0);
@@ -670,13 +674,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (wave_ok) {
     const int64_t row0 = (DIRECT ? (int64_t)t * a.h_q : ((int64_t)job.s * a.s_q + t) * a.h_q) + 16 * wave;
     const int col0 = job.part * kCols;
-    if (!DIRECT || a.out_dtype == kOutF32) {     // one 1 KB piece of a row per instruction
-      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + col0 + 4 * lane;
-      constexpr int kSeg = kCols / 256;
+    if (!DIRECT || a.out_dtype == kOutF32) {     // 1 KB of whole row pieces per instruction
+      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + col0;
 #pragma unroll
-      for (int j = 0; j < 16 * kSeg; ++j)
-        *(f32x4*)(dst + (j / kSeg) * 512 + (j % kSeg) * 256) =
-            *(const f32x4*)(stg + (j / kSeg) * kStagePitch + (j % kSeg) * 1024 + 16 * lane);
+      for (int j = 0; j < 16 * kCols / 256; ++j) {
+        const int f = 256 * j + 4 * lane;          // float index in the wave's 16 x kCols block
+        const int r = f / kCols, c = f % kCols;
+        *(f32x4*)(dst + r * 512 + c) = *(const f32x4*)(stg + r * kStagePitch + 4 * c);
+      }
     } else if (a.out_dtype == kOutBf16) {        // 1 KB (one or two row pieces) per instruction
       constexpr int kLanesPerRow = kCols / 8, kRowsPer = 64 / kLanesPerRow;
       const int rr = lane / kLanesPerRow, cc = 8 * (lane % kLanesPerRow);
@@ -858,7 +863,13 @@ template <bool DIRECT>
 hipError_t launch_decode(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
   const unsigned n_jobs = (unsigned)(a.s_q * (DIRECT ? 1 : a.num_splits));
   const dim3 block(kThreads);
-  if (a.col_parts == 2) {
+  if (a.col_parts == 4) {
+    const dim3 grid((n_jobs + 7) / 8 * 32);
+    if (kv_fp8)
+      hipLaunchKernelGGL((decode_kernel<true, DIRECT, 4>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<false, DIRECT, 4>), grid, block, 0, stream, a);
+  } else if (a.col_parts == 2) {
     const dim3 grid((n_jobs + 7) / 8 * 16);
     if (kv_fp8)
       hipLaunchKernelGGL((decode_kernel<true, DIRECT, 2>), grid, block, 0, stream, a);
