@@ -66,13 +66,19 @@ size_t smla_partial_bytes(int32_t s_q, int32_t h_q, int32_t num_splits) {
 int32_t smla_choose_num_splits(int32_t s_q, int32_t h_q, int32_t topk, int32_t num_cus) {
   if (s_q < 1 || h_q < 1 || topk < 1 || num_cus < 1) return 0;
   const int32_t n_blk = n_blocks_of(topk);
-  // As many splits as keep all s_q * S jobs within one round of one workgroup
-  // per compute unit.  A split count that spills into a second, partly
-  // filled round lengthens the step by a whole job; and once the tokens alone
-  // fill the compute units, splitting only adds partial traffic.
-  int32_t s = num_cus / s_q;
-  if (s > n_blk) s = n_blk;
-  if (s > SMLA_MAX_SPLITS) s = SMLA_MAX_SPLITS;
+  // Workgroups per job: jobs split their output columns over 4 or 2
+  // workgroups when that keeps every workgroup in one round over the compute
+  // units (sparse_mla_decode makes the same choice).  Measured on a 256-CU
+  // MI355X: with 4 column parts, more splits win as long as each keeps 4 or
+  // more; past that, 2 column parts with at least 2 splits; large batches
+  // (more than a quarter of the CUs in tokens) run unsplit.
+  const int32_t cap = n_blk < SMLA_MAX_SPLITS ? n_blk : SMLA_MAX_SPLITS;
+  int32_t s = num_cus / (4 * s_q);
+  if (s < 4) {
+    s = num_cus / (2 * s_q);
+    if (s < 2) s = 1;
+  }
+  if (s > cap) s = cap;
   return s < 1 ? 1 : s;
 }
 

@@ -726,13 +726,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // partial rows of the first splits are requested together with the LSEs, so
 // the row loads do not wait for the weights.
 // ---------------------------------------------------------------------------
-constexpr int kMergeChunk = 8;       // partial rows in flight per lane: 8 splits x 2 x 16 B
 
 struct Merged {
   f32x4 lo, hi;                      // columns 4l.., 256+4l..
   float lse;
 };
 
+// kMergeChunk: partial rows in flight per lane (splits x 2 x 16 B).
+template <int kMergeChunk>
 __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h) {
   const int lane = threadIdx.x & 63;
   const int S = a.num_splits;
@@ -796,7 +797,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x / bpt;
   const int h = (blockIdx.x - t * bpt) * 4 + wave;
   if (h >= a.h_q) return;
-  const Merged m = merge_head(a, t, h);
+  const Merged m = merge_head<16>(a, t, h);
   const int64_t row = (int64_t)t * a.h_q + h;
   if (a.out_dtype == kOutF32) {
     *(f32x4*)((float*)a.out + row * 512 + 4 * lane) = m.lo;
@@ -822,7 +823,7 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(CombineArgs a) {
     const int h = wave + 16 * k;
     o[k][0] = o[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (h < a.h_q) {
-      const Merged m = merge_head(a, t, h);
+      const Merged m = merge_head<8>(a, t, h);     // four heads per wave: fewer rows in flight
       o[k][0] = m.lo;
       o[k][1] = m.hi;
 #pragma unroll

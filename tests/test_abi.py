@@ -57,12 +57,12 @@ def test_choose_num_splits_properties():
             n_blk = -(-topk // 64)
             assert 1 <= s <= max(1, min(n_blk, 64))
             if s > 1:
-                assert s_q * s <= 256          # every job in one round of one workgroup per CU
-            if s_q > 128:
+                assert 2 * s_q * s <= 256      # split jobs keep two column parts in one round
+            if s_q > 64:
                 assert s == 1
-    assert smla.smla_choose_num_splits(1, 64, 640, 256) == 10
-    assert smla.smla_choose_num_splits(96, 64, 640, 256) == 2
-    assert smla.smla_choose_num_splits(384, 64, 640, 256) == 1
+    for s_q, expect in ((1, 10), (4, 10), (8, 8), (16, 4), (32, 4), (48, 2), (96, 1), (384, 1)):
+        assert smla.smla_choose_num_splits(s_q, 64, 640, 256) == expect, s_q
+    assert smla.smla_choose_num_splits(16, 64, 640, 512) == 8      # scales with the CU count
     assert smla.smla_choose_num_splits(0, 64, 640, 256) == 0
     # deterministic
     assert smla.smla_choose_num_splits(16, 64, 640, 256) == smla.smla_choose_num_splits(16, 64, 640, 256)
