@@ -134,6 +134,10 @@ smla_status combine_splits(const smla_params* p, int32_t num_splits, const float
   a.h_q = p->h_q;
   a.num_splits = num_splits;
   a.out_dtype = p->out_dtype;
+  // one wave per (token, head) row; as few rows per workgroup as keep the CUs busy
+  const int64_t rows = (int64_t)p->s_q * p->h_q;
+  const int32_t cus = device_cus();
+  a.heads_per_wg = rows <= cus ? 1 : rows <= 2 * cus ? 2 : 4;
   return smla::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 

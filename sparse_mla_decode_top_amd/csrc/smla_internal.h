@@ -36,6 +36,7 @@ struct CombineArgs {
   float* lse_out;
   int32_t s_q, h_q, num_splits;
   int32_t out_dtype;
+  int32_t heads_per_wg;       // 1, 2 or 4 (bf16 / f32 output)
 };
 
 // Each returns the launch status (hipSuccess or the runtime's error).

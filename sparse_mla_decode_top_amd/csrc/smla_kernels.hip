@@ -791,11 +791,14 @@ __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h)
 }
 
 // bf16 / fp32 output: 4 heads per workgroup, one wave per head.
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+// HPW heads (waves) per workgroup: 1 when few (token, head) rows would leave
+// compute units idle, so that each CU pulls fewer partial rows.
+template <int HPW>
+__global__ __launch_bounds__(64 * HPW) void combine_kernel(CombineArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bpt = (a.h_q + 3) / 4;
+  const int bpt = (a.h_q + HPW - 1) / HPW;
   const int t = blockIdx.x / bpt;
-  const int h = (blockIdx.x - t * bpt) * 4 + wave;
+  const int h = (blockIdx.x - t * bpt) * HPW + wave;
   if (h >= a.h_q) return;
   const Merged m = merge_head<16>(a, t, h);
   const int64_t row = (int64_t)t * a.h_q + h;
@@ -898,9 +901,12 @@ hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t st
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.out_dtype == kOutFp8) {
     hipLaunchKernelGGL(combine_fp8_kernel, dim3((unsigned)a.s_q), dim3(1024), 0, stream, a);
+  } else if (a.heads_per_wg == 1) {
+    hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)(a.s_q * a.h_q)), dim3(64), 0, stream, a);
+  } else if (a.heads_per_wg == 2) {
+    hipLaunchKernelGGL(combine_kernel<2>, dim3((unsigned)(a.s_q * ((a.h_q + 1) / 2))), dim3(128), 0, stream, a);
   } else {
-    const unsigned blocks = (unsigned)(a.s_q * ((a.h_q + 3) / 4));
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<4>, dim3((unsigned)(a.s_q * ((a.h_q + 3) / 4))), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
