@@ -168,13 +168,17 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   a.n_blocks = n_blocks_of(p->topk);
   a.out_dtype = p->out_dtype;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  // Few jobs leave most compute units idle: then 2 or 4 workgroups share each
+  // Few jobs leave most compute units idle: then 2, 4 or 8 workgroups share each
   // job, one per part of the 512 output columns (each computes the scores).
   // Not for a direct FP8 output, whose scale needs every column of a token.
   const bool direct = o_accum == nullptr;
   const int64_t jobs = (int64_t)p->s_q * (direct ? 1 : num_splits);
   const int32_t cus = device_cus();
-  a.col_parts = (direct && p->out_dtype == SMLA_OUT_FP8_E4M3) ? 1 : 4 * jobs <= cus ? 4 : 2 * jobs <= cus ? 2 : 1;
+  a.col_parts = (direct && p->out_dtype == SMLA_OUT_FP8_E4M3) ? 1
+                : 8 * jobs <= cus                                ? 8
+                : 4 * jobs <= cus                                ? 4
+                : 2 * jobs <= cus                                ? 2
+                                                                 : 1;
 
   if (direct) {        // direct path: one job per token, fused epilogue
     return smla::launch_decode_direct(a, fp8, hs) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;

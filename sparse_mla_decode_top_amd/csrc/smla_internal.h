@@ -24,7 +24,7 @@ struct DecodeArgs {
   int32_t s_q, h_q, topk, num_splits, n_blocks;
   int32_t out_dtype;          // smla_out_dtype (direct mode)
   float scale_log2;           // softmax_scale * log2(e)
-  int32_t col_parts;          // 1, 2 or 4 workgroups per job, each owning 512 / col_parts output columns
+  int32_t col_parts;          // 1, 2, 4 or 8 workgroups per job, each owning 512 / col_parts output columns
 };
 
 struct CombineArgs {

@@ -867,7 +867,13 @@ template <bool DIRECT>
 hipError_t launch_decode(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
   const unsigned n_jobs = (unsigned)(a.s_q * (DIRECT ? 1 : a.num_splits));
   const dim3 block(kThreads);
-  if (a.col_parts == 4) {
+  if (a.col_parts == 8) {
+    const dim3 grid((n_jobs + 7) / 8 * 64);
+    if (kv_fp8)
+      hipLaunchKernelGGL((decode_kernel<true, DIRECT, 8>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<false, DIRECT, 8>), grid, block, 0, stream, a);
+  } else if (a.col_parts == 4) {
     const dim3 grid((n_jobs + 7) / 8 * 32);
     if (kv_fp8)
       hipLaunchKernelGGL((decode_kernel<true, DIRECT, 4>), grid, block, 0, stream, a);
