@@ -68,6 +68,10 @@ constexpr float kNoFrame = 3.0e38f;
 
 enum OutDtype { kOutBf16 = 0, kOutF32 = 1, kOutFp8 = 2 };
 
+// A zero pool row: the spread-out gather copies it for masked slots, so each of
+// its DMA instructions is issued by every lane, branch free.
+__device__ __attribute__((aligned(256))) uint8_t g_zero_row[1152];
+
 // ---------------------------------------------------------------------------
 // LDS tile layout ("octet-major").  A bf16 row is 72 chunks of 16 bytes (8
 // elements), grouped in 9 octets of 8 chunks (128 bytes).  Chunk c of tile row
@@ -168,6 +172,26 @@ __device__ __forceinline__ int load_idx_and_q(const int32_t* idx_ptr, const void
 }
 #undef SMLA_DMA
 #undef SMLA_DMA_OP
+
+// One 16-byte direct-to-LDS load per lane: segment O of a row, i.e. global
+// address src + O * GSTEP and LDS address lds_base + O * LSTEP + 16 * lane (the
+// instruction offset O * GSTEP is added to both addresses, so m0 takes
+// lds_base + O * (LSTEP - GSTEP)).  Lets a block's gather be spread over the
+// MFMA work of the previous block.
+template <int LSTEP, int GSTEP, int O>
+__device__ __forceinline__ void dma_one(const void* src, uint32_t lds_base_uniform) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off offset:%4\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base_uniform), "n"(O * (LSTEP - GSTEP)), "n"(O * GSTEP)
+      : "memory");
+}
 
 // Hides a value from the optimiser, so that an address computed from it inside
 // the loop keeps its constant parts as instruction offsets instead of being
@@ -288,7 +312,10 @@ __device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int n_jo
 // The attention kernel.  KV_FP8: pool rows are e4m3 codes + a row scale.
 // DIRECT: single-split job writing the final output (sink + cast fused).
 // ---------------------------------------------------------------------------
-template <bool KV_FP8, bool DIRECT, int CS>
+// PREFETCH: some job has more than one block, so each block gathers the next
+// one (for a job's last block the gather copies the zero row into the idle
+// buffer, keeping the loop free of branches).
+template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeArgs a) {
   constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
   constexpr int kCols = 512 / CS;
@@ -435,15 +462,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
       lds_barrier();            // ... and every wave's; block b-1 fully consumed
 
-      // Prefetch block b+1 (its indices were loaded one block ahead).
+      // Block b+1 (indices loaded one block ahead) is gathered one DMA at a
+      // time between the MFMAs of block b's QK^T (see qk_half): a burst of 18
+      // stalls at issue when the memory pipeline is busy, and the MFMAs
+      // queued before each DMA keep running meanwhile.  Masked rows (and
+      // every row past the job's last block) copy the zero row.
       bool valid_nxt = false;
       float sc_nxt = 0.f;
-      if (b + 1 < job.b1) {
+      const uint8_t* gsrc[2] = {g_zero_row, g_zero_row};
+      uint32_t gbase[2] = {0u, 0u};
+      if (PREFETCH) {
         idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
-        issue_gather(idx_nxt, cur ^ 1);
         valid_nxt = valid_of(idx_nxt);
         if (KV_FP8 && wave == 0 && valid_nxt) sc_nxt = a.kv_scale[idx_nxt];
+        if (!KV_FP8) {
+#pragma unroll
+          for (int hgrp = 0; hgrp < 2; ++hgrp) {
+            const int rg = 2 * wave + hgrp;
+            const int row_idx = __shfl(idx_nxt, 8 * rg + (lane >> 3));
+            gsrc[hgrp] = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+                         (((lane & 7) ^ rsw(lane >> 3)) * 16);
+            gbase[hgrp] = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + rg * 1024);
+          }
+        } else {
+          const int row_idx = __shfl(idx_nxt, 16 * wave + (lane >> 2));
+          gsrc[0] = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
+          gbase[0] = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + wave * 1024);
+        }
       }
+      // DMA d of the next block: bf16 d = 0..17 (row group d / 9, octet d % 9);
+      // FP8 d = 0..8 (quartet d).
+      auto gather_dma = [&](const int d) __attribute__((always_inline)) {
+        if (!PREFETCH) return;
+        const int g = KV_FP8 ? 0 : d / 9, o = KV_FP8 ? d : d % 9;
+        constexpr int L = KV_FP8 ? 4096 : 8192, Gs = KV_FP8 ? 64 : 128;
+        switch (o) {
+          case 0: dma_one<L, Gs, 0>(gsrc[g], gbase[g]); break;
+          case 1: dma_one<L, Gs, 1>(gsrc[g], gbase[g]); break;
+          case 2: dma_one<L, Gs, 2>(gsrc[g], gbase[g]); break;
+          case 3: dma_one<L, Gs, 3>(gsrc[g], gbase[g]); break;
+          case 4: dma_one<L, Gs, 4>(gsrc[g], gbase[g]); break;
+          case 5: dma_one<L, Gs, 5>(gsrc[g], gbase[g]); break;
+          case 6: dma_one<L, Gs, 6>(gsrc[g], gbase[g]); break;
+          case 7: dma_one<L, Gs, 7>(gsrc[g], gbase[g]); break;
+          default: dma_one<L, Gs, 8>(gsrc[g], gbase[g]); break;
+        }
+      };
+      constexpr int kDmas = KV_FP8 ? 9 : 18;
       const int idx_after = load_idx(b + 2);
 
       const uint8_t* tile;
@@ -579,6 +644,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             sacc[2 * hh + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % (kAheadK + 1)][u], qf[ks],
                                                                        sacc[2 * hh + u], 0, 0, 0);
           if (hh == 1 && sm_at(ks) >= 0) sm_step(0, sm_at(ks));
+          // the next block's gather: DMAs 0..8 in half 0, 9..17 in half 1
+          if (ks < 9 && 9 * hh + ks < kDmas) gather_dma(9 * hh + ks);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -616,6 +683,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       sc_cur = sc_nxt;
       idx_nxt = idx_after;
     }
+    wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
     return overflow;
     };
 
@@ -863,45 +931,40 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(CombineArgs a) {
 }  // namespace
 
 namespace {
-template <bool DIRECT>
-hipError_t launch_decode(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
+template <bool DIRECT, bool PREFETCH>
+hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
   const unsigned n_jobs = (unsigned)(a.s_q * (DIRECT ? 1 : a.num_splits));
   const dim3 block(kThreads);
-  if (a.col_parts == 8) {
-    const dim3 grid((n_jobs + 7) / 8 * 64);
-    if (kv_fp8)
-      hipLaunchKernelGGL((decode_kernel<true, DIRECT, 8>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<false, DIRECT, 8>), grid, block, 0, stream, a);
-  } else if (a.col_parts == 4) {
-    const dim3 grid((n_jobs + 7) / 8 * 32);
-    if (kv_fp8)
-      hipLaunchKernelGGL((decode_kernel<true, DIRECT, 4>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<false, DIRECT, 4>), grid, block, 0, stream, a);
-  } else if (a.col_parts == 2) {
-    const dim3 grid((n_jobs + 7) / 8 * 16);
-    if (kv_fp8)
-      hipLaunchKernelGGL((decode_kernel<true, DIRECT, 2>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<false, DIRECT, 2>), grid, block, 0, stream, a);
-  } else {
-    const dim3 grid(n_jobs);
-    if (kv_fp8)
-      hipLaunchKernelGGL((decode_kernel<true, DIRECT, 1>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<false, DIRECT, 1>), grid, block, 0, stream, a);
-  }
+  const int cs = a.col_parts;
+  const dim3 grid(cs == 1 ? n_jobs : (n_jobs + 7) / 8 * 8 * cs);
+#define SMLA_LAUNCH(CSV)                                                                      \
+  do {                                                                                        \
+    if (kv_fp8)                                                                               \
+      hipLaunchKernelGGL((decode_kernel<true, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a);  \
+    else                                                                                      \
+      hipLaunchKernelGGL((decode_kernel<false, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a); \
+  } while (0)
+  if (cs == 8)
+    SMLA_LAUNCH(8);
+  else if (cs == 4)
+    SMLA_LAUNCH(4);
+  else if (cs == 2)
+    SMLA_LAUNCH(2);
+  else
+    SMLA_LAUNCH(1);
+#undef SMLA_LAUNCH
   return hipGetLastError();
 }
 }  // namespace
 
+// Jobs of one block at most (num_splits >= block count) need no look-ahead.
 hipError_t launch_decode_partial(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
-  return launch_decode<false>(a, kv_fp8, stream);
+  return a.num_splits >= a.n_blocks ? launch_decode_cs<false, false>(a, kv_fp8, stream)
+                                    : launch_decode_cs<false, true>(a, kv_fp8, stream);
 }
 
 hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
-  return launch_decode<true>(a, kv_fp8, stream);
+  return launch_decode_cs<true, true>(a, kv_fp8, stream);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
