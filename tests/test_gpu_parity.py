@@ -137,6 +137,28 @@ def test_fewer_heads(h_q):
         H.assert_lse_close(res["lse"], L_ref)
 
 
+def test_score_far_beyond_the_frame_restarts_the_job():
+    """A late slot whose log2-unit score exceeds the head's frame (fixed by the
+    first block) by far more than the 64-unit slack: the kernel re-runs the job
+    with the frame at the largest score.  Token 0: head 0 in block 5; token 1:
+    head 37 in the second half of block 9 (scores ~700 against a frame near 10).
+    LSE is compared relative to its size (f32 spacing near 700 is 6e-5)."""
+    inp = W.make_inputs(2, 64, 8192, 640, seed=21, sink=True)
+    q = inp.q
+    for t, head, slot in ((0, 0, 5 * 64 + 3), (1, 37, 9 * 64 + 40)):
+        row = int(inp.indices[t, slot])
+        inp.kv_bits[row] = W.f32_to_bf16_bits(20.0 * q[t, head])
+    dev = H.DeviceInputs(inp)
+    O_ref, L_ref = oracle.attend(q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    assert L_ref[0, 0] > 600 and L_ref[1, 37] > 600
+    for S, path in ((1, "direct"), (1, "split"), (2, "split"), (10, "split")):
+        res = H.run(dev, S, "f32", path)
+        H.assert_o_close(res["O"], O_fin)
+        lerr = np.abs(res["lse"] - L_ref) / np.maximum(1.0, np.abs(L_ref))
+        assert float(lerr.max()) <= H.TOL_LSE, f"S={S} {path}: relative LSE error {float(lerr.max()):.3g}"
+
+
 def test_ragged_topk_and_row_stride():
     """topk not a multiple of 64, and pool rows embedded in a wider buffer (row stride 640)."""
     inp = W.make_inputs(5, 64, 3000, 333, seed=12, sink=True, pad="random")
