@@ -7,31 +7,37 @@
 // the largest LSE) and cudnn-frontend PR #768 (near-equal block ranges with
 // the remainder on the leading splits; an empty split is O = 0, LSE = -inf).
 //
-// decode kernel: one workgroup of 4 wave64s per (token, split) job.
+// decode kernel: CS in {1, 2, 4, 8} workgroups of 4 wave64s per (token,
+// split) job, each owning 512 / CS output columns (all of them compute the
+// scores; few jobs then still occupy many compute units).
 //   * The 64 slots of a KV block share one LDS tile, gathered by index with
 //     16-byte direct-to-LDS loads (global_load_lds_dwordx4) in which 8 lanes
 //     fetch one contiguous 128-byte segment of a row; two tiles double-buffer
-//     the gather of block b+1 behind the compute of block b.  Masked slots are
-//     never read; their tile rows are zero-filled.
+//     the gather of block b+1 behind the compute of block b, its DMAs spread
+//     over block b's QK^T MFMAs.  Masked slots are never read: their tile
+//     rows are zero-filled, or copied from a zero row.
 //   * Wave w owns heads [16w, 16w+16) end to end, so the waves share nothing
 //     but the tile (one barrier per block).  S^T[slot][head] = K . Q^T and
 //     O^T[col][head] = V^T . P^T use v_mfma_f32_16x16x32_bf16; every lane
-//     holds one head's scores and accumulators.  Q stays in VGPRs (72 per
-//     lane); V^T is read from the row-major tile with the gfx950 transpose
-//     load ds_read_b64_tr_b16.
+//     holds one head's scores and accumulators.  Q is staged through LDS and
+//     kept in VGPRs (72 per lane); V^T is read from the row-major tile with
+//     the gfx950 transpose load ds_read_b64_tr_b16.  A block runs as two
+//     32-slot halves so that the softmax of one half is issued between the
+//     MFMAs of the other.
 //   * Softmax in log2 units against an integer frame M per head: each weight
 //     is p = 2^(t - floor t) * 2^(floor t - M).  Its bf16 rounding does not
 //     depend on M, so the partials of different split counts combine to the
 //     same value up to fp32 summation order.  M is the floor of the head's
-//     first non-empty block maximum and never moves inside a pass, so the
-//     accumulators are touched by MFMAs only (they stay in AGPRs).  A later
-//     score above M + 64 would risk overflow: the job then runs once more
-//     with M = floor of the largest score seen, which bounds every p by 2.
-//     The denominator sums the unrounded fp32 weights.
+//     first non-empty half-block maximum and never moves inside a pass, so
+//     the accumulators are touched by MFMAs only (they stay in AGPRs).  A
+//     later score above M + 64 would risk overflow: the job then runs once
+//     more with M = floor of the largest score seen, which bounds every p by
+//     2.  The denominator sums the unrounded fp32 weights.
 //   * P enters the PV product as two bf16 terms, hi = bf16(p) and
 //     lo = bf16(p - hi), sharing each V^T operand: a bf16-rounded P alone
 //     leaves O errors near 4e-3 when a few slots dominate (one 64-slot block);
 //     hi + lo carries p to about 2^-17 relative.
+//   * Outputs are staged through LDS and stored in whole-line pieces.
 //
 // combine kernel: split-major partials -> final output (+ sink, cast).
 
@@ -365,11 +371,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const uint32_t tile_lds0 = lds_addr(s_tile);
     constexpr int kBufBytes = KV_FP8 ? kCodeTileBytes : kTileBytes;
 
-    // Gather one block into buffer `buf`.  bf16: wave w fills rows
-    // [16w, 16w+16) as two groups of 8 rows; lane l gathers rows
-    // 16w + (l >> 3) and 16w + 8 + (l >> 3), chunk (l & 7) ^ swz of each octet.
-    // FP8: wave w fills rows [16w, 16w+16); lane l gathers row 16w + (l >> 2),
-    // chunk l & 3 of each quartet.  Masked rows are zero-filled.
+    // Gather a job's first block into buffer `buf` in one burst (nothing to
+    // overlap it with yet).  bf16: wave w fills rows [16w, 16w+16) as two
+    // groups of 8 rows; lane l gathers rows 16w + (l >> 3) and
+    // 16w + 8 + (l >> 3), chunk (l & 7) ^ (row & 7) of each octet.  FP8: wave w
+    // fills rows [16w, 16w+16); lane l gathers row 16w + (l >> 2), chunk l & 3
+    // of each quartet.  Masked rows are zero-filled.
     auto issue_gather = [&](int idx_lane, int buf) {
       if (!KV_FP8) {
 #pragma unroll
