@@ -42,17 +42,20 @@ Q_BYTES = 64 * 576 * 2
 IDX_BYTES = 640 * 4
 OUT_BYTES = 64 * 512 * 2       # bf16 output
 MAIN_BYTES_PER_TOKEN = KV_BYTES + Q_BYTES + IDX_BYTES     # 813,568: the attention kernel's share
+MAIN_BYTES_PER_TOKEN_FP8 = 640 * (576 + 4) + Q_BYTES + IDX_BYTES   # e4m3 rows + row scales: 447,488
 STEP_BYTES_PER_TOKEN = MAIN_BYTES_PER_TOKEN + OUT_BYTES   # 879,104
 FLOPS_PER_TOKEN = 2 * 64 * 640 * (576 + 512)              # 89,128,960
 KERNEL_SOURCE = os.path.join(ROOT, "sparse_mla_decode_top_amd", "csrc", "smla_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_kernel_single_token.json")
 
-WORKLOADS = {   # name -> (s_q, n_pool)
-    "single": (1, 65536),
-    "small6": (6, 131072),
-    "small16": (16, 131072),
-    "large96": (96, 262144),
-    "large384": (384, 262144),
+WORKLOADS = {   # name -> (s_q, n_pool, pool dtype / output dtype, fixed num_splits or 0)
+    "single": (1, 65536, "bf16", 0),
+    "small6": (6, 131072, "bf16", 0),
+    "small16": (16, 131072, "bf16", 0),
+    "large96": (96, 262144, "bf16", 0),
+    "large384": (384, 262144, "bf16", 0),
+    "fp8_1": (1, 131072, "fp8", 8),       # e4m3 pool + row scale, e4m3 output + token scale
+    "fp8_16": (16, 131072, "fp8", 8),
 }
 LLC_BYTES = 256 << 20
 
@@ -91,21 +94,29 @@ def source_hash():
 class Layer:
     """Device-resident inputs of one independent decode layer."""
 
-    def __init__(self, s_q, n_pool, seed, torch, W):
-        inp = W.make_inputs(s_q, 64, n_pool, 640, seed, kv_dtype="bf16", sink=True)
+    def __init__(self, s_q, n_pool, seed, torch, W, dtype="bf16"):
+        inp = W.make_inputs(s_q, 64, n_pool, 640, seed, kv_dtype=dtype, sink=True)
         self.inp = inp
         self.q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).cuda()
-        self.kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).cuda()
         self.indices = torch.from_numpy(inp.indices).cuda()
         self.sink = torch.from_numpy(inp.sink).cuda()
-        self.out = torch.empty((s_q, 64, 512), dtype=torch.bfloat16, device="cuda")
+        if dtype == "bf16":
+            self.kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).cuda()
+            self.kv_scale = None
+            self.out = torch.empty((s_q, 64, 512), dtype=torch.bfloat16, device="cuda")
+            self.out_scale = None
+        else:
+            self.kv = torch.from_numpy(inp.kv_codes).cuda()
+            self.kv_scale = torch.from_numpy(inp.kv_scale).cuda()
+            self.out = torch.empty((s_q, 64, 512), dtype=torch.uint8, device="cuda")
+            self.out_scale = torch.empty((s_q,), dtype=torch.float32, device="cuda")
 
 
-def build_layers(s_q, n_pool, torch, W, seed0=1000):
-    per_pool = n_pool * 576 * 2
+def build_layers(s_q, n_pool, torch, W, seed0=1000, dtype="bf16"):
+    per_pool = n_pool * 576 * (2 if dtype == "bf16" else 1)
     n_layers = max(2, -(-2 * LLC_BYTES // per_pool))       # pools total >= 2x the last-level cache
-    log(f"s_q={s_q}: generating {n_layers} layers of {per_pool / 1e6:.0f} MB pools")
-    return [Layer(s_q, n_pool, seed0 + i, torch, W) for i in range(n_layers)]
+    log(f"s_q={s_q}: generating {n_layers} layers of {per_pool / 1e6:.0f} MB {dtype} pools")
+    return [Layer(s_q, n_pool, seed0 + i, torch, W, dtype) for i in range(n_layers)]
 
 
 def time_steps(layers, S, steps, warmup, torch, smla):
@@ -116,8 +127,8 @@ def time_steps(layers, S, steps, warmup, torch, smla):
     lse_acc = torch.empty((S, s_q, 64), device="cuda") if S > 1 else None
 
     def step(L):
-        smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, sink=L.sink, o_accum=o_acc,
-                               lse_accum=lse_acc, out=L.out)
+        smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, kv_scale=L.kv_scale, sink=L.sink, o_accum=o_acc,
+                               lse_accum=lse_acc, out=L.out, out_scale=L.out_scale)
 
     for L in layers:                  # eager warm-up (also loads the library)
         step(L)
@@ -190,11 +201,12 @@ def kernel_durations(layers, S, reps, torch, smla):
         return e0.elapsed_time(e1) * 1e3 / reps
 
     if S == 1:
-        main = batch(lambda L: smla.sparse_mla_decode(L.q, L.kv, L.indices, 1, scale, sink=L.sink, out=L.out))
+        main = batch(lambda L: smla.sparse_mla_decode(L.q, L.kv, L.indices, 1, scale, kv_scale=L.kv_scale,
+                                                      sink=L.sink, out=L.out, out_scale=L.out_scale))
         return main, 0.0
-    main = batch(lambda L: smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, sink=L.sink,
-                                                  o_accum=o_acc, lse_accum=lse_acc))
-    comb = batch(lambda L: smla.combine_splits(o_acc, lse_acc, S, L.out, sink=L.sink))
+    main = batch(lambda L: smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, kv_scale=L.kv_scale,
+                                                  sink=L.sink, o_accum=o_acc, lse_accum=lse_acc))
+    comb = batch(lambda L: smla.combine_splits(o_acc, lse_acc, S, L.out, sink=L.sink, out_scale=L.out_scale))
     return main, comb
 
 
@@ -238,12 +250,13 @@ def cpu_baseline(layer, seconds):
 
 
 def measure(name, S_arg, steps, warmup, reps, torch, smla, W):
-    s_q, n_pool = WORKLOADS[name]
-    S = S_arg or smla.smla_choose_num_splits(s_q, 64, 640, 256)
-    layers = build_layers(s_q, n_pool, torch, W)
+    s_q, n_pool, dtype, S_fixed = WORKLOADS[name]
+    S = S_arg or S_fixed or smla.smla_choose_num_splits(s_q, 64, 640, 256)
+    layers = build_layers(s_q, n_pool, torch, W, dtype=dtype)
     us, ev_us, k, w = time_steps(layers, S, steps, warmup, torch, smla)
     main_us, comb_us = kernel_durations(layers, S, reps, torch, smla)
-    step_gbs = STEP_BYTES_PER_TOKEN * s_q / (ev_us * 1e-6) / 1e9
+    step_bytes = STEP_BYTES_PER_TOKEN if dtype == "bf16" else MAIN_BYTES_PER_TOKEN_FP8 + 64 * 512 + 4
+    step_gbs = step_bytes * s_q / (ev_us * 1e-6) / 1e9
     return dict(name=name, s_q=s_q, n_pool=n_pool, S=S, us=us, ev_us=ev_us, steps=k, warmup=w,
                 main_us=main_us, comb_us=comb_us, step_tbps=step_gbs / 1e3,
                 layers=len(layers)), layers
@@ -376,15 +389,16 @@ def main():
 
     sweep = {}
     if not args.no_sweep:
-        for name in ("small6", "small16", "large96", "large384"):
+        for name in ("small6", "small16", "large96", "large384", "fp8_1", "fp8_16"):
             if name == args.workload:
                 continue
             r, ls = measure(name, 0, max(20, args.steps // 4), args.warmup, max(20, args.kernel_reps // 4),
                             torch, smla, W)
             del ls
             torch.cuda.empty_cache()
-            mb = MAIN_BYTES_PER_TOKEN * r["s_q"]
-            sweep[name] = {"s_q": r["s_q"], "num_splits": r["S"], "us_per_step": round(r["ev_us"], 2),
+            mb = (MAIN_BYTES_PER_TOKEN if WORKLOADS[name][2] == "bf16" else MAIN_BYTES_PER_TOKEN_FP8) * r["s_q"]
+            sweep[name] = {"s_q": r["s_q"], "pool": WORKLOADS[name][2], "num_splits": r["S"],
+                           "us_per_step": round(r["ev_us"], 2),
                            "attention_kernel_us": round(r["main_us"], 2), "combine_us": round(r["comb_us"], 2),
                            "step_hbm_tbps": round(r["step_tbps"], 3),
                            "kernel_hbm_frac": round(mb / (r["main_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

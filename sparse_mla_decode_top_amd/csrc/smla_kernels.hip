@@ -868,14 +868,14 @@ __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h)
 // bf16 / fp32 output: 4 heads per workgroup, one wave per head.
 // HPW heads (waves) per workgroup: 1 when few (token, head) rows would leave
 // compute units idle, so that each CU pulls fewer partial rows.
-template <int HPW>
+template <int HPW, int CHUNK>
 __global__ __launch_bounds__(64 * HPW) void combine_kernel(CombineArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bpt = (a.h_q + HPW - 1) / HPW;
   const int t = blockIdx.x / bpt;
   const int h = (blockIdx.x - t * bpt) * HPW + wave;
   if (h >= a.h_q) return;
-  const Merged m = merge_head<16>(a, t, h);
+  const Merged m = merge_head<CHUNK>(a, t, h);
   const int64_t row = (int64_t)t * a.h_q + h;
   if (a.out_dtype == kOutF32) {
     *(f32x4*)((float*)a.out + row * 512 + 4 * lane) = m.lo;
@@ -888,51 +888,81 @@ __global__ __launch_bounds__(64 * HPW) void combine_kernel(CombineArgs a) {
   if (a.lse_out != nullptr && lane == 0) a.lse_out[row] = m.lse;
 }
 
-// FP8 output: one workgroup (16 waves) per token so the amax is a local
-// reduction; wave w merges heads w, w+16, ...
-__global__ __launch_bounds__(1024) void combine_fp8_kernel(CombineArgs a) {
-  __shared__ float s_red[16];
-  const int t = blockIdx.x;
+// FP8 output, in three launches that need no scratch memory.  The token's
+// scale needs the amax over all of its heads, so the rows are merged twice:
+//   init:   out_scale[t] = -0.0 (sign bit set: "an amax, not yet a scale")
+//   amax:   one wave per (token, head) merges the row; per 16 heads the
+//           largest amax raises out_scale[t] to 0x80000000 | bits(amax) with
+//           an unsigned atomic max (the bits of non-negative floats order like
+//           the floats);
+//   encode: one wave per (token, head) merges the row again, turns the value
+//           it reads in out_scale[t] into the scale (amax / 448, or 1 for a
+//           zero amax, when the sign bit is set; the scale itself otherwise),
+//           writes the e4m3 codes, and the wave of head 0 stores the scale.
+//           Every wave of the token derives the same scale whichever of the
+//           two forms it reads.
+__global__ __launch_bounds__(256) void combine_fp8_init_kernel(CombineArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < a.s_q) a.out_scale[t] = -0.0f;
+}
+
+__device__ __forceinline__ float abs_max4(f32x4 v) {
+  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+
+// HW heads per workgroup (one per wave): the heads' amaxes meet in LDS, so a
+// token sees h_q / HW atomics rather than h_q.  HW = 4 spreads a small batch
+// over more compute units; HW = 16 keeps the atomics of a large one few.
+template <int HW, int CHUNK>
+__global__ __launch_bounds__(64 * HW) void combine_fp8_amax_kernel(CombineArgs a) {
+  __shared__ float s_amax[HW];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  f32x4 o[4][2];
+  const int bpt = (a.h_q + HW - 1) / HW;
+  const int t = blockIdx.x / bpt;
+  const int h = (blockIdx.x - t * bpt) * HW + wave;
   float amax = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int h = wave + 16 * k;
-    o[k][0] = o[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (h < a.h_q) {
-      const Merged m = merge_head<8>(a, t, h);     // four heads per wave: fewer rows in flight
-      o[k][0] = m.lo;
-      o[k][1] = m.hi;
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[k][half][0]), fabsf(o[k][half][1])),
-                                 fmaxf(fabsf(o[k][half][2]), fabsf(o[k][half][3]))));
-      if (a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)t * a.h_q + h] = m.lse;
-    }
+  if (h < a.h_q) {
+    const Merged m = merge_head<CHUNK>(a, t, h);
+    amax = wave_max(fmaxf(abs_max4(m.lo), abs_max4(m.hi)));
+    if (lane == 0 && a.lse_out != nullptr) a.lse_out[(int64_t)t * a.h_q + h] = m.lse;
   }
-  amax = warp_max(amax);
-  if (lane == 0) s_red[wave] = amax;
+  if (lane == 0) s_amax[wave] = amax;
   __syncthreads();
-  amax = 0.f;
+  if (threadIdx.x == 0) {
+    float v = 0.f;
 #pragma unroll
-  for (int w = 0; w < 16; ++w) amax = fmaxf(amax, s_red[w]);
-  const float qscale = amax > 0.f ? amax / 448.0f : 1.0f;
-  if (threadIdx.x == 0) a.out_scale[t] = qscale;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int h = wave + 16 * k;
-    if (h < a.h_q) {
-      uint8_t* orow = (uint8_t*)a.out + ((int64_t)t * a.h_q + h) * 512;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t wd = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wd |= e4m3_encode(o[k][half][e] / qscale) << (8 * e);
-        *(uint32_t*)(orow + 256 * half + 4 * lane) = wd;
-      }
-    }
+    for (int w = 0; w < HW; ++w) v = fmaxf(v, s_amax[w]);
+    __hip_atomic_fetch_max((uint32_t*)a.out_scale + t, 0x80000000u | __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+template <int HPW, int CHUNK>
+__global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bpt = (a.h_q + HPW - 1) / HPW;
+  const int t = blockIdx.x / bpt;
+  const int h = (blockIdx.x - t * bpt) * HPW + wave;
+  if (h >= a.h_q) return;
+  const Merged m = merge_head<CHUNK>(a, t, h);
+  const uint32_t v = __hip_atomic_load((const uint32_t*)a.out_scale + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float qscale;
+  if (v & 0x80000000u) {
+    const float amax = __uint_as_float(v & 0x7FFFFFFFu);
+    qscale = amax > 0.f ? amax / 448.0f : 1.0f;
+  } else {
+    qscale = __uint_as_float(v);
+  }
+  uint8_t* orow = (uint8_t*)a.out + ((int64_t)t * a.h_q + h) * 512;
+  uint32_t wlo = 0, whi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    wlo |= e4m3_encode(m.lo[e] / qscale) << (8 * e);
+    whi |= e4m3_encode(m.hi[e] / qscale) << (8 * e);
+  }
+  *(uint32_t*)(orow + 4 * lane) = wlo;
+  *(uint32_t*)(orow + 256 + 4 * lane) = whi;
+  if (h == 0 && lane == 0) a.out_scale[t] = qscale;
 }
 
 }  // namespace
@@ -974,17 +1004,39 @@ hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t st
   return launch_decode_cs<true, true>(a, kv_fp8, stream);
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+namespace {
+// CHUNK: partial rows requested per pass (4, 8 or 16), the smallest that holds
+// every split, so no load repeats a row needlessly.
+template <int CHUNK>
+hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
+  const unsigned rows = (unsigned)(a.s_q * a.h_q);
+  const unsigned blocks4 = (unsigned)(a.s_q * ((a.h_q + 3) / 4));
   if (a.out_dtype == kOutFp8) {
-    hipLaunchKernelGGL(combine_fp8_kernel, dim3((unsigned)a.s_q), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL(combine_fp8_init_kernel, dim3((unsigned)((a.s_q + 255) / 256)), dim3(256), 0, stream, a);
+    if (a.heads_per_wg == 1)
+      hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((combine_fp8_amax_kernel<16, CHUNK>), dim3((unsigned)(a.s_q * ((a.h_q + 15) / 16))),
+                         dim3(1024), 0, stream, a);
+    if (a.heads_per_wg == 1)
+      hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK>), dim3(rows), dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
   } else if (a.heads_per_wg == 1) {
-    hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)(a.s_q * a.h_q)), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<1, CHUNK>), dim3(rows), dim3(64), 0, stream, a);
   } else if (a.heads_per_wg == 2) {
-    hipLaunchKernelGGL(combine_kernel<2>, dim3((unsigned)(a.s_q * ((a.h_q + 1) / 2))), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<2, CHUNK>), dim3((unsigned)(a.s_q * ((a.h_q + 1) / 2))), dim3(128), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(combine_kernel<4>, dim3((unsigned)(a.s_q * ((a.h_q + 3) / 4))), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  if (a.num_splits <= 4) return launch_combine_chunk<4>(a, stream);
+  if (a.num_splits <= 8) return launch_combine_chunk<8>(a, stream);
+  return launch_combine_chunk<16>(a, stream);
 }
 
 }  // namespace smla
