@@ -16,6 +16,8 @@ SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "smla_api.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # preload the attention kernel's leading scalar arguments into SGPRs
+    "-mllvm", "-amdgpu-kernarg-preload-count=7",
     "-Wall", "-Wno-unused-lambda-capture",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -321,8 +321,13 @@ __device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int n_jo
 // PREFETCH: some job has more than one block, so each block gathers the next
 // one (for a job's last block the gather copies the zero row into the idle
 // buffer, keeping the loop free of branches).
+// The fields that the first instructions need come as leading scalar
+// arguments, which the build asks to be preloaded into SGPRs at wave launch:
+// the index and Q loads then issue without waiting for a kernel-argument load.
 template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(
+    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
+    int32_t s_q, int32_t topk, int32_t h_q, DecodeArgs a) {
   constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
   constexpr int kCols = 512 / CS;
   constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
@@ -340,10 +345,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
   const int head = 16 * wave + hl;
 
-  const Job job = decode_job<CS>(a.num_splits, a.n_blocks, a.s_q * a.num_splits);
+  const Job job = decode_job<CS>(num_splits, n_blocks, s_q * num_splits);
   if (!job.live) return;                          // padding of the CS > 1 grid (whole workgroup)
   const int t = job.t;
-  const int32_t* idx_row = a.indices + (int64_t)t * a.topk;
+  const int32_t* idx_row = indices + (int64_t)t * topk;
 
   float M_run = kNoFrame;             // integer frame of this lane's head (log2 units)
   float m_seen = kMaskedScore;        // largest score seen so far
@@ -360,9 +365,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // branch, hence no early wait on it); slots past the split or the list are
     // masked where the index is used.
     auto load_idx = [&](int b) -> int {
-      return __builtin_nontemporal_load(idx_row + min(b * kBlk + lane, a.topk - 1));
+      return __builtin_nontemporal_load(idx_row + min(b * kBlk + lane, topk - 1));
     };
-    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < a.topk; };
+    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
     auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
     const float scale_log2 = a.scale_log2;
     // Q fragments (B operand of S^T = K . Q^T): head, dims 32ks + 8G .. +8.
@@ -427,10 +432,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     {
       const int r0 = 16 * wave + (lane >> 3), r1 = r0 + 8;
       const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
-      const uint8_t* qbase = (const uint8_t*)(a.q + (int64_t)t * a.h_q * 576);
-      idx_cur = load_idx_and_q(idx_row + min(job.b0 * kBlk + lane, a.topk - 1),
-                               qbase + (int64_t)(r0 < a.h_q ? r0 : 0) * 1152 + chunk,
-                               qbase + (int64_t)(r1 < a.h_q ? r1 : 0) * 1152 + chunk,
+      const uint8_t* qbase = (const uint8_t*)(q_ptr + (int64_t)t * h_q * 576);
+      idx_cur = load_idx_and_q(idx_row + min(job.b0 * kBlk + lane, topk - 1),
+                               qbase + (int64_t)(r0 < h_q ? r0 : 0) * 1152 + chunk,
+                               qbase + (int64_t)(r1 < h_q ? r1 : 0) * 1152 + chunk,
                                __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + (2 * wave) * 1024),
                                __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + (2 * wave + 1) * 1024));
     }
@@ -714,7 +719,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const bool any = l_head > 0.f;
   const float lse = any ? M_run + __builtin_amdgcn_logf(l_head) : kNegInf;
   float oscale = any ? 1.0f / l_head : 0.f;
-  const bool wave_ok = 16 * wave < a.h_q;        // h_q is a multiple of 16
+  const bool wave_ok = 16 * wave < h_q;        // h_q is a multiple of 16
   if (DIRECT && a.sink != nullptr && any && wave_ok) {
     const float z = a.sink[head] * kLog2e - lse;
     oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
@@ -747,7 +752,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (tid == 0) a.out_scale[t] = qscale;
   }
   if (wave_ok) {
-    const int64_t row0 = (DIRECT ? (int64_t)t * a.h_q : ((int64_t)job.s * a.s_q + t) * a.h_q) + 16 * wave;
+    const int64_t row0 = (DIRECT ? (int64_t)t * h_q : ((int64_t)job.s * s_q + t) * h_q) + 16 * wave;
     const int col0 = job.part * kCols;
     if (!DIRECT || a.out_dtype == kOutF32) {     // 1 KB of whole row pieces per instruction
       float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + col0;
@@ -977,9 +982,11 @@ hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream
 #define SMLA_LAUNCH(CSV)                                                                      \
   do {                                                                                        \
     if (kv_fp8)                                                                               \
-      hipLaunchKernelGGL((decode_kernel<true, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a);  \
-    else                                                                                      \
-      hipLaunchKernelGGL((decode_kernel<false, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a); \
+      hipLaunchKernelGGL((decode_kernel<true, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a.indices, a.q,  \
+                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                                  \
+    else                                                                                                     \
+      hipLaunchKernelGGL((decode_kernel<false, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a.indices, a.q, \
+                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                                  \
   } while (0)
   if (cs == 8)
     SMLA_LAUNCH(8);
