@@ -873,8 +873,17 @@ __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h)
 // bf16 / fp32 output: 4 heads per workgroup, one wave per head.
 // HPW heads (waves) per workgroup: 1 when few (token, head) rows would leave
 // compute units idle, so that each CU pulls fewer partial rows.
+// The fields the first loads need come as leading (SGPR-preloaded) arguments.
 template <int HPW, int CHUNK>
-__global__ __launch_bounds__(64 * HPW) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(64 * HPW) void combine_kernel(const float* __restrict__ o_accum,
+                                                           const float* __restrict__ lse_accum, int32_t s_q,
+                                                           int32_t h_q, int32_t num_splits, CombineArgs args) {
+  CombineArgs a = args;
+  a.o_accum = o_accum;
+  a.lse_accum = lse_accum;
+  a.s_q = s_q;
+  a.h_q = h_q;
+  a.num_splits = num_splits;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bpt = (a.h_q + HPW - 1) / HPW;
   const int t = blockIdx.x / bpt;
@@ -1030,11 +1039,14 @@ hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
   } else if (a.heads_per_wg == 1) {
-    hipLaunchKernelGGL((combine_kernel<1, CHUNK>), dim3(rows), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<1, CHUNK>), dim3(rows), dim3(64), 0, stream, a.o_accum, a.lse_accum, a.s_q,
+                       a.h_q, a.num_splits, a);
   } else if (a.heads_per_wg == 2) {
-    hipLaunchKernelGGL((combine_kernel<2, CHUNK>), dim3((unsigned)(a.s_q * ((a.h_q + 1) / 2))), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<2, CHUNK>), dim3((unsigned)(a.s_q * ((a.h_q + 1) / 2))), dim3(128), 0, stream,
+                       a.o_accum, a.lse_accum, a.s_q, a.h_q, a.num_splits, a);
   } else {
-    hipLaunchKernelGGL((combine_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a.o_accum, a.lse_accum,
+                       a.s_q, a.h_q, a.num_splits, a);
   }
   return hipGetLastError();
 }
