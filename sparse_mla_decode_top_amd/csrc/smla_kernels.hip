@@ -637,28 +637,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       // ---- QK^T of one half: 2 slot tiles x 18 k-steps; the K fragments of
       // k-step ks+kAheadK are requested before the MFMAs of ks.  hh = 1
       // carries the softmax of half 0.
-      constexpr int kAheadK = 4, kAheadV = 4;
+      // MFMAs on one accumulator are issued back to back in pairs (k-steps
+      // 2j and 2j+1): on gfx950 alternating accumulators from one MFMA to the
+      // next measured about 21 cycles per 16x16x32 MFMA, pairs about 16.5.
+      constexpr int kAheadK = 4, kAheadV = 4, kRing = kAheadK + 2;
       auto qk_half = [&](const int hh) __attribute__((always_inline)) {
-        bf16x8 kf[kAheadK + 1][2];
+        bf16x8 kf[kRing][2];
 #pragma unroll
         for (int a0 = 0; a0 < kAheadK; ++a0)
 #pragma unroll
           for (int u = 0; u < 2; ++u) kf[a0][u] = kfrag(a0, 2 * hh + u);
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          if (ks + kAheadK < 18) {
+        for (int j = 0; j < 9; ++j) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) kf[(ks + kAheadK) % (kAheadK + 1)][u] = kfrag(ks + kAheadK, 2 * hh + u);
+          for (int e = 0; e < 2; ++e) {
+            const int ka = 2 * j + e + kAheadK;
+            if (ka < 18) {
+#pragma unroll
+              for (int u = 0; u < 2; ++u) kf[ka % kRing][u] = kfrag(ka, 2 * hh + u);
+            }
           }
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
-            sacc[2 * hh + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % (kAheadK + 1)][u], qf[ks],
-                                                                       sacc[2 * hh + u], 0, 0, 0);
-          if (hh == 1 && sm_at(ks) >= 0) sm_step(0, sm_at(ks));
-          // the next block's gather: DMAs 0..8 in half 0, 9..17 in half 1
-          if (ks < 9 && 9 * hh + ks < kDmas) gather_dma(9 * hh + ks);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int u = 0; u < 2; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int ks = 2 * j + e;
+              sacc[2 * hh + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % kRing][u], qf[ks],
+                                                                         sacc[2 * hh + u], 0, 0, 0);
+            }
+            const int ks = 2 * j + u;              // the VALU / DMA slot of k-step ks
+            if (hh == 1 && sm_at(ks) >= 0) sm_step(0, sm_at(ks));
+            // the next block's gather: DMAs 0..8 in half 0, 9..17 in half 1
+            if (ks < 9 && 9 * hh + ks < kDmas) gather_dma(9 * hh + ks);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       };
       // ---- O^T += V^T . P^T over one half (k-step kk): the kCt column tiles
@@ -988,23 +1001,23 @@ hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream
   const dim3 block(kThreads);
   const int cs = a.col_parts;
   const dim3 grid(cs == 1 ? n_jobs : (n_jobs + 7) / 8 * 8 * cs);
-#define SMLA_LAUNCH(CSV)                                                                      \
-  do {                                                                                        \
-    if (kv_fp8)                                                                               \
-      hipLaunchKernelGGL((decode_kernel<true, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a.indices, a.q,  \
-                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                                  \
-    else                                                                                                     \
-      hipLaunchKernelGGL((decode_kernel<false, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a.indices, a.q, \
-                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                                  \
+#define SMLA_LAUNCH(KERNEL, CSV)                                                                            \
+  do {                                                                                                      \
+    if (kv_fp8)                                                                                             \
+      hipLaunchKernelGGL((KERNEL<true, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a.indices, a.q,      \
+                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                                \
+    else                                                                                                    \
+      hipLaunchKernelGGL((KERNEL<false, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a.indices, a.q,     \
+                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                                \
   } while (0)
   if (cs == 8)
-    SMLA_LAUNCH(8);
+    SMLA_LAUNCH(decode_kernel, 8);
   else if (cs == 4)
-    SMLA_LAUNCH(4);
+    SMLA_LAUNCH(decode_kernel, 4);
   else if (cs == 2)
-    SMLA_LAUNCH(2);
+    SMLA_LAUNCH(decode_kernel, 2);
   else
-    SMLA_LAUNCH(1);
+    SMLA_LAUNCH(decode_kernel, 1);
 #undef SMLA_LAUNCH
   return hipGetLastError();
 }
