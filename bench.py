@@ -6,7 +6,11 @@ over every (token, split) job plus the combine, on inputs already resident in
 HBM.  Steps are replayed from a HIP graph (the pages time their kernels under
 CUDA graphs) and cycle through L distinct "layers" -- independent pools,
 queries and index lists whose pools together exceed the 256 MB last-level
-cache -- so the gathered rows come from HBM as in a multi-layer decode.
+cache.  At small s_q the rows that all layers gather (0.74 MB per token and
+layer) still fit in that cache and stay there across replays, so the graph
+figure is a warm-cache one there; at s_q = 384 the gathered rows exceed it.
+cold_us_per_step repeats the step with every cache flushed before it (a 1 GiB
+overwrite between steps), so that indices, Q and rows all come from HBM.
 
 Prints ONE JSON line (rank 0, N = 1):
   value        microseconds per step (lower is better) at the single-token
@@ -14,8 +18,10 @@ Prints ONE JSON line (rank 0, N = 1):
                num_splits from smla_choose_num_splits
   roofline     the attention kernel's algorithmic bytes per launch over its mean
                duration (HIP events on its launch stream), against 8 TB/s
+  cold_us_per_step  the same step with the caches flushed before each step
   cpu_baseline the float64 oracle timed on the host cores on the same inputs
-  sweep        the same measurement at s_q = 6, 16, 96, 384 (context)
+  sweep        the same measurement at s_q = 6, 16, 96, 384 and for the FP8
+               path (context)
 """
 import argparse
 import hashlib
@@ -164,6 +170,37 @@ def time_steps(layers, S, steps, warmup, torch, smla):
     return (t1 - t0) * 1e6 / k, e0.elapsed_time(e1) * 1e3 / k, k, reps_w * n
 
 
+def time_cold(layers, S, steps, torch, smla, flush_bytes=1 << 30):
+    """Median step time with the caches flushed before every step: a 1 GiB buffer is
+    overwritten between steps (evicting the L2s and the 256 MB last-level cache, so the
+    indices, Q and the gathered rows all come from HBM), and a pair of HIP events on the
+    launch stream brackets each step alone (the flush runs before the first event)."""
+    s_q = layers[0].inp.s_q
+    scale = layers[0].inp.scale
+    o_acc = torch.empty((S, s_q, 64, 512), device="cuda") if S > 1 else None
+    lse_acc = torch.empty((S, s_q, 64), device="cuda") if S > 1 else None
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+
+    def step(L):
+        smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, kv_scale=L.kv_scale, sink=L.sink, o_accum=o_acc,
+                               lse_accum=lse_acc, out=L.out, out_scale=L.out_scale)
+
+    for L in layers:
+        step(L)
+    stream = torch.cuda.current_stream()
+    evs = []
+    for i in range(steps):
+        flush.fill_(float(i & 7))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(layers[i % len(layers)])
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del flush
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+
 def sleep_cycles_for(ms, torch):
     """torch.cuda._sleep argument that keeps the GPU busy about `ms` milliseconds."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -255,10 +292,11 @@ def measure(name, S_arg, steps, warmup, reps, torch, smla, W):
     layers = build_layers(s_q, n_pool, torch, W, dtype=dtype)
     us, ev_us, k, w = time_steps(layers, S, steps, warmup, torch, smla)
     main_us, comb_us = kernel_durations(layers, S, reps, torch, smla)
+    cold_us = time_cold(layers, S, max(20, steps // 4), torch, smla)
     step_bytes = STEP_BYTES_PER_TOKEN if dtype == "bf16" else MAIN_BYTES_PER_TOKEN_FP8 + 64 * 512 + 4
     step_gbs = step_bytes * s_q / (ev_us * 1e-6) / 1e9
     return dict(name=name, s_q=s_q, n_pool=n_pool, S=S, us=us, ev_us=ev_us, steps=k, warmup=w,
-                main_us=main_us, comb_us=comb_us, step_tbps=step_gbs / 1e3,
+                main_us=main_us, comb_us=comb_us, step_tbps=step_gbs / 1e3, cold_us=cold_us,
                 layers=len(layers)), layers
 
 
@@ -372,7 +410,7 @@ def main():
                            torch, smla, W)
     s_q, S = head["s_q"], head["S"]
     log(f"{args.workload}: {head['us']:.2f} us/step (events {head['ev_us']:.2f}), attention kernel "
-        f"{head['main_us']:.2f} us, combine {head['comb_us']:.2f} us, S={S}")
+        f"{head['main_us']:.2f} us, combine {head['comb_us']:.2f} us, cold step {head['cold_us']:.2f} us, S={S}")
     main_bytes = MAIN_BYTES_PER_TOKEN * s_q
     achieved = main_bytes / (head["main_us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -398,13 +436,14 @@ def main():
             torch.cuda.empty_cache()
             mb = (MAIN_BYTES_PER_TOKEN if WORKLOADS[name][2] == "bf16" else MAIN_BYTES_PER_TOKEN_FP8) * r["s_q"]
             sweep[name] = {"s_q": r["s_q"], "pool": WORKLOADS[name][2], "num_splits": r["S"],
-                           "us_per_step": round(r["ev_us"], 2),
+                           "us_per_step": round(r["ev_us"], 2), "cold_us_per_step": round(r["cold_us"], 2),
                            "attention_kernel_us": round(r["main_us"], 2), "combine_us": round(r["comb_us"], 2),
                            "step_hbm_tbps": round(r["step_tbps"], 3),
                            "kernel_hbm_frac": round(mb / (r["main_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                            "kernel_mfma_frac": round(FLOPS_PER_TOKEN * r["s_q"] / (r["main_us"] * 1e-6) / 1e12
                                                      / BF16_PEAK_TFLOPS, 4)}
-            log(f"{name}: {r['ev_us']:.2f} us/step, kernel {r['main_us']:.2f} us, S={r['S']}")
+            log(f"{name}: {r['ev_us']:.2f} us/step, kernel {r['main_us']:.2f} us, cold step {r['cold_us']:.2f} us, "
+                f"S={r['S']}")
 
     line = {
         "metric": METRIC, "value": round(head["ev_us"], 3), "unit": "us/step", "n_gpus": 1,
@@ -414,8 +453,11 @@ def main():
         "config": {"workload": f"single-token decode: s_q={s_q}, h_q=64, d_qk=576, d_v=512, topk=640, "
                                f"pool {head['n_pool']} bf16 rows x {head['layers']} layers, sink on, "
                                f"num_splits={S}",
-                   "global_batch": s_q, "num_splits": S, "timing": "HIP graph replay, cold layer rotation"},
+                   "global_batch": s_q, "num_splits": S,
+                   "timing": "HIP graph replay over the layers (warm: the rows all layers gather stay in the "
+                             "last-level cache at this size); cold_us_per_step flushes the caches before each step"},
         "hbm_tbps": round(head["step_tbps"], 4),
+        "cold_us_per_step": round(head["cold_us"], 3),
         "wall_us_per_step": round(head["us"], 3),
         "attention_kernel_us": round(head["main_us"], 3),
         "combine_kernel_us": round(head["comb_us"], 3),
