@@ -318,6 +318,30 @@ def summarize_kernel_stats(directory):
     for r in rows:
         print(f"{r['Name'][:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.3f} "
               f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
+    # The dispatches of the event-timed batches (kernel_durations): a GPU sleep, then
+    # one kernel launched back to back many times.  Their mean trace duration is the
+    # like-for-like counterpart of the HIP-event figure.
+    trace = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    print("\ndispatches of the event-timed batches (runs of >= 20 launches of one kernel after the GPU sleep):")
+    print(f"{'kernel':64s} {'batches':>7s} {'calls':>6s} {'avg_us':>9s}")
+    agg = {}
+    i = 0
+    while i < len(trace):
+        if "spin_kernel" not in trace[i]["Kernel_Name"]:
+            i += 1
+            continue
+        j = i + 1
+        while j < len(trace) and trace[j]["Kernel_Name"] == trace[i + 1]["Kernel_Name"]:
+            j += 1
+        run = trace[i + 1:j]
+        if len(run) >= 20:
+            a = agg.setdefault(run[0]["Kernel_Name"], [0, 0, 0.0])
+            a[0] += 1
+            a[1] += len(run)
+            a[2] += sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in run)
+        i += 1
+    for k, (nb, nc, ns) in agg.items():
+        print(f"{k[:64]:64s} {nb:7d} {nc:6d} {ns / nc / 1e3:9.3f}")
 
 
 def _counter_per_dispatch(directory, counter):

@@ -113,9 +113,15 @@ smla_status smla_validate(const smla_params* p, const void* q, const void* kv_po
   return SMLA_OK;
 }
 
-smla_status combine_splits(const smla_params* p, int32_t num_splits, const float* o_accum,
-                           const float* lse_accum, const float* sink, void* out, float* out_scale,
-                           float* lse_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The combine launch sequence; scale_ready: an FP8 output's out_scale already
+// holds the combine's starting value (-0.0).
+smla_status run_combine(const smla_params* p, int32_t num_splits, const float* o_accum, const float* lse_accum,
+                        const float* sink, void* out, float* out_scale, float* lse_out, void* stream,
+                        bool scale_ready) {
   smla_status st = check_common_shape(p, num_splits);
   if (st != SMLA_OK) return st;
   if (o_accum == nullptr || lse_accum == nullptr) return SMLA_ERR_MISSING_WORKSPACE;
@@ -138,7 +144,18 @@ smla_status combine_splits(const smla_params* p, int32_t num_splits, const float
   const int64_t rows = (int64_t)p->s_q * p->h_q;
   const int32_t cus = device_cus();
   a.heads_per_wg = rows <= cus ? 1 : rows <= 2 * cus ? 2 : 4;
+  a.scale_ready = scale_ready ? 1 : 0;
   return smla::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status combine_splits(const smla_params* p, int32_t num_splits, const float* o_accum,
+                           const float* lse_accum, const float* sink, void* out, float* out_scale,
+                           float* lse_out, void* stream) {
+  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, false);
 }
 
 smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* kv_pool, const float* kv_scale,
@@ -157,7 +174,10 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   a.o_accum = o_accum;
   a.lse_accum = lse_accum;
   a.out = out;
-  a.out_scale = out_scale;
+  const bool direct = o_accum == nullptr;
+  // split mode with an FP8 output to follow: the attention kernel seeds out_scale
+  const bool seed_scale = !direct && out != nullptr && p->out_dtype == SMLA_OUT_FP8_E4M3;
+  a.out_scale = (direct || seed_scale) ? out_scale : nullptr;
   a.lse_out = lse_out;
   a.n_pool = p->n_pool;
   a.row_stride_bytes = p->kv_row_stride * (fp8 ? 1 : 2);
@@ -171,7 +191,6 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   // Few jobs leave most compute units idle: then 2, 4 or 8 workgroups share each
   // job, one per part of the 512 output columns (each computes the scores).
   // Not for a direct FP8 output, whose scale needs every column of a token.
-  const bool direct = o_accum == nullptr;
   const int64_t jobs = (int64_t)p->s_q * (direct ? 1 : num_splits);
   const int32_t cus = device_cus();
   a.col_parts = (direct && p->out_dtype == SMLA_OUT_FP8_E4M3) ? 1
@@ -185,7 +204,7 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   }
   if (smla::launch_decode_partial(a, fp8, hs) != hipSuccess) return SMLA_ERR_HIP;
   if (out == nullptr) return SMLA_OK;   // partial-only: the caller combines
-  return combine_splits(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream);
+  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, seed_scale);
 }
 
 }  // extern "C"

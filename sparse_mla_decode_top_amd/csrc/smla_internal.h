@@ -17,7 +17,8 @@ struct DecodeArgs {
   float* o_accum;             // [S][s_q][h_q][512]   (partial mode)
   float* lse_accum;           // [S][s_q][h_q]        (partial mode)
   void* out;                  // [s_q][h_q][512]      (direct mode)
-  float* out_scale;           // [s_q]                (direct mode, FP8 out)
+  float* out_scale;           // [s_q] FP8 out: the scale (direct mode), or set to -0.0 for the combine
+                              // (split mode with an FP8 output to follow); else nullptr
   float* lse_out;             // [s_q][h_q] or nullptr (direct mode)
   int64_t n_pool;
   int64_t row_stride_bytes;
@@ -37,6 +38,7 @@ struct CombineArgs {
   int32_t s_q, h_q, num_splits;
   int32_t out_dtype;
   int32_t heads_per_wg;       // 1, 2 or 4 (bf16 / f32 output)
+  int32_t scale_ready;        // FP8 output: out_scale already holds -0.0 (set by the attention kernel)
 };
 
 // Each returns the launch status (hipSuccess or the runtime's error).

@@ -810,6 +810,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         a.lse_out[row0 + hl] = lse;
     }
   }
+  // Split jobs of a decode with an FP8 output: the combine's running amax per
+  // token starts from -0.0 (its "an amax, not yet a scale" form), stored here
+  // so that the combine needs no launch of its own for it.
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1041,7 +1045,8 @@ hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.s_q * a.h_q);
   const unsigned blocks4 = (unsigned)(a.s_q * ((a.h_q + 3) / 4));
   if (a.out_dtype == kOutFp8) {
-    hipLaunchKernelGGL(combine_fp8_init_kernel, dim3((unsigned)((a.s_q + 255) / 256)), dim3(256), 0, stream, a);
+    if (!a.scale_ready)
+      hipLaunchKernelGGL(combine_fp8_init_kernel, dim3((unsigned)((a.s_q + 255) / 256)), dim3(256), 0, stream, a);
     if (a.heads_per_wg == 1)
       hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
     else

@@ -327,3 +327,42 @@ def test_graph_capture_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
+def test_graph_capture_fp8_output_replays_match_eager():
+    """FP8 pool and FP8 output, split path in a HIP graph: the attention kernel seeds each
+    token's running amax before the combine's atomics, on every replay."""
+    import sparse_mla_decode_top_amd as smla
+    dev = dev_for("fp8_16", 0)
+    inp = dev.inp
+    S = 8
+    o_acc = torch.empty((S, inp.s_q, 64, 512), device="cuda")
+    lse_acc = torch.empty((S, inp.s_q, 64), device="cuda")
+    out = torch.empty((inp.s_q, 64, 512), device="cuda", dtype=torch.uint8)
+    scale = torch.empty((inp.s_q,), device="cuda")
+
+    def step():
+        smla.sparse_mla_decode(dev.q, dev.kv, dev.indices, S, inp.scale, kv_scale=dev.kv_scale, sink=dev.sink,
+                               o_accum=o_acc, lse_accum=lse_acc, out=out, out_scale=scale)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_scale = out.clone(), scale.clone()
+    ref = H.run(dev, S, "fp8", "split")                 # fresh buffers, eager
+    assert np.array_equal(ref_out.cpu().numpy(), ref["codes"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        scale.fill_(123.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(scale, ref_scale)
