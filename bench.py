@@ -64,6 +64,9 @@ WORKLOADS = {   # name -> (s_q, n_pool, pool dtype / output dtype, fixed num_spl
     "fp8_16": (16, 131072, "fp8", 8),
 }
 LLC_BYTES = 256 << 20
+LABELS = {"single": "single-token decode", "small6": "small decode batch", "small16": "small decode batch",
+          "large96": "large decode batch", "large384": "large decode batch", "fp8_1": "FP8 path",
+          "fp8_16": "FP8 path"}
 
 
 def log(msg):
@@ -89,6 +92,9 @@ def parse_args():
                     help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output directories of this bench "
                          "(--no-sweep) and of --copy-only: print the calibrated HBM bytes per launch of the "
                          "attention kernel, write them to the traffic record, and exit")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="rocprofv3 --pmc output directories of this bench: print each kernel's counters per "
+                         "dispatch (sum and max over the counter's instances) and the MFMA figures, and exit")
     return ap.parse_args()
 
 
@@ -391,6 +397,34 @@ def hbm_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     print(json.dumps(rec))
 
 
+def pmc_summary(dirs):
+    """Per kernel and counter: the mean over dispatches of the counter summed (and maxed)
+    over its hardware instances.  For the attention kernel also: the MFMA busy share
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) and the executed bf16 MFMA flops
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
+    per = {}                       # (kernel, counter) -> {dispatch: [values]}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            per.setdefault(key, {}).setdefault((d, r["Dispatch_Id"]), []).append(float(r["Counter_Value"]))
+    print(f"{'kernel':56s} {'counter':32s} {'dispatches':>10s} {'sum/dispatch':>16s} {'max/dispatch':>16s}")
+    stats = {}
+    for (k, c), disp in sorted(per.items()):
+        sums = [sum(v) for v in disp.values()]
+        maxs = [max(v) for v in disp.values()]
+        stats[(k, c)] = (np.mean(sums), np.mean(maxs))
+        print(f"{k[:56]:56s} {c:32s} {len(disp):10d} {np.mean(sums):16.1f} {np.mean(maxs):16.1f}")
+    for k in sorted({k for k, _ in stats if "decode_kernel" in k}):
+        busy = stats.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"))
+        active = stats.get((k, "GRBM_GUI_ACTIVE"))
+        mops = stats.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+        if busy and active:
+            print(f"{k[:56]}: MFMA busy {busy[0]:.0f} SIMD-cycles over {active[1]:.0f} active cycles x 1024 SIMDs "
+                  f"= {100.0 * busy[0] / (active[1] * 1024):.1f}%")
+        if mops:
+            print(f"{k[:56]}: executed bf16 MFMA flops per dispatch {mops[0] * 512:.4g}")
+
+
 def _single_splits():
     from sparse_mla_decode_top_amd import binding
     return binding.smla_choose_num_splits(WORKLOADS["single"][0], 64, 640, 256)
@@ -415,6 +449,9 @@ def main():
     if args.hbm_counters:
         hbm_counters(*args.hbm_counters)
         return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
               file=sys.stderr, flush=True)
@@ -435,11 +472,12 @@ def main():
     s_q, S = head["s_q"], head["S"]
     log(f"{args.workload}: {head['us']:.2f} us/step (events {head['ev_us']:.2f}), attention kernel "
         f"{head['main_us']:.2f} us, combine {head['comb_us']:.2f} us, cold step {head['cold_us']:.2f} us, S={S}")
-    main_bytes = MAIN_BYTES_PER_TOKEN * s_q
+    pool_dtype = WORKLOADS[args.workload][2]
+    main_bytes = (MAIN_BYTES_PER_TOKEN if pool_dtype == "bf16" else MAIN_BYTES_PER_TOKEN_FP8) * s_q
     achieved = main_bytes / (head["main_us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(S),
-                "kernel": "decode_kernel<bf16 pool, partial>" if S > 1 else "decode_kernel<bf16 pool, direct>",
+                "kernel": f"decode_kernel<{pool_dtype} pool, {'partial' if S > 1 else 'direct'}>",
                 "bytes_per_launch": main_bytes, "mean_launch_us": round(head["main_us"], 3),
                 "mfma_frac": round(FLOPS_PER_TOKEN * s_q / (head["main_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5)}
     cpu = None
@@ -474,8 +512,8 @@ def main():
         "steps": head["steps"], "warmup": head["warmup"], "ms_per_step": round(head["ev_us"] / 1e3, 6),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 pools, uniform unique top-k indices)",
-        "config": {"workload": f"single-token decode: s_q={s_q}, h_q=64, d_qk=576, d_v=512, topk=640, "
-                               f"pool {head['n_pool']} bf16 rows x {head['layers']} layers, sink on, "
+        "config": {"workload": f"{LABELS[args.workload]}: s_q={s_q}, h_q=64, d_qk=576, d_v=512, topk=640, "
+                               f"pool {head['n_pool']} {pool_dtype} rows x {head['layers']} layers, sink on, "
                                f"num_splits={S}",
                    "global_batch": s_q, "num_splits": S,
                    "timing": "HIP graph replay over the layers (warm: the rows all layers gather stay in the "
