@@ -176,6 +176,26 @@ __device__ __forceinline__ int load_idx_and_q(const int32_t* idx_ptr, const void
       : "memory");
   return idx;
 }
+// The same for one group of 8 Q rows (the 8-wave kernel: 9 DMAs per wave).
+__device__ __forceinline__ int load_idx_and_q1(const int32_t* idx_ptr, const void* q0, uint32_t lds0_uniform) {
+  int idx;
+  uint32_t saved;
+  asm volatile(
+      "global_load_dword %0, %2, off nt\n\t"
+      "s_mov_b32 %1, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      SMLA_DMA_OP(3, 8064, 128) SMLA_DMA_OP(3, 8064, 256) SMLA_DMA_OP(3, 8064, 384) SMLA_DMA_OP(3, 8064, 512)
+      SMLA_DMA_OP(3, 8064, 640) SMLA_DMA_OP(3, 8064, 768) SMLA_DMA_OP(3, 8064, 896) SMLA_DMA_OP(3, 8064, 1024)
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_waitcnt vmcnt(9)"
+      : "=&v"(idx), "=&s"(saved)
+      : "v"(idx_ptr), "v"(q0), "s"(lds0_uniform)
+      : "memory");
+  return idx;
+}
 #undef SMLA_DMA
 #undef SMLA_DMA_OP
 
@@ -817,6 +837,419 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 }
 
 // ---------------------------------------------------------------------------
+// The attention kernel with 8 waves, two per SIMD (h_q = 64, CS >= 2).
+// Wave w owns heads [16 (w & 3), +16) and slots [32 (w >> 2), +32) of every
+// block.  The two waves that share a SIMD (w and w + 4) own the same heads and
+// split the slots, so while one runs its softmax, LDS reads or gather issue,
+// the SIMD's matrix core can run the other's MFMAs; the one-wave-per-SIMD
+// kernel above has to interleave those itself and keeps its MFMA pipe busy
+// only about half the time.  Each wave runs its own online softmax over its
+// slots with its own integer frame per head; the two halves of a head merge
+// their (M, l, O) through LDS at the end, as two splits would.  Two waves per
+// SIMD leave 256 registers a wave, so the accumulators of 16 heads take
+// 128 / CS of them: the kernel serves 2, 4 or 8 column parts.
+// ---------------------------------------------------------------------------
+constexpr int kWaves8 = 8;
+constexpr int kThreads8 = 64 * kWaves8;
+
+template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
+__global__ __launch_bounds__(kThreads8) void decode_kernel8(
+    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
+    int32_t s_q, int32_t topk, int32_t h_q, DecodeArgs a) {
+  static_assert(CS >= 2, "the 8-wave layout needs at least two column parts");
+  constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
+  constexpr int kCols = 512 / CS;
+  constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
+  constexpr int kStageBytes = 64 * kStagePitch;   // the 64 staged head rows of one slot half
+  static_assert(2 * kStageBytes <= 2 * kTileBytes, "staging must fit in the tile buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) float s_scale[2][kBlk];
+  __shared__ __attribute__((aligned(16))) float s_bias[2][kBlk];   // 0: valid slot, kMaskedScore: masked
+  __shared__ float s_ml[2][2][64];     // [slot half][frame M, denominator l][head]
+  __shared__ float s_lse[64];
+  __shared__ int s_restart;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hl = lane & 15;               // head within the head tile (MFMA column)
+  const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
+  const int hq = wave & 3;                // head tile: heads [16 hq, 16 hq + 16)
+  const int sg = wave >> 2;               // slot half: slots [32 sg, 32 sg + 32) of each block
+  const int head = 16 * hq + hl;
+
+  const Job job = decode_job<CS>(num_splits, n_blocks, s_q * num_splits);
+  if (!job.live) return;                          // padding of the grid (whole workgroup)
+  const int t = job.t;
+  const int32_t* idx_row = indices + (int64_t)t * topk;
+
+  float M_run = kNoFrame;             // integer frame of this lane's head over this wave's slots
+  float m_seen = kMaskedScore;        // largest score seen so far
+  float l_run = 0.f;                  // this lane's share of the denominator
+  if (tid == 0) s_restart = 0;        // ordered before its readers by the loop barriers
+  f32x4 acc[kCt];                     // O^T: column tile ct -> columns kCols * part + 16ct + 4G + i
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (job.b0 < job.b1) {
+    auto load_idx = [&](int b) -> int {
+      return __builtin_nontemporal_load(idx_row + min(b * kBlk + lane, topk - 1));
+    };
+    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
+    auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
+    const float scale_log2 = a.scale_log2;
+    bf16x8 qf[18];                    // Q fragments: head, dims 32ks + 8G .. +8
+
+    const uint32_t tile_lds0 = lds_addr(s_tile);
+    constexpr int kBufBytes = KV_FP8 ? kCodeTileBytes : kTileBytes;
+    // Gather rows: bf16, wave w fills rows [8w, 8w + 8) (lanes 8k..8k+7 one
+    // row, chunk (l & 7) ^ (row & 7) of each octet); FP8, waves 0-3 fill rows
+    // [16w, 16w + 16) (4 lanes a row, chunk l & 3 of each quartet).
+    const bool gathers = !KV_FP8 || wave < 4;
+
+    auto issue_gather = [&](int idx_lane, int buf) {
+      if (!KV_FP8) {
+        const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
+        const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
+        if (valid_of(row_idx)) {
+          const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + (((lane & 7) ^ rsw(lane >> 3)) * 16);
+          dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
+        } else {
+          uint8_t* dst = s_tile + buf * kBufBytes + wave * 1024 + lane * 16;
+#pragma unroll
+          for (int o = 0; o < 9; ++o) *(u32x4*)(dst + 8192 * o) = u32x4{0u, 0u, 0u, 0u};
+        }
+      } else if (gathers) {
+        const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
+        const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
+        if (valid_of(row_idx)) {
+          const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + (lane & 3) * 16;
+          dma_quartets(src, __builtin_amdgcn_readfirstlane(lds_base));
+        } else {
+          uint8_t* dst = s_tile + buf * kBufBytes + wave * 1024 + lane * 16;
+#pragma unroll
+          for (int q = 0; q < 9; ++q) *(u32x4*)(dst + 4096 * q) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+
+    // per-lane LDS byte offsets of the operand reads (the tile layout above)
+    const int sw_k = rsw(hl);
+    const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
+    const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
+    const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
+    const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
+    int vb[4];                                                  // column tile ct & 3
+#pragma unroll
+    for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
+
+    // ---- prologue: Q rows (heads) [8w, 8w + 8) into LDS by wave w, at kQOffset
+    int idx_cur;
+    {
+      const int r0 = 8 * wave + (lane >> 3);
+      const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
+      const uint8_t* qbase = (const uint8_t*)(q_ptr + (int64_t)t * h_q * 576);
+      idx_cur = load_idx_and_q1(idx_row + min(job.b0 * kBlk + lane, topk - 1), qbase + (int64_t)r0 * 1152 + chunk,
+                                __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + wave * 1024));
+    }
+
+    auto run_pass = [&](const bool first) __attribute__((always_inline)) -> bool {
+    bool overflow = false;
+    if (!first) idx_cur = load_idx(job.b0);
+    idx_cur = slot_in(job.b0) ? idx_cur : -1;
+    issue_gather(idx_cur, 0);
+    int idx_nxt = load_idx(job.b0 + 1);
+    bool valid_cur = valid_of(idx_cur);
+    float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
+    if (first) {
+      wait_vmem_all();        // Q rows (and block b0) have landed
+      lds_barrier();
+      const uint32_t qt = lds_addr(s_tile) + kQOffset + hq * 2048;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
+        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
+      }
+    }
+
+    for (int b = job.b0; b < job.b1; ++b) {
+      const int cur = (b - job.b0) & 1;
+      wait_vmem_all();          // this wave's share of block b has landed
+      if (wave == 0) {
+        s_bias[cur][lane] = valid_cur ? 0.f : kMaskedScore;
+        if (KV_FP8) s_scale[cur][lane] = sc_cur;
+      }
+      lds_barrier();            // ... and every wave's; block b-1 fully consumed
+
+      // Block b+1: one DMA per QK^T k-step pair (masked rows and rows past the
+      // job's last block copy the zero row).
+      bool valid_nxt = false;
+      float sc_nxt = 0.f;
+      const uint8_t* gsrc = g_zero_row;
+      uint32_t gbase = 0u;
+      if (PREFETCH) {
+        idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
+        valid_nxt = valid_of(idx_nxt);
+        if (KV_FP8 && wave == 0 && valid_nxt) sc_nxt = a.kv_scale[idx_nxt];
+        if (!KV_FP8) {
+          const int row_idx = __shfl(idx_nxt, 8 * wave + (lane >> 3));
+          gsrc = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+                 (((lane & 7) ^ rsw(lane >> 3)) * 16);
+          gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + wave * 1024);
+        } else {
+          const int row_idx = __shfl(idx_nxt, 16 * (wave & 3) + (lane >> 2));
+          gsrc = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
+          gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + (wave & 3) * 1024);
+        }
+      }
+      auto gather_dma = [&](const int d) __attribute__((always_inline)) {
+        if (!PREFETCH || !gathers) return;
+        constexpr int L = KV_FP8 ? 4096 : 8192, Gs = KV_FP8 ? 64 : 128;
+        switch (d) {
+          case 0: dma_one<L, Gs, 0>(gsrc, gbase); break;
+          case 1: dma_one<L, Gs, 1>(gsrc, gbase); break;
+          case 2: dma_one<L, Gs, 2>(gsrc, gbase); break;
+          case 3: dma_one<L, Gs, 3>(gsrc, gbase); break;
+          case 4: dma_one<L, Gs, 4>(gsrc, gbase); break;
+          case 5: dma_one<L, Gs, 5>(gsrc, gbase); break;
+          case 6: dma_one<L, Gs, 6>(gsrc, gbase); break;
+          case 7: dma_one<L, Gs, 7>(gsrc, gbase); break;
+          default: dma_one<L, Gs, 8>(gsrc, gbase); break;
+        }
+      };
+      const int idx_after = load_idx(b + 2);
+
+      const uint8_t* tile;
+      if (!KV_FP8) {
+        tile = s_tile + cur * kTileBytes;
+      } else {
+        // Expand block b's e4m3 codes into the bf16 tile (exact conversion).
+        uint8_t* btile = s_tile + 2 * kCodeTileBytes;
+        const uint8_t* ctile = s_tile + cur * kCodeTileBytes;
+#pragma unroll 3
+        for (int j = 0; j < 9; ++j) {
+          const int p = j * kThreads8 + tid;
+          const int o = p >> 9, r = (p >> 3) & 63;
+          const int c = 8 * o + ((p & 7) ^ rsw(r));
+          const int cc = c >> 1;
+          const u32x2 codes =
+              *(const u32x2*)(ctile + ((cc >> 2) * 256 + r * 4 + (cc & 3)) * 16 + (c & 1) * 8);
+          u32x4 ov;
+          ov[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
+          ov[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
+          ov[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
+          ov[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
+          *(u32x4*)(btile + p * 16) = ov;
+        }
+        lds_barrier();
+        tile = btile;
+      }
+
+      const uint32_t tl = lds_addr(tile);
+      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
+                                 opaque(tl + kb1 + 65536)};
+      auto kfrag = [&](int ks, int st) -> bf16x8 {
+        const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
+        return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
+      };
+      const uint32_t tlv = tl + job.part * (kCt / 4) * 8192;
+      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
+      auto vfrag = [&](int ct, int kk) -> bf16x8 {
+        const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
+        const i16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)(vp + 2048));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, v1);
+        return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+      };
+
+      // ---- S^T = K . Q^T over this wave's 2 slot tiles (2 sg, 2 sg + 1);
+      // MFMAs on one accumulator in k-step pairs (the faster issue order).
+      constexpr int kAheadK = 2, kRing = kAheadK + 2, kAheadV = 2;
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      {
+        bf16x8 kf[kRing][2];
+#pragma unroll
+        for (int a0 = 0; a0 < kAheadK; ++a0)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) kf[a0][u] = kfrag(a0, 2 * sg + u);
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int ka = 2 * j + e + kAheadK;
+            if (ka < 18) {
+#pragma unroll
+              for (int u = 0; u < 2; ++u) kf[ka % kRing][u] = kfrag(ka, 2 * sg + u);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int ks = 2 * j + e;
+              sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % kRing][u], qf[ks], sacc[u], 0, 0, 0);
+            }
+          gather_dma(j);                // the next block's DMAs 0..8, one per k-step pair
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- softmax of this wave's 32 slots (lane: slots 32 sg + 16u + 4G + i)
+      float tv[8];
+      f32x4 rsc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4 bias = *(const f32x4*)&s_bias[cur][32 * sg + 16 * u + 4 * G];
+        if (KV_FP8) rsc[u] = *(const f32x4*)&s_scale[cur][32 * sg + 16 * u + 4 * G];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          tv[4 * u + i] = KV_FP8 ? fmaf(sacc[u][i] * scale_log2, rsc[u][i], bias[i]) : fmaf(sacc[u][i], scale_log2, bias[i]);
+      }
+      float m = fmaxf(fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3])), fmaxf(fmaxf(tv[4], tv[5]), fmaxf(tv[6], tv[7])));
+      m = rows_max(m);
+      m_seen = fmaxf(m_seen, m);
+      if (M_run == kNoFrame && m > kMaskedScore) M_run = floorf(m);
+      overflow |= m > M_run + kFrameSlack;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float tt = tv[e];
+        const float fl = floorf(tt);
+        const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
+        float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+        l_run += p;
+        if (KV_FP8) p *= rsc[e >> 2][e & 3];
+        pv[e] = p;
+      }
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t h2 = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+        ph[j] = h2;
+        pl[j] = pack_bf16x2(pv[2 * j] - __uint_as_float(h2 << 16), pv[2 * j + 1] - __uint_as_float(h2 & 0xFFFF0000u));
+      }
+
+      // ---- O^T += V^T . P^T over this wave's slots (k-step sg of the block)
+      {
+        const bf16x8 pfh = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+        const bf16x8 pfl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+        bf16x8 vf[kAheadV + 1];
+#pragma unroll
+        for (int a0 = 0; a0 < kAheadV && a0 < kCt; ++a0) vf[a0] = vfrag(a0, sg);
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) {
+          if (ct + kAheadV < kCt) vf[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, sg);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfh, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfl, acc[ct], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      valid_cur = valid_nxt;
+      sc_cur = sc_nxt;
+      idx_nxt = idx_after;
+    }
+    wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
+    return overflow;
+    };
+
+    const bool overflow = run_pass(true);
+    if (__any(overflow) && lane == 0) s_restart = 1;
+    lds_barrier();              // also: every wave is past its last tile read
+    if (s_restart != 0) {
+      // a slot half without a valid slot keeps no frame (its weights stay 0)
+      M_run = m_seen > kMaskedScore ? floorf(m_seen) : kNoFrame;
+      l_run = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      run_pass(false);
+    }
+  }
+
+  // ---- epilogue: merge the two slot halves of every head ---------------------
+  // Each half has (frame M_h, denominator l_h, accumulator acc_h) relative to
+  // its own frame; with M = the larger frame of the halves that saw weight,
+  // f_h = 2^(M_h - M) (an exact power of two), l = l_0 f_0 + l_1 f_1 and
+  // O = (acc_0 f_0 + acc_1 f_1) / l.  Both waves of a head compute the same l
+  // and M from the exchanged values.
+  const float l_w = rows_sum(l_run);
+  if (G == 0) {
+    s_ml[sg][0][head] = M_run;
+    s_ml[sg][1][head] = l_w;
+  }
+  lds_barrier();              // the exchange, and every wave past its last tile read
+  float fscale;
+  {
+    const float M0 = s_ml[0][0][head], L0 = s_ml[0][1][head];
+    const float M1 = s_ml[1][0][head], L1 = s_ml[1][1][head];
+    const bool v0 = L0 > 0.f, v1 = L1 > 0.f;
+    const float M = v0 ? (v1 ? fmaxf(M0, M1) : M0) : M1;
+    const float f0 = v0 ? __builtin_amdgcn_ldexpf(1.0f, (int)fmaxf(M0 - M, -256.f)) : 0.f;
+    const float f1 = v1 ? __builtin_amdgcn_ldexpf(1.0f, (int)fmaxf(M1 - M, -256.f)) : 0.f;
+    const float l = L0 * f0 + L1 * f1;
+    const bool any = l > 0.f;
+    const float lse = any ? M + __builtin_amdgcn_logf(l) : kNegInf;
+    float oscale = any ? 1.0f / l : 0.f;
+    if (DIRECT && a.sink != nullptr && any) {
+      const float z = a.sink[head] * kLog2e - lse;
+      oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
+    }
+    fscale = (sg == 0 ? f0 : f1) * oscale;
+    if (sg == 0 && G == 0) s_lse[head] = lse;
+  }
+
+  // Staging: slot half h writes its scaled rows at s_tile + h * kStageBytes
+  // (row = head); after the barrier wave w sums the two halves of heads
+  // [8w, 8w + 8) and stores them in whole-line pieces.
+  {
+    uint8_t* stg = s_tile + sg * kStageBytes + head * kStagePitch + 16 * G;
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) *(f32x4*)(stg + 64 * ct) = acc[ct] * fscale;
+  }
+  lds_barrier();
+  const uint8_t* st0 = s_tile + 8 * wave * kStagePitch;
+  const uint8_t* st1 = st0 + kStageBytes;
+  const int64_t row0 = (DIRECT ? (int64_t)t * h_q : ((int64_t)job.s * s_q + t) * h_q) + 8 * wave;
+  const int col0 = job.part * kCols;
+  if (!DIRECT || a.out_dtype == kOutF32) {       // 1 KB of whole row pieces per instruction
+    float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + col0;
+#pragma unroll
+    for (int j = 0; j < 8 * kCols / 256; ++j) {
+      const int f = 256 * j + 4 * lane;
+      const int r = f / kCols, c = f % kCols;
+      *(f32x4*)(dst + r * 512 + c) =
+          *(const f32x4*)(st0 + r * kStagePitch + 4 * c) + *(const f32x4*)(st1 + r * kStagePitch + 4 * c);
+    }
+  } else {                                       // bf16 (a direct FP8 output never takes this kernel)
+    constexpr int kLanesPerRow = kCols / 8, kRowsPer = 64 / kLanesPerRow;
+    const int rr = lane / kLanesPerRow, cc = 8 * (lane % kLanesPerRow);
+    uint16_t* dst = (uint16_t*)a.out + row0 * 512 + col0 + cc;
+#pragma unroll
+    for (int j = 0; j < 8 / kRowsPer; ++j) {
+      const int r = kRowsPer * j + rr;
+      const f32x4 v0 = *(const f32x4*)(st0 + r * kStagePitch + 4 * cc) + *(const f32x4*)(st1 + r * kStagePitch + 4 * cc);
+      const f32x4 v1 =
+          *(const f32x4*)(st0 + r * kStagePitch + 4 * cc + 16) + *(const f32x4*)(st1 + r * kStagePitch + 4 * cc + 16);
+      *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                       pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+    }
+  }
+  if (lane < 8 && job.part == 0) {               // every column part holds the same LSE
+    const float lse = s_lse[8 * wave + lane];
+    if (!DIRECT)
+      a.lse_accum[row0 + lane] = lse;
+    else if (a.lse_out != nullptr)
+      a.lse_out[row0 + lane] = lse;
+  }
+  // Split jobs of a decode with an FP8 output: seed the combine's running amax.
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
+}
+
+// ---------------------------------------------------------------------------
 // Combine: O = sum_s 2^(LSE_s - M) O_s / sum_s 2^(LSE_s - M), then the sink and
 // the cast.  One wave merges one (token, head) row: lane l owns columns
 // [4l, 4l+4) and [256+4l, 256+4l+4); lane s also loads split s's LSE.  The
@@ -1002,26 +1435,33 @@ namespace {
 template <bool DIRECT, bool PREFETCH>
 hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
   const unsigned n_jobs = (unsigned)(a.s_q * (DIRECT ? 1 : a.num_splits));
-  const dim3 block(kThreads);
   const int cs = a.col_parts;
   const dim3 grid(cs == 1 ? n_jobs : (n_jobs + 7) / 8 * 8 * cs);
-#define SMLA_LAUNCH(KERNEL, CSV)                                                                            \
-  do {                                                                                                      \
-    if (kv_fp8)                                                                                             \
-      hipLaunchKernelGGL((KERNEL<true, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a.indices, a.q,      \
-                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                                \
-    else                                                                                                    \
-      hipLaunchKernelGGL((KERNEL<false, DIRECT, CSV, PREFETCH>), grid, block, 0, stream, a.indices, a.q,     \
-                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                                \
+#define SMLA_LAUNCH(KERNEL, THREADS, CSV)                                                                 \
+  do {                                                                                                    \
+    if (kv_fp8)                                                                                           \
+      hipLaunchKernelGGL((KERNEL<true, DIRECT, CSV, PREFETCH>), grid, dim3(THREADS), 0, stream, a.indices, \
+                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                         \
+    else                                                                                                  \
+      hipLaunchKernelGGL((KERNEL<false, DIRECT, CSV, PREFETCH>), grid, dim3(THREADS), 0, stream, a.indices,\
+                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                         \
   } while (0)
-  if (cs == 8)
-    SMLA_LAUNCH(decode_kernel, 8);
+  // 64 heads in 2, 4 or 8 column parts: the 8-wave kernel (two waves per SIMD).
+  const bool eight = a.h_q == 64 && cs >= 2;
+  if (eight && cs == 8)
+    SMLA_LAUNCH(decode_kernel8, kThreads8, 8);
+  else if (eight && cs == 4)
+    SMLA_LAUNCH(decode_kernel8, kThreads8, 4);
+  else if (eight)
+    SMLA_LAUNCH(decode_kernel8, kThreads8, 2);
+  else if (cs == 8)
+    SMLA_LAUNCH(decode_kernel, kThreads, 8);
   else if (cs == 4)
-    SMLA_LAUNCH(decode_kernel, 4);
+    SMLA_LAUNCH(decode_kernel, kThreads, 4);
   else if (cs == 2)
-    SMLA_LAUNCH(decode_kernel, 2);
+    SMLA_LAUNCH(decode_kernel, kThreads, 2);
   else
-    SMLA_LAUNCH(decode_kernel, 1);
+    SMLA_LAUNCH(decode_kernel, kThreads, 1);
 #undef SMLA_LAUNCH
   return hipGetLastError();
 }
