@@ -385,7 +385,7 @@ def hbm_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
         b = (fetch.get(k, 0.0) * rf + write.get(k, 0.0) * wf) * 1024
         print(f"{k[:64]:64s} {fetch.get(k, 0.0):10.1f} {write.get(k, 0.0):10.1f} {b:12.0f}")
     kf, kw = pick(fetch, "decode_kernel"), pick(write, "decode_kernel")
-    rec = {"kernel": "decode_kernel<bf16 pool, partial>", "workload": "single",
+    rec = {"kernel": kernel_label(WORKLOADS["single"][0], _single_splits(), "bf16"), "workload": "single",
            "num_splits": _single_splits(),
            "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kw, 1),
            "read_factor": round(rf, 4), "write_factor": round(wf, 4),
@@ -423,6 +423,15 @@ def pmc_summary(dirs):
                   f"= {100.0 * busy[0] / (active[1] * 1024):.1f}%")
         if mops:
             print(f"{k[:56]}: executed bf16 MFMA flops per dispatch {mops[0] * 512:.4g}")
+
+
+def kernel_label(s_q, S, pool, cus=256):
+    """Which attention kernel a launch runs (mirrors sparse_mla_decode's choice for 64
+    heads): the 8-wave kernel when the jobs take 2, 4 or 8 column parts."""
+    jobs = s_q * S
+    cs = 8 if 8 * jobs <= cus else 4 if 4 * jobs <= cus else 2 if 2 * jobs <= cus else 1
+    name = "decode_kernel8" if cs >= 2 else "decode_kernel"
+    return f"{name}<{pool} pool, {'partial' if S > 1 else 'direct'}, {cs} column part{'s' if cs > 1 else ''}>"
 
 
 def _single_splits():
@@ -477,7 +486,7 @@ def main():
     achieved = main_bytes / (head["main_us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(S),
-                "kernel": f"decode_kernel<{pool_dtype} pool, {'partial' if S > 1 else 'direct'}>",
+                "kernel": kernel_label(s_q, S, pool_dtype),
                 "bytes_per_launch": main_bytes, "mean_launch_us": round(head["main_us"], 3),
                 "mfma_frac": round(FLOPS_PER_TOKEN * s_q / (head["main_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5)}
     cpu = None

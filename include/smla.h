@@ -128,12 +128,12 @@ smla_status combine_splits(const smla_params* p, int32_t num_splits, const float
  * smla_choose_num_splits -- a split count for the shape that gives small decode
  * batches enough (token, split) jobs to fill `num_cus` compute units and keeps
  * large batches unsplit ("The Split-K Dispatch", "The Reasoning Behind the
- * Design": the split count adapts to the batch): S = num_cus / (4 s_q) when
- * that is at least 4, else num_cus / (2 s_q) when that is at least 2, else 1,
- * capped at the block count (and SMLA_MAX_SPLITS).  Split jobs then run with
- * 4 or 2 workgroups each (one per part of the output columns).  Deterministic
- * in its arguments, so a captured graph stays valid.  Returns >= 1, or 0 when
- * an argument is non-positive.
+ * Design": the split count adapts to the batch).  With x = num_cus / s_q
+ * compute units per token: S = x / 8 when x >= 40, 4 when x >= 8, 2 when
+ * x >= 4, else 1, capped at the block count (and SMLA_MAX_SPLITS).  Split jobs
+ * then run as 2, 4 or 8 workgroups each (one per part of the output columns).
+ * Deterministic in its arguments, so a captured graph stays valid.  Returns
+ * >= 1, or 0 when an argument is non-positive.
  */
 int32_t smla_choose_num_splits(int32_t s_q, int32_t h_q, int32_t topk, int32_t num_cus);
 

@@ -66,18 +66,16 @@ size_t smla_partial_bytes(int32_t s_q, int32_t h_q, int32_t num_splits) {
 int32_t smla_choose_num_splits(int32_t s_q, int32_t h_q, int32_t topk, int32_t num_cus) {
   if (s_q < 1 || h_q < 1 || topk < 1 || num_cus < 1) return 0;
   const int32_t n_blk = n_blocks_of(topk);
-  // Workgroups per job: jobs split their output columns over 4 or 2
-  // workgroups when that keeps every workgroup in one round over the compute
-  // units (sparse_mla_decode makes the same choice).  Measured on a 256-CU
-  // MI355X: with 4 column parts, more splits win as long as each keeps 4 or
-  // more; past that, 2 column parts with at least 2 splits; large batches
-  // (more than a quarter of the CUs in tokens) run unsplit.
+  // By compute units per token x = num_cus / s_q: S = x / 8 when x >= 40, 4
+  // when x >= 8, 2 when x >= 4, else 1 (capped at the block count).  Split
+  // jobs then run as 2, 4 or 8 column-part workgroups (sparse_mla_decode picks
+  // the most that fit one round over the CUs).  This was the best measured S,
+  // or within 2% of it, at every batch size of a sweep on a 256-CU MI355X
+  // (s_q = 1 ... 128): more splits shorten a small batch's critical path,
+  // but every split adds a partial to write and merge.
+  const int64_t cus = num_cus, t = s_q;
+  int32_t s = cus >= 40 * t ? (int32_t)(cus / (8 * t)) : cus >= 8 * t ? 4 : cus >= 4 * t ? 2 : 1;
   const int32_t cap = n_blk < SMLA_MAX_SPLITS ? n_blk : SMLA_MAX_SPLITS;
-  int32_t s = num_cus / (4 * s_q);
-  if (s < 4) {
-    s = num_cus / (2 * s_q);
-    if (s < 2) s = 1;
-  }
   if (s > cap) s = cap;
   return s < 1 ? 1 : s;
 }

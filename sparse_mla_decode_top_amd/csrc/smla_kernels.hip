@@ -1066,7 +1066,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
 
       // ---- S^T = K . Q^T over this wave's 2 slot tiles (2 sg, 2 sg + 1);
       // MFMAs on one accumulator in k-step pairs (the faster issue order).
-      constexpr int kAheadK = 2, kRing = kAheadK + 2, kAheadV = 2;
+      constexpr int kAheadK = 2, kRing = kAheadK + 2, kAheadV = kCt < 4 ? kCt : 4;
       f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       {
         bf16x8 kf[kRing][2];
@@ -1097,17 +1097,26 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
         }
       }
 
-      // ---- softmax of this wave's 32 slots (lane: slots 32 sg + 16u + 4G + i)
-      float tv[8];
-      f32x4 rsc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // ---- softmax of this wave's 32 slots (lane: slots 32 sg + 16u + 4G + i).
+      // The first V^T fragments of PV are requested after the bias reads and
+      // before the softmax math, so their LDS latency hides behind it (LDS
+      // returns in order: the softmax waits only for the bias).
+      f32x4 bias[2], rsc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const f32x4 bias = *(const f32x4*)&s_bias[cur][32 * sg + 16 * u + 4 * G];
+        bias[u] = *(const f32x4*)&s_bias[cur][32 * sg + 16 * u + 4 * G];
         if (KV_FP8) rsc[u] = *(const f32x4*)&s_scale[cur][32 * sg + 16 * u + 4 * G];
+      }
+      bf16x8 vf[kAheadV + 1];
+#pragma unroll
+      for (int a0 = 0; a0 < kAheadV; ++a0) vf[a0] = vfrag(a0, sg);
+      float tv[8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          tv[4 * u + i] = KV_FP8 ? fmaf(sacc[u][i] * scale_log2, rsc[u][i], bias[i]) : fmaf(sacc[u][i], scale_log2, bias[i]);
-      }
+          tv[4 * u + i] = KV_FP8 ? fmaf(sacc[u][i] * scale_log2, rsc[u][i], bias[u][i])
+                                 : fmaf(sacc[u][i], scale_log2, bias[u][i]);
       float m = fmaxf(fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3])), fmaxf(fmaxf(tv[4], tv[5]), fmaxf(tv[6], tv[7])));
       m = rows_max(m);
       m_seen = fmaxf(m_seen, m);
@@ -1136,9 +1145,6 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
       {
         const bf16x8 pfh = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
         const bf16x8 pfl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
-        bf16x8 vf[kAheadV + 1];
-#pragma unroll
-        for (int a0 = 0; a0 < kAheadV && a0 < kCt; ++a0) vf[a0] = vfrag(a0, sg);
 #pragma unroll
         for (int ct = 0; ct < kCt; ++ct) {
           if (ct + kAheadV < kCt) vf[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, sg);

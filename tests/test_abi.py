@@ -60,9 +60,11 @@ def test_choose_num_splits_properties():
                 assert 2 * s_q * s <= 256      # split jobs keep two column parts in one round
             if s_q > 64:
                 assert s == 1
-    for s_q, expect in ((1, 10), (4, 10), (8, 8), (16, 4), (32, 4), (48, 2), (96, 1), (384, 1)):
+    for s_q, expect in ((1, 10), (4, 8), (6, 5), (8, 4), (16, 4), (32, 4), (48, 2), (64, 2), (96, 1), (384, 1)):
         assert smla.smla_choose_num_splits(s_q, 64, 640, 256) == expect, s_q
-    assert smla.smla_choose_num_splits(16, 64, 640, 512) == 8      # scales with the CU count
+    assert smla.smla_choose_num_splits(32, 64, 640, 512) == 4      # scales with the CU count
+    assert smla.smla_choose_num_splits(8, 64, 640, 512) == 8
+    assert smla.smla_choose_num_splits(1, 64, 64, 256) == 1        # capped at the block count
     assert smla.smla_choose_num_splits(0, 64, 640, 256) == 0
     # deterministic
     assert smla.smla_choose_num_splits(16, 64, 640, 256) == smla.smla_choose_num_splits(16, 64, 640, 256)
