@@ -39,6 +39,12 @@
 //     hi + lo carries p to about 2^-17 relative.
 //   * Outputs are staged through LDS and stored in whole-line pieces.
 //
+// decode_kernel8: the same job with 8 waves, two per SIMD, for 64 heads in 2,
+// 4 or 8 column parts.  The two waves on a SIMD own the same 16 heads and
+// split each block's slots, so the hardware overlaps one's softmax and LDS
+// reads with the other's MFMAs; the two slot halves of a head merge in the
+// epilogue as two splits would.
+//
 // combine kernel: split-major partials -> final output (+ sink, cast).
 
 #include <hip/hip_runtime.h>
