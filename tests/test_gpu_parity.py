@@ -159,6 +159,31 @@ def test_score_far_beyond_the_frame_restarts_the_job():
         assert float(lerr.max()) <= H.TOL_LSE, f"S={S} {path}: relative LSE error {float(lerr.max()):.3g}"
 
 
+def test_restart_with_one_slot_half_fully_masked():
+    """The 8-wave kernel splits each block's slots between two waves, each with its own
+    frame.  Token 0 masks slots 0-31 of every block and token 1 slots 32-63, so one wave
+    of each pair never sees a valid slot, while a score far beyond the frame in the other
+    half forces a restart: the empty half must stay frameless (weight 0) through it."""
+    inp = W.make_inputs(2, 64, 8192, 640, seed=23, sink=True)
+    q = inp.q
+    slots = np.arange(640)
+    inp.indices[0, (slots % 64) < 32] = -1
+    inp.indices[1, (slots % 64) >= 32] = -1
+    for t, head, slot in ((0, 5, 5 * 64 + 40), (1, 50, 7 * 64 + 10)):
+        row = int(inp.indices[t, slot])
+        assert row >= 0
+        inp.kv_bits[row] = W.f32_to_bf16_bits(20.0 * q[t, head])
+    dev = H.DeviceInputs(inp)
+    O_ref, L_ref = oracle.attend(q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    assert L_ref[0, 5] > 600 and L_ref[1, 50] > 600
+    for S, path in ((1, "direct"), (2, "split"), (10, "split")):
+        res = H.run(dev, S, "f32", path)
+        H.assert_o_close(res["O"], O_fin)
+        lerr = np.abs(res["lse"] - L_ref) / np.maximum(1.0, np.abs(L_ref))
+        assert float(lerr.max()) <= H.TOL_LSE, f"S={S} {path}: relative LSE error {float(lerr.max()):.3g}"
+
+
 def test_ragged_topk_and_row_stride():
     """topk not a multiple of 64, and pool rows embedded in a wider buffer (row stride 640)."""
     inp = W.make_inputs(5, 64, 3000, 333, seed=12, sink=True, pad="random")
