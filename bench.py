@@ -446,6 +446,60 @@ def _single_splits():
     return binding.smla_choose_num_splits(WORKLOADS["single"][0], 64, 640, 256)
 
 
+def measured_peaks(torch):
+    """Peak denominators measured on this GPU, reported beside the published ones:
+    HBM read (1 GiB streamed in 16-byte loads), HBM copy (1 GiB read + 1 GiB
+    written), and the bf16 matrix-core rate of an MFMA issue loop (both probes in
+    libsmla_peak.so)."""
+    import ctypes
+    n = 1 << 28                                     # 1 GiB of float32
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    peak = ctypes.CDLL(os.path.join(ROOT, "sparse_mla_decode_top_amd", "libsmla_peak.so"))
+    peak.smla_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    peak.smla_peak_mfma_bf16.restype = ctypes.c_int
+    peak.smla_peak_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    peak.smla_peak_mfma_flops.restype = ctypes.c_double
+    peak.smla_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    peak.smla_peak_hbm_read.restype = ctypes.c_int
+    stream = torch.cuda.current_stream().cuda_stream
+    rblocks = 4096
+    words = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+
+    def read():
+        if peak.smla_peak_hbm_read(a.data_ptr(), n * 4, rblocks, words.data_ptr(), stream) != 0:
+            raise RuntimeError("smla_peak_hbm_read failed")
+
+    t_read = timed(read, 10)
+    t_copy = timed(lambda: b.copy_(a), 10)
+    del a, b, words
+    torch.cuda.empty_cache()
+    blocks, iters = 1024, 2000
+    out = torch.empty(blocks * 256, device="cuda")
+
+    def mfma():
+        if peak.smla_peak_mfma_bf16(blocks, iters, out.data_ptr(), stream) != 0:
+            raise RuntimeError("smla_peak_mfma_bf16 failed")
+
+    t_mfma = timed(mfma, 3)
+    return {"hbm_read_gbs": round(n * 4 / t_read / 1e9, 1), "hbm_copy_gbs": round(2 * n * 4 / t_copy / 1e9, 1),
+            "mfma_bf16_tflops": round(peak.smla_peak_mfma_flops(blocks, iters) / t_mfma / 1e12, 1),
+            "published": {"hbm_gbs": HBM_PEAK_GBS, "mfma_bf16_tflops": BF16_PEAK_TFLOPS}}
+
+
 def copy_only(torch):
     n = 256 << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -496,6 +550,8 @@ def main():
                 "kernel": kernel_label(s_q, S, pool_dtype),
                 "bytes_per_launch": main_bytes, "mean_launch_us": round(head["main_us"], 3),
                 "mfma_frac": round(FLOPS_PER_TOKEN * s_q / (head["main_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5)}
+    peaks = measured_peaks(torch)
+    log(f"measured peaks: {peaks}")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host cores")
@@ -540,6 +596,7 @@ def main():
         "attention_kernel_us": round(head["main_us"], 3),
         "combine_kernel_us": round(head["comb_us"], 3),
         "roofline": roofline,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "sweep": sweep,
         "context": {"b200_fused_kernel_us_s_q1": {"unsplit": 26.6, "split8": 14.4, "split16": 14.3}},

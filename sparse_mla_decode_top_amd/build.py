@@ -12,6 +12,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsmla.so")
 SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "smla_api.cpp")]
+# the peak probe (bench.py's measured matrix-core rate), a library of its own
+PEAK_LIB = os.path.join(HERE, "libsmla_peak.so")
+PEAK_SOURCES = [os.path.join(CSRC, "smla_peak.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -28,10 +31,9 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose=False):
-    """Compile every source into libsmla.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-x", "hip"] + SOURCES + ["-o", tmp]
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-x", "hip"] + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,7 +43,13 @@ def build(verbose=False):
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile libsmla.so (the decode) and libsmla_peak.so (the peak probe); always recompiles."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PEAK_SOURCES, PEAK_LIB, verbose)
     return LIB
 
 

@@ -159,3 +159,22 @@ def test_decode_rejects_before_launch():
     assert st == MISSING_WS
     st = lib.sparse_mla_decode(ctypes.byref(_p(h_q=8)), A, A, None, A, 1, None, None, None, A, None, None, None)
     assert st == UNSUPPORTED
+
+
+def test_peak_probe_exports_its_header():
+    """libsmla_peak.so (bench.py's matrix-core probe) exports what include/smla_peak.h declares."""
+    text = open(os.path.join(ROOT, "include", "smla_peak.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text))
+    assert names == {"smla_peak_mfma_bf16", "smla_peak_mfma_flops", "smla_peak_hbm_read"}
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_mla_decode_top_amd", "libsmla_peak.so"))
+    lib.smla_peak_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.smla_peak_mfma_flops.restype = ctypes.c_double
+    assert lib.smla_peak_mfma_flops(2, 3) == 2 * 4 * 3 * 16 * (16 * 16 * 32 * 2)
+    lib.smla_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.smla_peak_mfma_bf16(0, 1, A, None) == 1          # rejected before any launch
+    assert lib.smla_peak_mfma_bf16(1, 1, None, None) == 1
+    lib.smla_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    assert lib.smla_peak_hbm_read(A + 8, 1 << 20, 4, A, None) == 1     # misaligned
+    assert lib.smla_peak_hbm_read(A, 8, 4, A, None) == 1               # shorter than one load
