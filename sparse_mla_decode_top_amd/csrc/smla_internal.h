@@ -37,7 +37,7 @@ struct CombineArgs {
   float* lse_out;
   int32_t s_q, h_q, num_splits;
   int32_t out_dtype;
-  int32_t heads_per_wg;       // 1, 2 or 4 (bf16 / f32 output)
+  int32_t heads_per_wg;       // -1: a quarter of a row per wave, 0: half a row, 4: four rows per workgroup
   int32_t scale_ready;        // FP8 output: out_scale already holds -0.0 (set by the attention kernel)
 };
 

@@ -60,6 +60,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef short i16x4 __attribute__((__vector_size__(8)));
 typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef float f32x2 __attribute__((__vector_size__(8)));
 typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 
@@ -1274,24 +1275,35 @@ struct Merged {
   float lse;
 };
 
-// kMergeChunk: partial rows in flight per lane (splits x 2 x 16 B).
-template <int kMergeChunk>
-__device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h) {
+// kMergeChunk: partial rows in flight per lane.  PARTS: the row is merged by
+// 1, 2 or 4 waves.  PARTS = 1: lane l owns columns 4l.. and 256 + 4l.. (lo,
+// hi); PARTS = 2: columns col0 + 4l.. (lo); PARTS = 4: columns col0 + 2l,
+// col0 + 2l + 1 (lo[0], lo[1]).  Each element sees the same operations either way.
+template <int kMergeChunk, int PARTS = 1>
+__device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h, int col0 = 0) {
+  constexpr int NV = PARTS == 1 ? 2 : 1;               // 16-byte (or 8-byte) pieces per lane and split
   const int lane = threadIdx.x & 63;
   const int S = a.num_splits;
   const int64_t row = (int64_t)t * a.h_q + h;
   const int64_t ostride = (int64_t)a.s_q * a.h_q * 512;
-  const float* op = a.o_accum + row * 512 + 4 * lane;
+  const float* op = a.o_accum + row * 512 + col0 + (PARTS == 4 ? 2 : 4) * lane;
+  auto piece = [&](const float* src) -> f32x4 {
+    if (PARTS == 4) {
+      const f32x2 x = *(const f32x2*)src;
+      return f32x4{x[0], x[1], 0.f, 0.f};
+    }
+    return *(const f32x4*)src;
+  };
   const float ls = lane < S ? a.lse_accum[lane * (int64_t)a.s_q * a.h_q + row] : kNegInf;
   // Split indices past S are clamped to S - 1 (an L1 hit on a row already
   // requested) so the loads are unconditional and the LSE wait leaves them
   // in flight; their terms are skipped below.
-  f32x4 v[kMergeChunk][2];
+  f32x4 v[kMergeChunk][NV];
 #pragma unroll
   for (int c = 0; c < kMergeChunk; ++c) {
     const float* src = op + min(c, S - 1) * ostride;
-    v[c][0] = *(const f32x4*)src;
-    v[c][1] = *(const f32x4*)(src + 256);
+    v[c][0] = piece(src);
+    if (NV == 2) v[c][NV - 1] = *(const f32x4*)(src + 256);
   }
   const float M = wave_max(ls);
   const float wl = (M == kNegInf || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls - M);
@@ -1305,23 +1317,29 @@ __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h)
 #pragma unroll
   for (int c = 0; c < kMergeChunk; ++c) {
     const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), c));
-    const f32x4 l2 = lo + w * v[c][0], h2 = hi + w * v[c][1];
+    const f32x4 l2 = lo + w * v[c][0];
     lo = c < S ? l2 : lo;
-    hi = c < S ? h2 : hi;
+    if (NV == 2) {
+      const f32x4 h2 = hi + w * v[c][NV - 1];
+      hi = c < S ? h2 : hi;
+    }
   }
   for (int s0 = kMergeChunk; s0 < S; s0 += kMergeChunk) {
 #pragma unroll
     for (int c = 0; c < kMergeChunk; ++c) {
       const float* src = op + min(s0 + c, S - 1) * ostride;
-      v[c][0] = *(const f32x4*)src;
-      v[c][1] = *(const f32x4*)(src + 256);
+      v[c][0] = piece(src);
+      if (NV == 2) v[c][NV - 1] = *(const f32x4*)(src + 256);
     }
 #pragma unroll
     for (int c = 0; c < kMergeChunk; ++c) {
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(s0 + c, 63)));
-      const f32x4 l2 = lo + w * v[c][0], h2 = hi + w * v[c][1];
+      const f32x4 l2 = lo + w * v[c][0];
       lo = s0 + c < S ? l2 : lo;
-      hi = s0 + c < S ? h2 : hi;
+      if (NV == 2) {
+        const f32x4 h2 = hi + w * v[c][NV - 1];
+        hi = s0 + c < S ? h2 : hi;
+      }
     }
   }
   float f = 1.0f / ws;
@@ -1332,11 +1350,12 @@ __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h)
   return m;
 }
 
-// bf16 / fp32 output: 4 heads per workgroup, one wave per head.
-// HPW heads (waves) per workgroup: 1 when few (token, head) rows would leave
-// compute units idle, so that each CU pulls fewer partial rows.
+// bf16 / fp32 output.  PARTS = 1: HPW whole (token, head) rows per workgroup,
+// one wave per row.  PARTS = 2 or 4 (HPW = 1): one wave merges 1 / PARTS of a
+// row (workgroup PARTS r + j: row r, columns (512 / PARTS) j ..), so that a few
+// rows spread over more waves, each with fewer loads in flight.
 // The fields the first loads need come as leading (SGPR-preloaded) arguments.
-template <int HPW, int CHUNK>
+template <int HPW, int CHUNK, int PARTS = 1>
 __global__ __launch_bounds__(64 * HPW) void combine_kernel(const float* __restrict__ o_accum,
                                                            const float* __restrict__ lse_accum, int32_t s_q,
                                                            int32_t h_q, int32_t num_splits, CombineArgs args) {
@@ -1348,20 +1367,30 @@ __global__ __launch_bounds__(64 * HPW) void combine_kernel(const float* __restri
   a.num_splits = num_splits;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bpt = (a.h_q + HPW - 1) / HPW;
-  const int t = blockIdx.x / bpt;
-  const int h = (blockIdx.x - t * bpt) * HPW + wave;
+  const int rb = (int)blockIdx.x / PARTS;
+  const int col0 = (512 / PARTS) * ((int)blockIdx.x % PARTS);
+  const int t = rb / bpt;
+  const int h = (rb - t * bpt) * HPW + wave;
   if (h >= a.h_q) return;
-  const Merged m = merge_head<CHUNK>(a, t, h);
+  const Merged m = merge_head<CHUNK, PARTS>(a, t, h, col0);
   const int64_t row = (int64_t)t * a.h_q + h;
+  constexpr int kLaneCols = PARTS == 4 ? 2 : 4;
   if (a.out_dtype == kOutF32) {
-    *(f32x4*)((float*)a.out + row * 512 + 4 * lane) = m.lo;
-    *(f32x4*)((float*)a.out + row * 512 + 256 + 4 * lane) = m.hi;
+    float* o = (float*)a.out + row * 512 + col0 + kLaneCols * lane;
+    if (PARTS == 4)
+      *(f32x2*)o = f32x2{m.lo[0], m.lo[1]};
+    else
+      *(f32x4*)o = m.lo;
+    if (PARTS == 1) *(f32x4*)(o + 256) = m.hi;
   } else {
-    uint16_t* o = (uint16_t*)a.out + row * 512 + 4 * lane;
-    *(u32x2*)o = u32x2{pack_bf16x2(m.lo[0], m.lo[1]), pack_bf16x2(m.lo[2], m.lo[3])};
-    *(u32x2*)(o + 256) = u32x2{pack_bf16x2(m.hi[0], m.hi[1]), pack_bf16x2(m.hi[2], m.hi[3])};
+    uint16_t* o = (uint16_t*)a.out + row * 512 + col0 + kLaneCols * lane;
+    if (PARTS == 4)
+      *(uint32_t*)o = pack_bf16x2(m.lo[0], m.lo[1]);
+    else
+      *(u32x2*)o = u32x2{pack_bf16x2(m.lo[0], m.lo[1]), pack_bf16x2(m.lo[2], m.lo[3])};
+    if (PARTS == 1) *(u32x2*)(o + 256) = u32x2{pack_bf16x2(m.hi[0], m.hi[1]), pack_bf16x2(m.hi[2], m.hi[3])};
   }
-  if (a.lse_out != nullptr && lane == 0) a.lse_out[row] = m.lse;
+  if (a.lse_out != nullptr && lane == 0 && col0 == 0) a.lse_out[row] = m.lse;
 }
 
 // FP8 output, in three launches that need no scratch memory.  The token's
@@ -1490,8 +1519,8 @@ hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t st
 }
 
 namespace {
-// CHUNK: partial rows requested per pass (4, 8 or 16), the smallest that holds
-// every split, so no load repeats a row needlessly.
+// CHUNK: partial rows requested per pass (4, 8, 12 or 16), the smallest that
+// holds every split, so few loads repeat a row needlessly.
 template <int CHUNK>
 hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)(a.s_q * a.h_q);
@@ -1499,21 +1528,21 @@ hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
   if (a.out_dtype == kOutFp8) {
     if (!a.scale_ready)
       hipLaunchKernelGGL(combine_fp8_init_kernel, dim3((unsigned)((a.s_q + 255) / 256)), dim3(256), 0, stream, a);
-    if (a.heads_per_wg == 1)
+    if (a.heads_per_wg <= 1)
       hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((combine_fp8_amax_kernel<16, CHUNK>), dim3((unsigned)(a.s_q * ((a.h_q + 15) / 16))),
                          dim3(1024), 0, stream, a);
-    if (a.heads_per_wg == 1)
+    if (a.heads_per_wg <= 1)
       hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK>), dim3(rows), dim3(64), 0, stream, a);
     else
       hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
-  } else if (a.heads_per_wg == 1) {
-    hipLaunchKernelGGL((combine_kernel<1, CHUNK>), dim3(rows), dim3(64), 0, stream, a.o_accum, a.lse_accum, a.s_q,
-                       a.h_q, a.num_splits, a);
-  } else if (a.heads_per_wg == 2) {
-    hipLaunchKernelGGL((combine_kernel<2, CHUNK>), dim3((unsigned)(a.s_q * ((a.h_q + 1) / 2))), dim3(128), 0, stream,
-                       a.o_accum, a.lse_accum, a.s_q, a.h_q, a.num_splits, a);
+  } else if (a.heads_per_wg == -1) {              // a quarter of a row per wave
+    hipLaunchKernelGGL((combine_kernel<1, CHUNK, 4>), dim3(4 * rows), dim3(64), 0, stream, a.o_accum,
+                       a.lse_accum, a.s_q, a.h_q, a.num_splits, a);
+  } else if (a.heads_per_wg == 0) {               // half a row per wave
+    hipLaunchKernelGGL((combine_kernel<1, CHUNK, 2>), dim3(2 * rows), dim3(64), 0, stream, a.o_accum,
+                       a.lse_accum, a.s_q, a.h_q, a.num_splits, a);
   } else {
     hipLaunchKernelGGL((combine_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a.o_accum, a.lse_accum,
                        a.s_q, a.h_q, a.num_splits, a);
@@ -1525,6 +1554,7 @@ hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.num_splits <= 4) return launch_combine_chunk<4>(a, stream);
   if (a.num_splits <= 8) return launch_combine_chunk<8>(a, stream);
+  if (a.num_splits <= 12) return launch_combine_chunk<12>(a, stream);
   return launch_combine_chunk<16>(a, stream);
 }
 
