@@ -1415,21 +1415,36 @@ __device__ __forceinline__ float abs_max4(f32x4 v) {
   return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 }
 
-// HW heads per workgroup (one per wave): the heads' amaxes meet in LDS, so a
-// token sees h_q / HW atomics rather than h_q.  HW = 4 spreads a small batch
-// over more compute units; HW = 16 keeps the atomics of a large one few.
-template <int HW, int CHUNK>
+// HW waves per workgroup, whose amaxes meet in LDS, so a token sees fewer
+// atomics.  PARTS = 1: one wave per (token, head) row, HW = 4 spreading a small
+// batch over more compute units or HW = 16 keeping the atomics of a large one
+// few.  PARTS = 2 or 4 (HW = 4): one wave per 1 / PARTS of a row (wave u of
+// the grid: row u / PARTS, part u % PARTS); a token's h_q * PARTS waves fill
+// whole workgroups, so a workgroup never spans two tokens.
+template <int HW, int CHUNK, int PARTS = 1>
 __global__ __launch_bounds__(64 * HW) void combine_fp8_amax_kernel(CombineArgs a) {
   __shared__ float s_amax[HW];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bpt = (a.h_q + HW - 1) / HW;
-  const int t = blockIdx.x / bpt;
-  const int h = (blockIdx.x - t * bpt) * HW + wave;
+  int t, h, col0 = 0;
+  bool ok;
+  if (PARTS == 1) {
+    const int bpt = (a.h_q + HW - 1) / HW;
+    t = blockIdx.x / bpt;
+    h = (blockIdx.x - t * bpt) * HW + wave;
+    ok = h < a.h_q;
+  } else {
+    const int64_t u = (int64_t)blockIdx.x * HW + wave;
+    const int64_t r = u / PARTS;
+    col0 = (512 / PARTS) * (int)(u - r * PARTS);
+    t = (int)(r / a.h_q);
+    h = (int)(r - (int64_t)t * a.h_q);
+    ok = true;
+  }
   float amax = 0.f;
-  if (h < a.h_q) {
-    const Merged m = merge_head<CHUNK>(a, t, h);
-    amax = wave_max(fmaxf(abs_max4(m.lo), abs_max4(m.hi)));
-    if (lane == 0 && a.lse_out != nullptr) a.lse_out[(int64_t)t * a.h_q + h] = m.lse;
+  if (ok) {
+    const Merged m = merge_head<CHUNK, PARTS>(a, t, h, col0);
+    amax = wave_max(PARTS == 1 ? fmaxf(abs_max4(m.lo), abs_max4(m.hi)) : abs_max4(m.lo));
+    if (lane == 0 && col0 == 0 && a.lse_out != nullptr) a.lse_out[(int64_t)t * a.h_q + h] = m.lse;
   }
   if (lane == 0) s_amax[wave] = amax;
   __syncthreads();
@@ -1442,14 +1457,18 @@ __global__ __launch_bounds__(64 * HW) void combine_fp8_amax_kernel(CombineArgs a
   }
 }
 
-template <int HPW, int CHUNK>
+// PARTS = 1: HPW whole rows per workgroup; PARTS = 2 or 4 (HPW = 1): workgroup
+// PARTS r + j encodes part j of row r.
+template <int HPW, int CHUNK, int PARTS = 1>
 __global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bpt = (a.h_q + HPW - 1) / HPW;
-  const int t = blockIdx.x / bpt;
-  const int h = (blockIdx.x - t * bpt) * HPW + wave;
+  const int rb = (int)blockIdx.x / PARTS;
+  const int col0 = (512 / PARTS) * ((int)blockIdx.x % PARTS);
+  const int t = rb / bpt;
+  const int h = (rb - t * bpt) * HPW + wave;
   if (h >= a.h_q) return;
-  const Merged m = merge_head<CHUNK>(a, t, h);
+  const Merged m = merge_head<CHUNK, PARTS>(a, t, h, col0);
   const uint32_t v = __hip_atomic_load((const uint32_t*)a.out_scale + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float qscale;
   if (v & 0x80000000u) {
@@ -1458,16 +1477,21 @@ __global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArg
   } else {
     qscale = __uint_as_float(v);
   }
-  uint8_t* orow = (uint8_t*)a.out + ((int64_t)t * a.h_q + h) * 512;
-  uint32_t wlo = 0, whi = 0;
+  uint8_t* orow = (uint8_t*)a.out + ((int64_t)t * a.h_q + h) * 512 + col0;
+  if (PARTS == 4) {                        // columns col0 + 2l, col0 + 2l + 1
+    const uint32_t w2 = e4m3_encode(m.lo[0] / qscale) | (e4m3_encode(m.lo[1] / qscale) << 8);
+    *(uint16_t*)(orow + 2 * lane) = (uint16_t)w2;
+  } else {
+    uint32_t wlo = 0, whi = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    wlo |= e4m3_encode(m.lo[e] / qscale) << (8 * e);
-    whi |= e4m3_encode(m.hi[e] / qscale) << (8 * e);
+    for (int e = 0; e < 4; ++e) {
+      wlo |= e4m3_encode(m.lo[e] / qscale) << (8 * e);
+      if (PARTS == 1) whi |= e4m3_encode(m.hi[e] / qscale) << (8 * e);
+    }
+    *(uint32_t*)(orow + 4 * lane) = wlo;
+    if (PARTS == 1) *(uint32_t*)(orow + 256 + 4 * lane) = whi;
   }
-  *(uint32_t*)(orow + 4 * lane) = wlo;
-  *(uint32_t*)(orow + 256 + 4 * lane) = whi;
-  if (h == 0 && lane == 0) a.out_scale[t] = qscale;
+  if (h == 0 && lane == 0 && col0 == 0) a.out_scale[t] = qscale;
 }
 
 }  // namespace
@@ -1528,15 +1552,17 @@ hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
   if (a.out_dtype == kOutFp8) {
     if (!a.scale_ready)
       hipLaunchKernelGGL(combine_fp8_init_kernel, dim3((unsigned)((a.s_q + 255) / 256)), dim3(256), 0, stream, a);
-    if (a.heads_per_wg <= 1)
-      hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
-    else
+    if (a.heads_per_wg == -1) {                   // a quarter of a row per wave
+      hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 4>), dim3(rows), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 4>), dim3(4 * rows), dim3(64), 0, stream, a);
+    } else if (a.heads_per_wg == 0) {             // half a row per wave
+      hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 2>), dim3(rows / 2), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 2>), dim3(2 * rows), dim3(64), 0, stream, a);
+    } else {
       hipLaunchKernelGGL((combine_fp8_amax_kernel<16, CHUNK>), dim3((unsigned)(a.s_q * ((a.h_q + 15) / 16))),
                          dim3(1024), 0, stream, a);
-    if (a.heads_per_wg <= 1)
-      hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK>), dim3(rows), dim3(64), 0, stream, a);
-    else
       hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
+    }
   } else if (a.heads_per_wg == -1) {              // a quarter of a row per wave
     hipLaunchKernelGGL((combine_kernel<1, CHUNK, 4>), dim3(4 * rows), dim3(64), 0, stream, a.o_accum,
                        a.lse_accum, a.s_q, a.h_q, a.num_splits, a);
