@@ -914,18 +914,15 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
     // [16w, 16w + 16) (4 lanes a row, chunk l & 3 of each quartet).
     const bool gathers = !KV_FP8 || wave < 4;
 
+    // bf16: every lane issues its 9 DMAs (a masked row copies the zero row), so a
+    // wave always has exactly 9 of them in flight (the first pass counts on it).
     auto issue_gather = [&](int idx_lane, int buf) {
       if (!KV_FP8) {
         const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
         const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
-        if (valid_of(row_idx)) {
-          const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + (((lane & 7) ^ rsw(lane >> 3)) * 16);
-          dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
-        } else {
-          uint8_t* dst = s_tile + buf * kBufBytes + wave * 1024 + lane * 16;
-#pragma unroll
-          for (int o = 0; o < 9; ++o) *(u32x4*)(dst + 8192 * o) = u32x4{0u, 0u, 0u, 0u};
-        }
+        const uint8_t* src = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+                             (((lane & 7) ^ rsw(lane >> 3)) * 16);
+        dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
       } else if (gathers) {
         const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
         const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
@@ -969,7 +966,15 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
     bool valid_cur = valid_of(idx_cur);
     float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
     if (first) {
-      wait_vmem_all();        // Q rows (and block b0) have landed
+      // Q rows landed: bf16 waits for them alone (issued first; behind them the 9
+      // DMAs of block b0 and, with the look-ahead, the next index load, which
+      // stay in flight while the Q fragments are read); FP8 waits for everything.
+      if (KV_FP8)
+        wait_vmem_all();
+      else if (PREFETCH)
+        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
       lds_barrier();
       const uint32_t qt = lds_addr(s_tile) + kQOffset + hq * 2048;
 #pragma unroll
