@@ -1268,6 +1268,368 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
 }
 
 // ---------------------------------------------------------------------------
+// decode_kernel8p: one 8-wave workgroup per job that owns all 512 output
+// columns (64 heads, bf16 pool), for launches with a single column part.
+// As in decode_kernel8, the two waves on a SIMD own the same 16 heads and
+// each scores one 32-slot half of every block.  Here they trade their bf16
+// weights through LDS, and each wave accumulates every slot of the block into
+// its own half of the columns (256): 64 accumulator registers a wave, which
+// keeps two waves per SIMD without a second workgroup repeating QK^T.  The
+// two halves of a head share one integer frame, agreed on in the first block
+// that has a valid slot, so their weights add into one accumulator.
+// LDS: the two tiles and the weight exchange fill the 160 KB exactly; the
+// frame, end-of-pass and denominator exchanges reuse the weight area, and
+// validity comes from a ballot of the block's indices.
+// ---------------------------------------------------------------------------
+template <bool DIRECT, bool PREFETCH>
+__global__ __launch_bounds__(kThreads8) void decode_kernel8p(
+    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
+    int32_t s_q, int32_t topk, int32_t h_q, DecodeArgs a) {
+  constexpr int kCt = 16;                         // column tiles of 16 owned by a wave
+  constexpr int kStagePitch = 512 * 4 + 16;       // LDS pitch of a staged fp32 output row
+  static_assert(64 * kStagePitch <= 2 * kTileBytes, "staging must fit in the tile buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
+  // Per wave: its block weights (bf16 hi terms at +0, lo terms at +1024, 16
+  // bytes a lane in MFMA operand order), read by the partner wave.
+  __shared__ __attribute__((aligned(16))) uint8_t s_pex[kWaves8][2048];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hl = lane & 15;               // head within the head tile (MFMA column)
+  const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
+  const int hq = wave & 3;                // head tile: heads [16 hq, 16 hq + 16)
+  const int sg = wave >> 2;               // scores: slots [32 sg, +32); output: columns [256 sg, +256)
+  const int head = 16 * hq + hl;
+  float* const pex_own = (float*)s_pex[wave];
+  const float* const pex_par = (const float*)s_pex[wave ^ 4];
+
+  const Job job = decode_job<1>(num_splits, n_blocks, s_q * num_splits);
+  if (!job.live) return;                          // padding of the grid (whole workgroup)
+  const int t = job.t;
+  const int32_t* idx_row = indices + (int64_t)t * topk;
+
+  float M_run = kNoFrame;             // integer frame of this lane's head, shared by the wave pair
+  float m_seen = kMaskedScore;        // largest score seen so far over this wave's slots
+  float l_run = 0.f;                  // this lane's share of the denominator
+  float l_par = 0.f;                  // the partner wave's denominator (after the last pass)
+  f32x4 acc[kCt];                     // O^T: column tile ct -> columns 256 sg + 16ct + 4G + i
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (job.b0 < job.b1) {
+    auto load_idx = [&](int b) -> int {
+      return __builtin_nontemporal_load(idx_row + min(b * kBlk + lane, topk - 1));
+    };
+    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
+    auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
+    const float scale_log2 = a.scale_log2;
+    bf16x8 qf[18];                    // Q fragments: head, dims 32ks + 8G .. +8
+    const uint32_t tile_lds0 = lds_addr(s_tile);
+    bool framed = false;              // workgroup-uniform: the pair frames are set
+
+    // Wave w gathers rows [8w, 8w + 8): lanes 8k..8k+7 one row, chunk
+    // (l & 7) ^ (row & 7) of each octet; a masked row copies the zero row, so a
+    // wave always has exactly 9 DMAs in flight (the first pass counts on it).
+    auto issue_gather = [&](int idx_lane, int buf) {
+      const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
+      const uint32_t lds_base = tile_lds0 + buf * kTileBytes + wave * 1024;
+      const uint8_t* src = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+                           (((lane & 7) ^ rsw(lane >> 3)) * 16);
+      dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
+    };
+
+    // per-lane LDS byte offsets of the operand reads (the tile layout above)
+    const int sw_k = rsw(hl);
+    const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
+    const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
+    const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
+    const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
+    int vb[4];                                                  // column tile ct & 3
+#pragma unroll
+    for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
+
+    // ---- prologue: Q rows (heads) [8w, 8w + 8) into LDS by wave w, at kQOffset
+    int idx_cur;
+    {
+      const int r0 = 8 * wave + (lane >> 3);
+      const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
+      const uint8_t* qbase = (const uint8_t*)(q_ptr + (int64_t)t * h_q * 576);
+      idx_cur = load_idx_and_q1(idx_row + min(job.b0 * kBlk + lane, topk - 1), qbase + (int64_t)r0 * 1152 + chunk,
+                                __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + wave * 1024));
+    }
+
+    auto run_pass = [&](const bool first) __attribute__((always_inline)) -> bool {
+    bool overflow = false;
+    if (!first) idx_cur = load_idx(job.b0);
+    idx_cur = slot_in(job.b0) ? idx_cur : -1;
+    issue_gather(idx_cur, 0);
+    int idx_nxt = load_idx(job.b0 + 1);
+    bool valid_cur = valid_of(idx_cur);
+    if (first) {
+      // Q rows landed (issued first; block b0's 9 DMAs and, with the
+      // look-ahead, the next index load stay in flight).
+      if (PREFETCH)
+        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      lds_barrier();
+      const uint32_t qt = lds_addr(s_tile) + kQOffset + hq * 2048;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
+        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
+      }
+    }
+
+    for (int b = job.b0; b < job.b1; ++b) {
+      const int cur = (b - job.b0) & 1;
+      wait_vmem_all();          // this wave's share of block b has landed
+      lds_barrier();            // ... and every wave's; block b-1 and its weights fully consumed
+      // slot s of the block is valid iff bit s is set (the same in every wave)
+      const uint32_t vhalf = (uint32_t)(__ballot(valid_cur) >> (32 * sg));
+      const bool blk_any = __ballot(valid_cur) != 0ull;
+
+      // Block b+1: one DMA per QK^T k-step pair (masked rows and rows past the
+      // job's last block copy the zero row).
+      bool valid_nxt = false;
+      const uint8_t* gsrc = g_zero_row;
+      uint32_t gbase = 0u;
+      if (PREFETCH) {
+        idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
+        valid_nxt = valid_of(idx_nxt);
+        const int row_idx = __shfl(idx_nxt, 8 * wave + (lane >> 3));
+        gsrc = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+               (((lane & 7) ^ rsw(lane >> 3)) * 16);
+        gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + wave * 1024);
+      }
+      auto gather_dma = [&](const int d) __attribute__((always_inline)) {
+        if (!PREFETCH) return;
+        switch (d) {
+          case 0: dma_one<8192, 128, 0>(gsrc, gbase); break;
+          case 1: dma_one<8192, 128, 1>(gsrc, gbase); break;
+          case 2: dma_one<8192, 128, 2>(gsrc, gbase); break;
+          case 3: dma_one<8192, 128, 3>(gsrc, gbase); break;
+          case 4: dma_one<8192, 128, 4>(gsrc, gbase); break;
+          case 5: dma_one<8192, 128, 5>(gsrc, gbase); break;
+          case 6: dma_one<8192, 128, 6>(gsrc, gbase); break;
+          case 7: dma_one<8192, 128, 7>(gsrc, gbase); break;
+          default: dma_one<8192, 128, 8>(gsrc, gbase); break;
+        }
+      };
+      const int idx_after = load_idx(b + 2);
+
+      const uint32_t tl = lds_addr(s_tile + cur * kTileBytes);
+      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
+                                 opaque(tl + kb1 + 65536)};
+      auto kfrag = [&](int ks, int st) -> bf16x8 {
+        const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
+        return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
+      };
+      const uint32_t tlv = tl + sg * 4 * 8192;     // this wave's 256 columns
+      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
+      auto vfrag = [&](int ct, int kk) -> bf16x8 {
+        const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
+        const i16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)(vp + 2048));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, v1);
+        return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+      };
+
+      // ---- S^T = K . Q^T over this wave's 2 slot tiles (2 sg, 2 sg + 1)
+      constexpr int kAheadK = 2, kRing = kAheadK + 2, kAheadV = 4;
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      {
+        bf16x8 kf[kRing][2];
+#pragma unroll
+        for (int a0 = 0; a0 < kAheadK; ++a0)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) kf[a0][u] = kfrag(a0, 2 * sg + u);
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int ka = 2 * j + e + kAheadK;
+            if (ka < 18) {
+#pragma unroll
+              for (int u = 0; u < 2; ++u) kf[ka % kRing][u] = kfrag(ka, 2 * sg + u);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int ks = 2 * j + e;
+              sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % kRing][u], qf[ks], sacc[u], 0, 0, 0);
+            }
+          gather_dma(j);                // the next block's DMAs 0..8, one per k-step pair
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- softmax of this wave's 32 slots (lane: slots 32 sg + 16u + 4G + i).
+      // The first V^T fragments of the PV over these slots are requested first.
+      bf16x8 vf[kAheadV + 1];
+#pragma unroll
+      for (int a0 = 0; a0 < kAheadV; ++a0) vf[a0] = vfrag(a0, sg);
+      const uint32_t vbits = vhalf >> (4 * G);
+      float tv[8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          tv[4 * u + i] = fmaf(sacc[u][i], scale_log2, ((vbits >> (16 * u + i)) & 1u) ? 0.f : kMaskedScore);
+      float m = fmaxf(fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3])), fmaxf(fmaxf(tv[4], tv[5]), fmaxf(tv[6], tv[7])));
+      m = rows_max(m);
+      m_seen = fmaxf(m_seen, m);
+      if (!framed && blk_any) {
+        // first block with a valid slot: the pair's frame is the floor of the
+        // larger of the two halves' maxima
+        if (G == 0) pex_own[hl] = m;
+        lds_barrier();
+        M_run = floorf(fmaxf(m, pex_par[hl]));
+        framed = true;
+        lds_barrier();          // the partner has read m before the weights overwrite it
+      }
+      overflow |= m > M_run + kFrameSlack;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float tt = tv[e];
+        const float fl = floorf(tt);
+        const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
+        const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+        l_run += p;
+        pv[e] = p;
+      }
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t h2 = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+        ph[j] = h2;
+        pl[j] = pack_bf16x2(pv[2 * j] - __uint_as_float(h2 << 16), pv[2 * j + 1] - __uint_as_float(h2 & 0xFFFF0000u));
+      }
+      const bf16x8 pfh = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+      const bf16x8 pfl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+      *(bf16x8*)(s_pex[wave] + 16 * lane) = pfh;
+      *(bf16x8*)(s_pex[wave] + 1024 + 16 * lane) = pfl;
+
+      // ---- O^T += V^T . P^T: this wave's slots (k-step sg), then the partner's
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) {
+        if (ct + kAheadV < kCt) vf[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, sg);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfh, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfl, acc[ct], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bf16x8 vg[kAheadV + 1];
+#pragma unroll
+      for (int a0 = 0; a0 < kAheadV; ++a0) vg[a0] = vfrag(a0, sg ^ 1);
+      lds_barrier();            // every wave's weights are in LDS
+      const bf16x8 qfh = *(const bf16x8*)(s_pex[wave ^ 4] + 16 * lane);
+      const bf16x8 qfl = *(const bf16x8*)(s_pex[wave ^ 4] + 1024 + 16 * lane);
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) {
+        if (ct + kAheadV < kCt) vg[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, sg ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vg[ct % (kAheadV + 1)], qfh, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vg[ct % (kAheadV + 1)], qfl, acc[ct], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      valid_cur = valid_nxt;
+      idx_nxt = idx_after;
+    }
+    wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
+    return overflow;
+    };
+
+    // End of a pass: every wave posts its largest score, its denominator and
+    // its overflow flag; returns whether any wave of the workgroup overflowed.
+    auto end_exchange = [&](const bool overflow) __attribute__((always_inline)) -> bool {
+      const float l_w = rows_sum(l_run);
+      const bool ov = __any(overflow);
+      lds_barrier();            // every wave is past its last reads of the tiles and the weights
+      if (G == 0) {
+        pex_own[hl] = m_seen;
+        pex_own[16 + hl] = l_w;
+      }
+      if (lane == 0) ((int*)pex_own)[32] = ov ? 1 : 0;
+      lds_barrier();
+      l_run = l_w;
+      l_par = pex_par[16 + hl];
+      int any_ov = 0;
+#pragma unroll
+      for (int v = 0; v < kWaves8; ++v) any_ov |= ((const int*)s_pex[v])[32];
+      return any_ov != 0;
+    };
+
+    if (end_exchange(run_pass(true))) {
+      // the frame of the pair's largest score bounds every weight by 2
+      const float ms = fmaxf(m_seen, pex_par[hl]);
+      M_run = ms > kMaskedScore ? floorf(ms) : kNoFrame;
+      framed = true;
+      l_run = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      end_exchange(run_pass(false));
+    }
+  }
+
+  // ---- epilogue: l = both halves' denominators (one frame), O = acc / l ----
+  const float l = l_run + l_par;
+  const bool any = l > 0.f;
+  const float lse = any ? M_run + __builtin_amdgcn_logf(l) : kNegInf;
+  float oscale = any ? 1.0f / l : 0.f;
+  if (DIRECT && a.sink != nullptr && any) {
+    const float z = a.sink[head] * kLog2e - lse;
+    oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
+  }
+  const int64_t rowt = DIRECT ? (int64_t)t * h_q : ((int64_t)job.s * s_q + t) * h_q;
+  if (sg == 0 && G == 0) {
+    if (!DIRECT)
+      a.lse_accum[rowt + head] = lse;
+    else if (a.lse_out != nullptr)
+      a.lse_out[rowt + head] = lse;
+  }
+
+  // Staging (row = head, the tiles are free): wave (hq, sg) writes its 16
+  // heads x 256 columns; after the barrier wave w stores heads [8w, 8w + 8)
+  // in whole rows.
+  {
+    uint8_t* stg = s_tile + head * kStagePitch + (256 * sg + 4 * G) * 4;
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) *(f32x4*)(stg + 64 * ct) = acc[ct] * oscale;
+  }
+  lds_barrier();
+  const uint8_t* st = s_tile + 8 * wave * kStagePitch;
+  const int64_t row0 = rowt + 8 * wave;
+  if (!DIRECT || a.out_dtype == kOutF32) {       // 1 KB of one row per instruction
+    float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = j >> 1, c = 256 * (j & 1) + 4 * lane;
+      *(f32x4*)(dst + r * 512 + c) = *(const f32x4*)(st + r * kStagePitch + 4 * c);
+    }
+  } else {                                       // bf16 (a direct FP8 output never takes this kernel)
+    uint16_t* dst = (uint16_t*)a.out + row0 * 512 + 8 * lane;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const f32x4 v0 = *(const f32x4*)(st + r * kStagePitch + 32 * lane);
+      const f32x4 v1 = *(const f32x4*)(st + r * kStagePitch + 32 * lane + 16);
+      *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                       pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+    }
+  }
+  // Split jobs of a decode with an FP8 output: seed the combine's running amax.
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && tid == 0) a.out_scale[t] = -0.0f;
+}
+
+// ---------------------------------------------------------------------------
 // Combine: O = sum_s 2^(LSE_s - M) O_s / sum_s 2^(LSE_s - M), then the sink and
 // the cast.  One wave merges one (token, head) row: lane l owns columns
 // [4l, 4l+4) and [256+4l, 256+4l+4); lane s also loads split s's LSE.  The
@@ -1516,6 +1878,13 @@ hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream
       hipLaunchKernelGGL((KERNEL<false, DIRECT, CSV, PREFETCH>), grid, dim3(THREADS), 0, stream, a.indices,\
                          a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                         \
   } while (0)
+  // 64 heads in one column part, bf16 pool, no direct FP8 output: the 8-wave
+  // kernel whose wave pairs trade their weights.
+  if (a.h_q == 64 && cs == 1 && !kv_fp8 && !(DIRECT && a.out_dtype == kOutFp8)) {
+    hipLaunchKernelGGL((decode_kernel8p<DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices, a.q,
+                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);
+    return hipGetLastError();
+  }
   // 64 heads in 2, 4 or 8 column parts: the 8-wave kernel (two waves per SIMD).
   const bool eight = a.h_q == 64 && cs >= 2;
   if (eight && cs == 8)
