@@ -332,29 +332,51 @@ def summarize_kernel_stats(directory):
         print(f"{r['Name'][:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.3f} "
               f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
     # The dispatches of the event-timed batches (kernel_durations): a GPU sleep, then
-    # one kernel launched back to back many times.  Their mean trace duration is the
-    # like-for-like counterpart of the HIP-event figure.
+    # one call of the library repeated back to back (one or two kernels per call).
+    # Their mean trace duration is the like-for-like counterpart of the HIP-event figure.
+    import re
     trace = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
-    print("\ndispatches of the event-timed batches (runs of >= 20 launches of one kernel after the GPU sleep):")
+
+    def short(name):
+        m = re.search(r"::(\w+)<", name)
+        return m.group(1) if m else name[:40]
+
+    print("\ndispatches of the event-timed batches (>= 20 repeats of one call's launches after the GPU sleep):")
     print(f"{'kernel':64s} {'batches':>7s} {'calls':>6s} {'avg_us':>9s}")
     agg = {}
+    per_call = []
     i = 0
     while i < len(trace):
         if "spin_kernel" not in trace[i]["Kernel_Name"]:
             i += 1
             continue
+        # the call's kernels: the launches up to the first repeated name
+        period = []
+        for r in trace[i + 1:]:
+            if "smla::" not in r["Kernel_Name"] or r["Kernel_Name"] in period:
+                break
+            period.append(r["Kernel_Name"])
         j = i + 1
-        while j < len(trace) and trace[j]["Kernel_Name"] == trace[i + 1]["Kernel_Name"]:
+        while period and j < len(trace) and trace[j]["Kernel_Name"] == period[(j - i - 1) % len(period)]:
             j += 1
-        run = trace[i + 1:j]
-        if len(run) >= 20:
-            a = agg.setdefault(run[0]["Kernel_Name"], [0, 0, 0.0])
-            a[0] += 1
-            a[1] += len(run)
-            a[2] += sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in run)
-        i += 1
+        calls = (j - i - 1) // len(period) if period else 0
+        if calls >= 20:
+            run = trace[i + 1:i + 1 + calls * len(period)]
+            tot = 0
+            for r in run:
+                a = agg.setdefault(r["Kernel_Name"], [0, 0, 0])
+                a[1] += 1
+                d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                a[2] += d
+                tot += d
+            for n in period:
+                agg[n][0] += 1
+            per_call.append((" + ".join(short(n) for n in period), calls, tot / calls / 1e3))
+        i = max(j, i + 1)
     for k, (nb, nc, ns) in agg.items():
         print(f"{k[:64]:64s} {nb:7d} {nc:6d} {ns / nc / 1e3:9.3f}")
+    for label, calls, us in per_call:
+        print(f"batch of {calls} calls ({label}): kernel time per call {us:.3f} us")
 
 
 def _counter_per_dispatch(directory, counter):
@@ -421,24 +443,41 @@ def pmc_summary(dirs):
         maxs = [max(v) for v in disp.values()]
         stats[(k, c)] = (np.mean(sums), np.mean(maxs))
         print(f"{k[:56]:56s} {c:32s} {len(disp):10d} {np.mean(sums):16.1f} {np.mean(maxs):16.1f}")
-    for k in sorted({k for k, _ in stats if "decode_kernel" in k}):
+    # GRBM_GUI_ACTIVE comes summed over the 8 XCDs: a dispatch's active cycles are a
+    # eighth of it (the MFMA loop probe then reads ~96% busy, as a pure MFMA loop should).
+    for k in sorted({k for k, _ in stats if "decode_kernel" in k or "mfma_loop" in k}):
         busy = stats.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"))
         active = stats.get((k, "GRBM_GUI_ACTIVE"))
         mops = stats.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
         if busy and active:
-            print(f"{k[:56]}: MFMA busy {busy[0]:.0f} SIMD-cycles over {active[1]:.0f} active cycles x 1024 SIMDs "
-                  f"= {100.0 * busy[0] / (active[1] * 1024):.1f}%")
+            cyc = active[0] / 8
+            print(f"{k[:56]}: MFMA busy {busy[0]:.0f} SIMD-cycles over {cyc:.0f} active cycles x 1024 SIMDs "
+                  f"= {100.0 * busy[0] / (cyc * 1024):.1f}%")
         if mops:
             print(f"{k[:56]}: executed bf16 MFMA flops per dispatch {mops[0] * 512:.4g}")
 
 
 def kernel_label(s_q, S, pool, cus=256):
-    """Which attention kernel a launch runs (mirrors sparse_mla_decode's choice for 64
-    heads): the 8-wave kernel when the jobs take 2, 4 or 8 column parts."""
+    """Which attention kernel(s) a launch runs (mirrors sparse_mla_decode's choice for 64
+    heads): the 8-wave kernel when the jobs take 2, 4 or 8 column parts; with one part,
+    the paired 8-wave kernel (bf16 pool) or the 4-wave kernel (FP8 pool), and a last
+    round that would fill at most half of the CUs goes to a second launch with more
+    column parts."""
     jobs = s_q * S
     cs = 8 if 8 * jobs <= cus else 4 if 4 * jobs <= cus else 2 if 2 * jobs <= cus else 1
-    name = "decode_kernel8" if cs >= 2 else "decode_kernel"
-    return f"{name}<{pool} pool, {'partial' if S > 1 else 'direct'}, {cs} column part{'s' if cs > 1 else ''}>"
+    mode = "partial" if S > 1 else "direct"
+
+    def one(c):
+        if c >= 2:
+            return f"decode_kernel8<{pool} pool, {mode}, {c} column parts>"
+        name = "decode_kernel8p" if pool == "bf16" else "decode_kernel"
+        return f"{name}<{pool} pool, {mode}, 1 column part>"
+
+    tail = jobs % cus
+    if cs == 1 and jobs > cus and 0 < tail and 2 * tail <= cus:
+        ct = 8 if 8 * tail <= cus else 4 if 4 * tail <= cus else 2
+        return f"{one(1)} over {jobs - tail} jobs + {one(ct)} over the last {tail}"
+    return one(cs)
 
 
 def _single_splits():

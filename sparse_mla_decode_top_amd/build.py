@@ -20,7 +20,7 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # preload the attention kernel's leading scalar arguments into SGPRs
-    "-mllvm", "-amdgpu-kernarg-preload-count=7",
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
     "-Wall", "-Wno-unused-lambda-capture",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

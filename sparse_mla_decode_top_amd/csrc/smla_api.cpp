@@ -200,6 +200,7 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
                 : 4 * jobs <= cus                                ? 4
                 : 2 * jobs <= cus                                ? 2
                                                                  : 1;
+  a.cus = cus;
 
   if (direct) {        // direct path: one job per token, fused epilogue
     return smla::launch_decode_direct(a, fp8, hs) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;

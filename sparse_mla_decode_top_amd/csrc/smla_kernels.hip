@@ -45,6 +45,13 @@
 // reads with the other's MFMAs; the two slot halves of a head merge in the
 // epilogue as two splits would.
 //
+// decode_kernel8p: 8 waves for 64 heads in one column part (bf16 pool).  The
+// waves of a pair score one slot half each, trade their weights through LDS
+// and accumulate every slot into their own half of the columns, under one
+// shared frame per head.  With more jobs than compute units, a last round
+// that fills at most half of them runs as a second launch with 2, 4 or 8
+// column parts.
+//
 // combine kernel: split-major partials -> final output (+ sink, cast).
 
 #include <hip/hip_runtime.h>
@@ -313,18 +320,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Job decode shared by every wave.  Job id = token * num_splits + split; with
-// CS > 1 column parts, the workgroups of a job are 8 block ids apart in
-// groups of 8 * CS (blocks are spread over the 8 XCDs round robin, so all of
-// them land on one XCD and share its L2 for the job's rows).  Blocks [b0, b1) of split
-// s: near-equal ranges, the remainder on the leading splits, empty past the
-// end.  part: which 512 / CS output columns this workgroup owns.
+// Job decode shared by every wave.  Job id = token * num_splits + split; a
+// launch covers the jobs from job0 on.  With CS > 1 column parts, the
+// workgroups of a job are 8 block ids apart in groups of 8 * CS (blocks are
+// spread over the 8 XCDs round robin, so all of them land on one XCD and
+// share its L2 for the job's rows).  Blocks [b0, b1) of split s: near-equal
+// ranges, the remainder on the leading splits, empty past the end.  part:
+// which 512 / CS output columns this workgroup owns.
 struct Job {
   int t, s, b0, b1, part;
   bool live;
 };
 template <int CS>
-__device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int n_jobs) {
+__device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int job0, int n_jobs) {
   Job j;
   int id = blockIdx.x;
   j.part = 0;
@@ -332,6 +340,7 @@ __device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int n_jo
     j.part = (id >> 3) % CS;
     id = (id / (8 * CS)) * 8 + (id & 7);
   }
+  id += job0;
   j.live = id < n_jobs;
   j.t = id / num_splits;
   j.s = id - j.t * num_splits;
@@ -354,7 +363,7 @@ __device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int n_jo
 template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
-    int32_t s_q, int32_t topk, int32_t h_q, DecodeArgs a) {
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
   constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
   constexpr int kCols = 512 / CS;
   constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
@@ -372,7 +381,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
   const int head = 16 * wave + hl;
 
-  const Job job = decode_job<CS>(num_splits, n_blocks, s_q * num_splits);
+  const Job job = decode_job<CS>(num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the CS > 1 grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = indices + (int64_t)t * topk;
@@ -862,7 +871,7 @@ constexpr int kThreads8 = 64 * kWaves8;
 template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
 __global__ __launch_bounds__(kThreads8) void decode_kernel8(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
-    int32_t s_q, int32_t topk, int32_t h_q, DecodeArgs a) {
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
   static_assert(CS >= 2, "the 8-wave layout needs at least two column parts");
   constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
   constexpr int kCols = 512 / CS;
@@ -885,7 +894,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
   const int sg = wave >> 2;               // slot half: slots [32 sg, 32 sg + 32) of each block
   const int head = 16 * hq + hl;
 
-  const Job job = decode_job<CS>(num_splits, n_blocks, s_q * num_splits);
+  const Job job = decode_job<CS>(num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = indices + (int64_t)t * topk;
@@ -1284,7 +1293,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
 template <bool DIRECT, bool PREFETCH>
 __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
-    int32_t s_q, int32_t topk, int32_t h_q, DecodeArgs a) {
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
   constexpr int kCt = 16;                         // column tiles of 16 owned by a wave
   constexpr int kStagePitch = 512 * 4 + 16;       // LDS pitch of a staged fp32 output row
   static_assert(64 * kStagePitch <= 2 * kTileBytes, "staging must fit in the tile buffers");
@@ -1304,7 +1313,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
   float* const pex_own = (float*)s_pex[wave];
   const float* const pex_par = (const float*)s_pex[wave ^ 4];
 
-  const Job job = decode_job<1>(num_splits, n_blocks, s_q * num_splits);
+  const Job job = decode_job<1>(num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = indices + (int64_t)t * topk;
@@ -1864,25 +1873,25 @@ __global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArg
 }  // namespace
 
 namespace {
+// One launch over jobs [job0, job1) with cs column parts.
 template <bool DIRECT, bool PREFETCH>
-hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
-  const unsigned n_jobs = (unsigned)(a.s_q * (DIRECT ? 1 : a.num_splits));
-  const int cs = a.col_parts;
+hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int job1, hipStream_t stream) {
+  const unsigned n_jobs = (unsigned)(job1 - job0);
   const dim3 grid(cs == 1 ? n_jobs : (n_jobs + 7) / 8 * 8 * cs);
 #define SMLA_LAUNCH(KERNEL, THREADS, CSV)                                                                 \
   do {                                                                                                    \
     if (kv_fp8)                                                                                           \
       hipLaunchKernelGGL((KERNEL<true, DIRECT, CSV, PREFETCH>), grid, dim3(THREADS), 0, stream, a.indices, \
-                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                         \
+                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);                   \
     else                                                                                                  \
       hipLaunchKernelGGL((KERNEL<false, DIRECT, CSV, PREFETCH>), grid, dim3(THREADS), 0, stream, a.indices,\
-                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);                         \
+                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);                   \
   } while (0)
   // 64 heads in one column part, bf16 pool, no direct FP8 output: the 8-wave
   // kernel whose wave pairs trade their weights.
   if (a.h_q == 64 && cs == 1 && !kv_fp8 && !(DIRECT && a.out_dtype == kOutFp8)) {
     hipLaunchKernelGGL((decode_kernel8p<DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices, a.q,
-                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, a);
+                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
     return hipGetLastError();
   }
   // 64 heads in 2, 4 or 8 column parts: the 8-wave kernel (two waves per SIMD).
@@ -1903,6 +1912,25 @@ hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream
     SMLA_LAUNCH(decode_kernel, kThreads, 1);
 #undef SMLA_LAUNCH
   return hipGetLastError();
+}
+
+// The whole launch plan.  With one column part and more jobs than compute
+// units, the last round would leave CUs idle: when it holds at most half of
+// them, its jobs go to a second launch with 2, 4 or 8 column parts (the
+// largest that keeps it within one round), so it finishes sooner.  A direct
+// FP8 output keeps one part (its scale needs every column).
+template <bool DIRECT, bool PREFETCH>
+hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
+  const int n_jobs = a.s_q * (DIRECT ? 1 : a.num_splits);
+  const int cus = a.cus;
+  const int tail = cus > 0 ? n_jobs % cus : 0;
+  if (a.col_parts == 1 && n_jobs > cus && tail > 0 && 2 * tail <= cus && !(DIRECT && a.out_dtype == kOutFp8)) {
+    const int cs_tail = 8 * tail <= cus ? 8 : 4 * tail <= cus ? 4 : 2;
+    const hipError_t e = launch_jobs<DIRECT, PREFETCH>(a, kv_fp8, 1, 0, n_jobs - tail, stream);
+    if (e != hipSuccess) return e;
+    return launch_jobs<DIRECT, PREFETCH>(a, kv_fp8, cs_tail, n_jobs - tail, n_jobs, stream);
+  }
+  return launch_jobs<DIRECT, PREFETCH>(a, kv_fp8, a.col_parts, 0, n_jobs, stream);
 }
 }  // namespace
 
