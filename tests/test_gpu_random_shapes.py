@@ -2,7 +2,10 @@
 pool sizes, split counts, padding, sink, pool and output formats drawn at
 random, so that every kernel the library picks (the 8-wave and the 4-wave
 attention kernels at 1, 2, 4 or 8 column parts, with and without the look-ahead
-gather) and both paths meet the oracle bars on shapes no fixed test names.
+gather) and both paths meet the oracle bars on shapes no fixed test names.  A
+second set draws more jobs than compute units (s_q from 129 to 390): the
+one-part kernel whose wave pairs trade weights, and the second launch that takes
+a last round of at most half the compute units with more column parts.
 """
 import numpy as np
 import pytest
@@ -15,6 +18,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 N_CASES = 40
+N_LARGE = 12
 
 
 def _case(i):
@@ -35,9 +39,33 @@ def _case(i):
                 path=path, out=out, seed=2000 + i)
 
 
+def _case_large(i):
+    rng = np.random.default_rng(5000 + i)
+    s_q = int(rng.choice([129, 160, 200, 257, 300, 390]))
+    h_q = int(rng.choice([32, 64, 64, 64]))
+    topk = int(rng.choice([64, 100, 128, 200, 333]))
+    n_pool = int(rng.choice([4096, 20000, 70000]))
+    kv_dtype = "fp8" if rng.random() < 0.25 else "bf16"
+    pad = rng.choice([None, "random", "trailing"])
+    sink = bool(rng.random() < 0.7)
+    S = int(rng.choice([1, 1, 2, 3]))
+    path = "direct" if S == 1 and rng.random() < 0.6 else "split"
+    out = str(rng.choice(["f32", "bf16", "fp8"]))
+    return dict(s_q=s_q, h_q=h_q, topk=topk, n_pool=n_pool, kv_dtype=kv_dtype, pad=pad, sink=sink, S=S,
+                path=path, out=out, seed=6000 + i)
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape_matches_oracle(i):
-    c = _case(i)
+    _check(i, _case(i))
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_large_batch_matches_oracle(i):
+    _check(i, _case_large(i))
+
+
+def _check(i, c):
     print(f"[case] {i}: {c}", flush=True)
     inp = W.make_inputs(c["s_q"], c["h_q"], c["n_pool"], c["topk"], c["seed"], kv_dtype=c["kv_dtype"],
                         sink=c["sink"], pad=c["pad"])
