@@ -460,9 +460,9 @@ def pmc_summary(dirs):
 def kernel_label(s_q, S, pool, cus=256):
     """Which attention kernel(s) a launch runs (mirrors sparse_mla_decode's choice for 64
     heads): the 8-wave kernel when the jobs take 2, 4 or 8 column parts; with one part,
-    the paired 8-wave kernel (bf16 pool) or the 4-wave kernel (FP8 pool), and a last
-    round that would fill at most half of the CUs goes to a second launch with more
-    column parts."""
+    the paired 8-wave kernel (bf16 pool) or the 4-wave kernel (FP8 pool); a last round
+    that would fill at most half of the CUs takes more column parts, in the same launch
+    (bf16 pool: the mixed kernel) or a second one."""
     jobs = s_q * S
     cs = 8 if 8 * jobs <= cus else 4 if 4 * jobs <= cus else 2 if 2 * jobs <= cus else 1
     mode = "partial" if S > 1 else "direct"
@@ -476,6 +476,9 @@ def kernel_label(s_q, S, pool, cus=256):
     tail = jobs % cus
     if cs == 1 and jobs > cus and 0 < tail and 2 * tail <= cus:
         ct = 8 if 8 * tail <= cus else 4 if 4 * tail <= cus else 2
+        if pool == "bf16" and (jobs - tail) % 8 == 0:
+            return (f"decode_kernel8m<bf16 pool, {mode}: decode_kernel8p's body over {jobs - tail} jobs, "
+                    f"decode_kernel8's with {ct} column parts over the last {tail}>")
         return f"{one(1)} over {jobs - tail} jobs + {one(ct)} over the last {tail}"
     return one(cs)
 

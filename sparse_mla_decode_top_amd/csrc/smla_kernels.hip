@@ -49,8 +49,8 @@
 // waves of a pair score one slot half each, trade their weights through LDS
 // and accumulate every slot into their own half of the columns, under one
 // shared frame per head.  With more jobs than compute units, a last round
-// that fills at most half of them runs as a second launch with 2, 4 or 8
-// column parts.
+// that fills at most half of them takes 2, 4 or 8 column parts:
+// decode_kernel8m runs both bodies in one launch.
 //
 // combine kernel: split-major partials -> final output (+ sink, cast).
 
@@ -332,9 +332,9 @@ struct Job {
   bool live;
 };
 template <int CS>
-__device__ __forceinline__ Job decode_job(int num_splits, int n_blocks, int job0, int n_jobs) {
+__device__ __forceinline__ Job decode_job(int block, int num_splits, int n_blocks, int job0, int n_jobs) {
   Job j;
-  int id = blockIdx.x;
+  int id = block;
   j.part = 0;
   if (CS > 1) {
     j.part = (id >> 3) % CS;
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
   const int head = 16 * wave + hl;
 
-  const Job job = decode_job<CS>(num_splits, n_blocks, job0, s_q * num_splits);
+  const Job job = decode_job<CS>((int)blockIdx.x, num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the CS > 1 grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = indices + (int64_t)t * topk;
@@ -868,22 +868,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 constexpr int kWaves8 = 8;
 constexpr int kThreads8 = 64 * kWaves8;
 
+// LDS of decode_kernel8: the two tiles, then the per-block scale and bias rows,
+// the epilogue's frame / denominator exchange, the LSEs and the restart flag.
+constexpr int kLds8Scale = 2 * kTileBytes;
+constexpr int kLds8Bias = kLds8Scale + 2 * kBlk * 4;
+constexpr int kLds8Ml = kLds8Bias + 2 * kBlk * 4;
+constexpr int kLds8Lse = kLds8Ml + 2 * 2 * 64 * 4;
+constexpr int kLds8Restart = kLds8Lse + 64 * 4;
+constexpr int kLds8Bytes = kLds8Restart + 16;
+
+// The body of decode_kernel8 for workgroup `block` of its launch, on the LDS at
+// `smem` (kLds8Bytes); a kernel of its own, or one half of a mixed launch.
 template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
-__global__ __launch_bounds__(kThreads8) void decode_kernel8(
+__device__ __forceinline__ void decode8_body(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
-    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, const DecodeArgs& a, int block, uint8_t* smem) {
   static_assert(CS >= 2, "the 8-wave layout needs at least two column parts");
   constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
   constexpr int kCols = 512 / CS;
   constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
   constexpr int kStageBytes = 64 * kStagePitch;   // the 64 staged head rows of one slot half
   static_assert(2 * kStageBytes <= 2 * kTileBytes, "staging must fit in the tile buffers");
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
-  __shared__ __attribute__((aligned(16))) float s_scale[2][kBlk];
-  __shared__ __attribute__((aligned(16))) float s_bias[2][kBlk];   // 0: valid slot, kMaskedScore: masked
-  __shared__ float s_ml[2][2][64];     // [slot half][frame M, denominator l][head]
-  __shared__ float s_lse[64];
-  __shared__ int s_restart;
+  uint8_t* const s_tile = smem;                                                  // [2 * kTileBytes]
+  float (*const s_scale)[kBlk] = reinterpret_cast<float (*)[kBlk]>(smem + kLds8Scale);   // [2][kBlk]
+  // [2][kBlk]: 0 for a valid slot, kMaskedScore for a masked one
+  float (*const s_bias)[kBlk] = reinterpret_cast<float (*)[kBlk]>(smem + kLds8Bias);
+  // [slot half][frame M, denominator l][head]
+  float (*const s_ml)[2][64] = reinterpret_cast<float (*)[2][64]>(smem + kLds8Ml);
+  float* const s_lse = reinterpret_cast<float*>(smem + kLds8Lse);               // [64]
+  int& s_restart = *reinterpret_cast<int*>(smem + kLds8Restart);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -894,7 +907,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
   const int sg = wave >> 2;               // slot half: slots [32 sg, 32 sg + 32) of each block
   const int head = 16 * hq + hl;
 
-  const Job job = decode_job<CS>(num_splits, n_blocks, job0, s_q * num_splits);
+  const Job job = decode_job<CS>(block, num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = indices + (int64_t)t * topk;
@@ -1276,6 +1289,15 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
   if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
 }
 
+template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
+__global__ __launch_bounds__(kThreads8) void decode_kernel8(
+    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds8Bytes];
+  decode8_body<KV_FP8, DIRECT, CS, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a,
+                                             (int)blockIdx.x, smem);
+}
+
 // ---------------------------------------------------------------------------
 // decode_kernel8p: one 8-wave workgroup per job that owns all 512 output
 // columns (64 heads, bf16 pool), for launches with a single column part.
@@ -1290,17 +1312,23 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8(
 // frame, end-of-pass and denominator exchanges reuse the weight area, and
 // validity comes from a ballot of the block's indices.
 // ---------------------------------------------------------------------------
+// LDS of decode_kernel8p: the two tiles, then the weight exchange.
+constexpr int kLds8pBytes = 2 * kTileBytes + kWaves8 * 2048;
+static_assert(kLds8pBytes >= kLds8Bytes, "a mixed launch takes the larger LDS of its two bodies");
+
+// The body of decode_kernel8p for workgroup `block` of its launch, on the LDS
+// at `smem` (kLds8pBytes).
 template <bool DIRECT, bool PREFETCH>
-__global__ __launch_bounds__(kThreads8) void decode_kernel8p(
+__device__ __forceinline__ void decode8p_body(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
-    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, const DecodeArgs& a, int block, uint8_t* smem) {
   constexpr int kCt = 16;                         // column tiles of 16 owned by a wave
   constexpr int kStagePitch = 512 * 4 + 16;       // LDS pitch of a staged fp32 output row
   static_assert(64 * kStagePitch <= 2 * kTileBytes, "staging must fit in the tile buffers");
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
+  uint8_t* const s_tile = smem;                   // [2 * kTileBytes]
   // Per wave: its block weights (bf16 hi terms at +0, lo terms at +1024, 16
   // bytes a lane in MFMA operand order), read by the partner wave.
-  __shared__ __attribute__((aligned(16))) uint8_t s_pex[kWaves8][2048];
+  uint8_t (*const s_pex)[2048] = reinterpret_cast<uint8_t (*)[2048]>(smem + 2 * kTileBytes);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -1313,7 +1341,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
   float* const pex_own = (float*)s_pex[wave];
   const float* const pex_par = (const float*)s_pex[wave ^ 4];
 
-  const Job job = decode_job<1>(num_splits, n_blocks, job0, s_q * num_splits);
+  const Job job = decode_job<1>(block, num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = indices + (int64_t)t * topk;
@@ -1638,6 +1666,34 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
   if (!DIRECT && a.out_scale != nullptr && job.s == 0 && tid == 0) a.out_scale[t] = -0.0f;
 }
 
+template <bool DIRECT, bool PREFETCH>
+__global__ __launch_bounds__(kThreads8) void decode_kernel8p(
+    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds8pBytes];
+  decode8p_body<DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a, (int)blockIdx.x,
+                                  smem);
+}
+
+// One launch for more jobs than compute units, with a short last round: its
+// first n_head workgroups run decode_kernel8p's body over jobs [0, n_head),
+// the rest decode_kernel8's body with CST column parts over the jobs from
+// n_head on.  The tail's workgroups start as soon as compute units free up,
+// with no kernel boundary in between.  n_head is a multiple of 8, so the tail
+// keeps decode_kernel8's XCD grouping of a job's column parts.
+template <bool DIRECT, bool PREFETCH, int CST>
+__global__ __launch_bounds__(kThreads8) void decode_kernel8m(
+    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t n_head, DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds8pBytes];
+  const int block = (int)blockIdx.x;
+  if (block < n_head)
+    decode8p_body<DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, 0, a, block, smem);
+  else
+    decode8_body<false, DIRECT, CST, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, n_head, a,
+                                               block - n_head, smem);
+}
+
 // ---------------------------------------------------------------------------
 // Combine: O = sum_s 2^(LSE_s - M) O_s / sum_s 2^(LSE_s - M), then the sink and
 // the cast.  One wave merges one (token, head) row: lane l owns columns
@@ -1916,9 +1972,10 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
 
 // The whole launch plan.  With one column part and more jobs than compute
 // units, the last round would leave CUs idle: when it holds at most half of
-// them, its jobs go to a second launch with 2, 4 or 8 column parts (the
-// largest that keeps it within one round), so it finishes sooner.  A direct
-// FP8 output keeps one part (its scale needs every column).
+// them, its jobs take 2, 4 or 8 column parts (the largest that keeps it within
+// one round), so it finishes sooner -- in the same launch for a bf16 pool and
+// 64 heads (decode_kernel8m), else in a second one.  A direct FP8 output
+// keeps one part (its scale needs every column).
 template <bool DIRECT, bool PREFETCH>
 hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
   const int n_jobs = a.s_q * (DIRECT ? 1 : a.num_splits);
@@ -1926,6 +1983,21 @@ hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream
   const int tail = cus > 0 ? n_jobs % cus : 0;
   if (a.col_parts == 1 && n_jobs > cus && tail > 0 && 2 * tail <= cus && !(DIRECT && a.out_dtype == kOutFp8)) {
     const int cs_tail = 8 * tail <= cus ? 8 : 4 * tail <= cus ? 4 : 2;
+    const int n_head = n_jobs - tail;
+    if (a.h_q == 64 && !kv_fp8 && n_head % 8 == 0) {     // both bodies in one launch
+      const dim3 grid((unsigned)(n_head + (tail + 7) / 8 * 8 * cs_tail));
+#define SMLA_LAUNCH_MIXED(CSV)                                                                                \
+  hipLaunchKernelGGL((decode_kernel8m<DIRECT, PREFETCH, CSV>), grid, dim3(kThreads8), 0, stream, a.indices, a.q, \
+                     a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, n_head, a)
+      if (cs_tail == 8)
+        SMLA_LAUNCH_MIXED(8);
+      else if (cs_tail == 4)
+        SMLA_LAUNCH_MIXED(4);
+      else
+        SMLA_LAUNCH_MIXED(2);
+#undef SMLA_LAUNCH_MIXED
+      return hipGetLastError();
+    }
     const hipError_t e = launch_jobs<DIRECT, PREFETCH>(a, kv_fp8, 1, 0, n_jobs - tail, stream);
     if (e != hipSuccess) return e;
     return launch_jobs<DIRECT, PREFETCH>(a, kv_fp8, cs_tail, n_jobs - tail, n_jobs, stream);
