@@ -170,7 +170,7 @@ __device__ __forceinline__ int load_idx_and_q(const int32_t* idx_ptr, const void
   int idx;
   uint32_t saved;
   asm volatile(
-      "global_load_dword %0, %2, off nt\n\t"
+      "global_load_dword %0, %2, off\n\t"
       "s_mov_b32 %1, m0\n\t"
       "s_mov_b32 m0, %5\n\t"
       "s_nop 0\n\t"
@@ -195,7 +195,7 @@ __device__ __forceinline__ int load_idx_and_q1(const int32_t* idx_ptr, const voi
   int idx;
   uint32_t saved;
   asm volatile(
-      "global_load_dword %0, %2, off nt\n\t"
+      "global_load_dword %0, %2, off\n\t"
       "s_mov_b32 %1, m0\n\t"
       "s_mov_b32 m0, %4\n\t"
       "s_nop 0\n\t"
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // branch, hence no early wait on it); slots past the split or the list are
     // masked where the index is used.
     auto load_idx = [&](int b) -> int {
-      return __builtin_nontemporal_load(idx_row + min(b * kBlk + lane, topk - 1));
+      return idx_row[min(b * kBlk + lane, topk - 1)];
     };
     auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
     auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
@@ -922,7 +922,7 @@ __device__ __forceinline__ void decode8_body(
 
   if (job.b0 < job.b1) {
     auto load_idx = [&](int b) -> int {
-      return __builtin_nontemporal_load(idx_row + min(b * kBlk + lane, topk - 1));
+      return idx_row[min(b * kBlk + lane, topk - 1)];
     };
     auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
     auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
@@ -1356,7 +1356,7 @@ __device__ __forceinline__ void decode8p_body(
 
   if (job.b0 < job.b1) {
     auto load_idx = [&](int b) -> int {
-      return __builtin_nontemporal_load(idx_row + min(b * kBlk + lane, topk - 1));
+      return idx_row[min(b * kBlk + lane, topk - 1)];
     };
     auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
     auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
