@@ -354,6 +354,46 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
 
 
+
+def test_graph_capture_of_the_mixed_launch_replays_match_eager():
+    """300 tokens on the direct path: one launch runs the one-part body over 256 jobs and
+    the 4-part body over the last 44.  Captured into a HIP graph, every replay equals
+    eager, and eager equals the oracle on a sample of tokens."""
+    import sparse_mla_decode_top_amd as smla
+    inp = W.make_inputs(300, 64, 20000, 640, seed=41, sink=True, pad="random")
+    dev = H.DeviceInputs(inp)
+    out = torch.empty((inp.s_q, 64, 512), device="cuda")
+    lse = torch.empty((inp.s_q, 64), device="cuda")
+
+    def step():
+        smla.sparse_mla_decode(dev.q, dev.kv, dev.indices, 1, inp.scale, sink=dev.sink, out=out, lse_out=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    sample = np.array([0, 1, 137, 255, 256, 257, 280, 299])     # both bodies, their boundary, the last job
+    O_ref, L_ref = oracle.attend(inp.q[sample].astype(np.float64), H.oracle_pool(inp), inp.indices[sample],
+                                 inp.n_pool, inp.scale)
+    O_fin = oracle.apply_sink(O_ref, L_ref, inp.sink.astype(np.float64))
+    H.assert_o_close(ref_out.cpu().numpy()[sample], O_fin)
+    H.assert_lse_close(ref_lse.cpu().numpy()[sample], L_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
 def test_graph_capture_fp8_output_replays_match_eager():
     """FP8 pool and FP8 output, split path in a HIP graph: the attention kernel seeds each
     token's running amax before the combine's atomics, on every replay."""
