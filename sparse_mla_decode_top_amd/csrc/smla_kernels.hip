@@ -936,8 +936,9 @@ __device__ __forceinline__ void decode8_body(
     // [16w, 16w + 16) (4 lanes a row, chunk l & 3 of each quartet).
     const bool gathers = !KV_FP8 || wave < 4;
 
-    // bf16: every lane issues its 9 DMAs (a masked row copies the zero row), so a
-    // wave always has exactly 9 of them in flight (the first pass counts on it).
+    // Every gathering lane issues its 9 DMAs (a masked row copies the zero row),
+    // so a gathering wave always has exactly 9 of them in flight (the first pass
+    // counts on it).
     auto issue_gather = [&](int idx_lane, int buf) {
       if (!KV_FP8) {
         const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
@@ -948,14 +949,9 @@ __device__ __forceinline__ void decode8_body(
       } else if (gathers) {
         const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
         const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
-        if (valid_of(row_idx)) {
-          const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + (lane & 3) * 16;
-          dma_quartets(src, __builtin_amdgcn_readfirstlane(lds_base));
-        } else {
-          uint8_t* dst = s_tile + buf * kBufBytes + wave * 1024 + lane * 16;
-#pragma unroll
-          for (int q = 0; q < 9; ++q) *(u32x4*)(dst + 4096 * q) = u32x4{0u, 0u, 0u, 0u};
-        }
+        const uint8_t* src =
+            (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
+        dma_quartets(src, __builtin_amdgcn_readfirstlane(lds_base));
       }
     };
 
@@ -986,17 +982,21 @@ __device__ __forceinline__ void decode8_body(
     issue_gather(idx_cur, 0);
     int idx_nxt = load_idx(job.b0 + 1);
     bool valid_cur = valid_of(idx_cur);
-    float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
     if (first) {
-      // Q rows landed: bf16 waits for them alone (issued first; behind them the 9
-      // DMAs of block b0 and, with the look-ahead, the next index load, which
-      // stay in flight while the Q fragments are read); FP8 waits for everything.
-      if (KV_FP8)
-        wait_vmem_all();
-      else if (PREFETCH)
-        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      // Q rows landed.  They were issued first; behind them stay in flight, while
+      // the Q fragments are read: block b0's 9 DMAs (bf16: every wave; FP8: the
+      // gathering waves 0-3) and, with the look-ahead, the next index load.
+      if (gathers) {
+        if (PREFETCH)
+          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else {
+        if (PREFETCH)
+          asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       lds_barrier();
       const uint32_t qt = lds_addr(s_tile) + kQOffset + hq * 2048;
 #pragma unroll
@@ -1005,6 +1005,8 @@ __device__ __forceinline__ void decode8_body(
         qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
       }
     }
+    // FP8: block b0's row scales (read at the top of the block loop).
+    float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
 
     for (int b = job.b0; b < job.b1; ++b) {
       const int cur = (b - job.b0) & 1;
