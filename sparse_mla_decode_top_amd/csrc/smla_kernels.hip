@@ -2031,6 +2031,379 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8h(
                                   smem);
 }
 
+// ---------------------------------------------------------------------------
+// decode4t_body: a job in 4 CP workgroups of 4 waves, each owning one head tile
+// (16 heads) and 512 / CP of the output columns (bf16 pool, 64 heads; CP = 1
+// or 2).  None of them repeats another head tile's QK^T, where 4 or 8 column
+// parts would each compute all 64 heads' scores.  Wave w scores slot quarter
+// w (16 slots) of every block; the four waves trade their bf16 weights through
+// LDS (as decode8h_body's head tile) and each accumulates every slot into its
+// quarter of the workgroup's columns.  One frame per head for the four.  The
+// workgroups of a job are 8 block ids apart (one XCD, one L2 for the rows).
+// ---------------------------------------------------------------------------
+constexpr int kLds4tBytes = 2 * kTileBytes + kWaves * 1024;
+
+template <bool DIRECT, bool PREFETCH, int CP>
+__device__ __forceinline__ void decode4t_body(
+    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, const DecodeArgs& a, int block, uint8_t* smem) {
+  static_assert(CP == 1 || CP == 2, "one head tile takes 1 or 2 column parts");
+  constexpr int kCols = 512 / CP;                 // columns of the workgroup
+  constexpr int kWCols = kCols / 4;               // columns of a wave
+  constexpr int kCt = kWCols / 16;                // column tiles of 16 owned by a wave
+  constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
+  uint8_t* const s_tile = smem;                   // [2 * kTileBytes]
+  // Per wave: its block weights (4 a lane, MFMA output order): bf16 hi terms
+  // at +0, lo terms at +512, 8 bytes a lane.
+  uint8_t (*const s_pex)[1024] = reinterpret_cast<uint8_t (*)[1024]>(smem + 2 * kTileBytes);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;              // slot quarter of the scores; column quarter of the output
+  const int lane = tid & 63;
+  const int hl = lane & 15;               // head within the head tile (MFMA column)
+  const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
+  float* const pex_own = (float*)s_pex[wave];
+  auto pex_of = [&](int q) -> const float* { return (const float*)s_pex[q]; };
+
+  const Job job = decode_job<4 * CP>(block, num_splits, n_blocks, job0, s_q * num_splits);
+  if (!job.live) return;                          // padding of the grid (whole workgroup)
+  const int t = job.t;
+  const int htile = job.part / CP;                // head tile: heads [16 htile, +16)
+  const int cpart = job.part % CP;                // columns [kCols cpart, +kCols)
+  const int head = 16 * htile + hl;
+  const int32_t* idx_row = indices + (int64_t)t * topk;
+
+  float M_run = kNoFrame;             // integer frame of this lane's head, shared by the four waves
+  float m_seen = kMaskedScore;        // largest score seen so far over this wave's slots
+  float l_run = 0.f;                  // this lane's share of the denominator
+  float l_tot = 0.f;                  // the head's denominator over all four quarters (after the last pass)
+  f32x4 acc[kCt];                     // O^T: column tile ct -> columns kCols cpart + kWCols wave + 16ct + 4G + i
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (job.b0 < job.b1) {
+    auto load_idx = [&](int b) -> int {
+      return idx_row[min(b * kBlk + lane, topk - 1)];
+    };
+    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
+    auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
+    const float scale_log2 = a.scale_log2;
+    bf16x8 qf[18];                    // Q fragments: head, dims 32ks + 8G .. +8
+    const uint32_t tile_lds0 = lds_addr(s_tile);
+    bool framed = false;              // workgroup-uniform: the frames are set
+
+    // Wave w gathers rows [16w, 16w + 16) as two groups of 8 (lanes 8k..8k+7
+    // one row, chunk (l & 7) ^ (row & 7) of each octet): 18 DMAs a wave, a
+    // masked row copying the zero row.
+    auto row_src = [&](int idx_lane, int grp) -> const uint8_t* {
+      const int row_idx = __shfl(idx_lane, 16 * wave + 8 * grp + (lane >> 3));
+      return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+             (((lane & 7) ^ rsw(lane >> 3)) * 16);
+    };
+    auto issue_gather = [&](int idx_lane, int buf) {
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp)
+        dma_octets(row_src(idx_lane, grp),
+                   __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kTileBytes + (2 * wave + grp) * 1024));
+    };
+
+    // per-lane LDS byte offsets of the operand reads (the tile layout above)
+    const int sw_k = rsw(hl);
+    const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
+    const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
+    const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
+    const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
+    int vb[4];                                                  // column tile ct & 3
+#pragma unroll
+    for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
+
+    // ---- prologue: the head tile's 16 Q rows into LDS at kQOffset; wave w
+    // stages rows [8 (w & 1), +8) (waves 2-3 repeat waves 0-1's rows, same
+    // bytes, so every wave has the same loads in flight).
+    int idx_cur;
+    {
+      const int r0 = 8 * (wave & 1) + (lane >> 3);
+      const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
+      const uint8_t* qbase = (const uint8_t*)(q_ptr + ((int64_t)t * h_q + 16 * htile) * 576);
+      idx_cur = load_idx_and_q1(idx_row + min(job.b0 * kBlk + lane, topk - 1), qbase + (int64_t)r0 * 1152 + chunk,
+                                __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + (wave & 1) * 1024));
+    }
+
+    auto run_pass = [&](const bool first) __attribute__((always_inline)) -> bool {
+    bool overflow = false;
+    if (!first) idx_cur = load_idx(job.b0);
+    idx_cur = slot_in(job.b0) ? idx_cur : -1;
+    issue_gather(idx_cur, 0);
+    int idx_nxt = load_idx(job.b0 + 1);
+    bool valid_cur = valid_of(idx_cur);
+    if (first) {
+      // Q rows landed (issued first; block b0's 18 DMAs and, with the
+      // look-ahead, the next index load stay in flight).
+      if (PREFETCH)
+        asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      lds_barrier();
+      const uint32_t qt = lds_addr(s_tile) + kQOffset;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
+        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
+      }
+    }
+
+    for (int b = job.b0; b < job.b1; ++b) {
+      const int cur = (b - job.b0) & 1;
+      wait_vmem_all();          // this wave's share of block b has landed
+      lds_barrier();            // ... and every wave's; block b-1 and its weights fully consumed
+      // slot s of the block is valid iff bit s is set (the same in every wave)
+      const uint64_t vmask = __ballot(valid_cur);
+      const uint32_t vquart = (uint32_t)(vmask >> (16 * wave));
+      const bool blk_any = vmask != 0ull;
+
+      // Block b+1: one DMA per QK^T k-step (group 0's 9, then group 1's; masked
+      // rows and rows past the job's last block copy the zero row).
+      bool valid_nxt = false;
+      const uint8_t* gsrc0 = g_zero_row;
+      const uint8_t* gsrc1 = g_zero_row;
+      uint32_t gbase0 = 0u, gbase1 = 0u;
+      if (PREFETCH) {
+        idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
+        valid_nxt = valid_of(idx_nxt);
+        gsrc0 = row_src(idx_nxt, 0);
+        gsrc1 = row_src(idx_nxt, 1);
+        gbase0 = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + (2 * wave) * 1024);
+        gbase1 = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + (2 * wave + 1) * 1024);
+      }
+      auto gather_dma = [&](const int d) __attribute__((always_inline)) {
+        if (!PREFETCH) return;
+        switch (d) {
+          case 0: dma_one<8192, 128, 0>(gsrc0, gbase0); break;
+          case 1: dma_one<8192, 128, 1>(gsrc0, gbase0); break;
+          case 2: dma_one<8192, 128, 2>(gsrc0, gbase0); break;
+          case 3: dma_one<8192, 128, 3>(gsrc0, gbase0); break;
+          case 4: dma_one<8192, 128, 4>(gsrc0, gbase0); break;
+          case 5: dma_one<8192, 128, 5>(gsrc0, gbase0); break;
+          case 6: dma_one<8192, 128, 6>(gsrc0, gbase0); break;
+          case 7: dma_one<8192, 128, 7>(gsrc0, gbase0); break;
+          case 8: dma_one<8192, 128, 8>(gsrc0, gbase0); break;
+          case 9: dma_one<8192, 128, 0>(gsrc1, gbase1); break;
+          case 10: dma_one<8192, 128, 1>(gsrc1, gbase1); break;
+          case 11: dma_one<8192, 128, 2>(gsrc1, gbase1); break;
+          case 12: dma_one<8192, 128, 3>(gsrc1, gbase1); break;
+          case 13: dma_one<8192, 128, 4>(gsrc1, gbase1); break;
+          case 14: dma_one<8192, 128, 5>(gsrc1, gbase1); break;
+          case 15: dma_one<8192, 128, 6>(gsrc1, gbase1); break;
+          case 16: dma_one<8192, 128, 7>(gsrc1, gbase1); break;
+          default: dma_one<8192, 128, 8>(gsrc1, gbase1); break;
+        }
+      };
+      const int idx_after = load_idx(b + 2);
+
+      const uint32_t tl = lds_addr(s_tile + cur * kTileBytes);
+      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
+                                 opaque(tl + kb1 + 65536)};
+      auto kfrag = [&](int ks, int st) -> bf16x8 {
+        const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
+        return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
+      };
+      // this wave's columns start at octet (kCols cpart + kWCols wave) / 64
+      const uint32_t tlv = tl + ((kCols * cpart + kWCols * wave) / 64) * 8192;
+      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
+      auto vfrag = [&](int ct, int kk) -> bf16x8 {
+        const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
+        const i16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)(vp + 2048));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, v1);
+        return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+      };
+
+      // ---- S^T = K . Q^T over this wave's slot tile: one accumulator
+      constexpr int kAheadK = 3, kRing = kAheadK + 1, kAheadV = 4;
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        bf16x8 kf[kRing];
+#pragma unroll
+        for (int a0 = 0; a0 < kAheadK; ++a0) kf[a0] = kfrag(a0, wave);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          if (ks + kAheadK < 18) kf[(ks + kAheadK) % kRing] = kfrag(ks + kAheadK, wave);
+          __builtin_amdgcn_sched_barrier(0);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % kRing], qf[ks], sacc, 0, 0, 0);
+          gather_dma(ks);               // the next block's DMAs 0..17, one per k-step
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- softmax of this wave's 16 slots (lane: slots 16 wave + 4G + i)
+      constexpr int kAV = kAheadV < 2 * kCt ? kAheadV : 2 * kCt;
+      bf16x8 vf[kAV + 1];
+#pragma unroll
+      for (int a0 = 0; a0 < kAV; ++a0) vf[a0] = vfrag(a0 % kCt, a0 / kCt);
+      const uint32_t vbits = vquart >> (4 * G);
+      float tv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tv[i] = fmaf(sacc[i], scale_log2, ((vbits >> i) & 1u) ? 0.f : kMaskedScore);
+      float m = fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3]));
+      m = rows_max(m);
+      m_seen = fmaxf(m_seen, m);
+      if (!framed && blk_any) {
+        // first block with a valid slot: the frame is the floor of the largest
+        // of the four quarters' maxima
+        if (G == 0) pex_own[hl] = m;
+        lds_barrier();
+        M_run = floorf(fmaxf(fmaxf(pex_of(0)[hl], pex_of(1)[hl]), fmaxf(pex_of(2)[hl], pex_of(3)[hl])));
+        framed = true;
+        lds_barrier();          // every wave has read the maxima before the weights overwrite them
+      }
+      overflow |= m > M_run + kFrameSlack;
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float tt = tv[e];
+        const float fl = floorf(tt);
+        const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
+        const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+        l_run += p;
+        pv[e] = p;
+      }
+      uint32_t ph[2], pl[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t h2 = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+        ph[j] = h2;
+        pl[j] = pack_bf16x2(pv[2 * j] - __uint_as_float(h2 << 16), pv[2 * j + 1] - __uint_as_float(h2 & 0xFFFF0000u));
+      }
+      *(u32x2*)(s_pex[wave] + 8 * lane) = u32x2{ph[0], ph[1]};
+      *(u32x2*)(s_pex[wave] + 512 + 8 * lane) = u32x2{pl[0], pl[1]};
+      lds_barrier();            // every wave's weights are in LDS
+
+      // ---- O^T += V^T . P^T over the block: k-step kk takes the weights of
+      // quarters 2kk (the first 4 k-indices of each lane's group) and 2kk + 1.
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x2 h0 = *(const u32x2*)(s_pex[2 * kk] + 8 * lane);
+        const u32x2 h1 = *(const u32x2*)(s_pex[2 * kk + 1] + 8 * lane);
+        const u32x2 l0 = *(const u32x2*)(s_pex[2 * kk] + 512 + 8 * lane);
+        const u32x2 l1 = *(const u32x2*)(s_pex[2 * kk + 1] + 512 + 8 * lane);
+        const bf16x8 pfh = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
+        const bf16x8 pfl = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) {
+          const int n = kCt * kk + ct;            // position in the fragment stream
+          if (n + kAV < 2 * kCt) vf[(n + kAV) % (kAV + 1)] = vfrag((n + kAV) % kCt, (n + kAV) / kCt);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[n % (kAV + 1)], pfh, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[n % (kAV + 1)], pfl, acc[ct], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      valid_cur = valid_nxt;
+      idx_nxt = idx_after;
+    }
+    wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
+    return overflow;
+    };
+
+    // End of a pass: every wave posts its largest score, its denominator and
+    // its overflow flag; returns whether any wave of the workgroup overflowed.
+    auto end_exchange = [&](const bool overflow) __attribute__((always_inline)) -> bool {
+      const float l_w = rows_sum(l_run);
+      const bool ov = __any(overflow);
+      lds_barrier();            // every wave is past its last reads of the tiles and the weights
+      if (G == 0) {
+        pex_own[hl] = m_seen;
+        pex_own[16 + hl] = l_w;
+      }
+      if (lane == 0) ((int*)pex_own)[32] = ov ? 1 : 0;
+      lds_barrier();
+      l_run = l_w;
+      // the same sum, in the same order, in each of the four waves
+      l_tot = ((pex_of(0)[16 + hl] + pex_of(1)[16 + hl]) + pex_of(2)[16 + hl]) + pex_of(3)[16 + hl];
+      int any_ov = 0;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) any_ov |= ((const int*)s_pex[v])[32];
+      return any_ov != 0;
+    };
+
+    if (end_exchange(run_pass(true))) {
+      // the frame of the largest score of the four quarters bounds every weight by 2
+      const float ms = fmaxf(fmaxf(pex_of(0)[hl], pex_of(1)[hl]), fmaxf(pex_of(2)[hl], pex_of(3)[hl]));
+      M_run = ms > kMaskedScore ? floorf(ms) : kNoFrame;
+      framed = true;
+      l_run = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      end_exchange(run_pass(false));
+    }
+  }
+
+  // ---- epilogue: l = the four quarters' denominators (one frame), O = acc / l
+  const float l = l_tot;
+  const bool any = l > 0.f;
+  const float lse = any ? M_run + __builtin_amdgcn_logf(l) : kNegInf;
+  float oscale = any ? 1.0f / l : 0.f;
+  if (DIRECT && a.sink != nullptr && any) {
+    const float z = a.sink[head] * kLog2e - lse;
+    oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
+  }
+  const int64_t rowt = (DIRECT ? (int64_t)t * h_q : ((int64_t)job.s * s_q + t) * h_q) + 16 * htile;
+  if (wave == 0 && G == 0 && cpart == 0) {       // every column part holds the same LSE
+    if (!DIRECT)
+      a.lse_accum[rowt + hl] = lse;
+    else if (a.lse_out != nullptr)
+      a.lse_out[rowt + hl] = lse;
+  }
+
+  // Staging (row = head of the tile, the tiles are free): wave w writes its 16
+  // heads x kWCols columns; after the barrier wave w stores heads [4w, 4w + 4)
+  // in whole pieces of the workgroup's kCols columns.
+  {
+    uint8_t* stg = s_tile + hl * kStagePitch + (kWCols * wave + 4 * G) * 4;
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) *(f32x4*)(stg + 64 * ct) = acc[ct] * oscale;
+  }
+  lds_barrier();
+  const uint8_t* st = s_tile + 4 * wave * kStagePitch;
+  const int64_t row0 = rowt + 4 * wave;
+  const int col0 = kCols * cpart;
+  if (!DIRECT || a.out_dtype == kOutF32) {       // 1 KB per instruction
+    float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + col0;
+#pragma unroll
+    for (int j = 0; j < 4 * kCols / 256; ++j) {
+      const int f = 256 * j + 4 * lane;
+      const int r = f / kCols, c = f % kCols;
+      *(f32x4*)(dst + r * 512 + c) = *(const f32x4*)(st + r * kStagePitch + 4 * c);
+    }
+  } else {                                       // bf16 (a direct FP8 output never takes this kernel)
+    constexpr int kLanesPerRow = kCols / 8, kRowsPer = 64 / kLanesPerRow;
+    const int rr = lane / kLanesPerRow, cc = 8 * (lane % kLanesPerRow);
+    uint16_t* dst = (uint16_t*)a.out + row0 * 512 + col0 + cc;
+#pragma unroll
+    for (int j = 0; j < 4 / kRowsPer; ++j) {
+      const int r = kRowsPer * j + rr;
+      const f32x4 v0 = *(const f32x4*)(st + r * kStagePitch + 4 * cc);
+      const f32x4 v1 = *(const f32x4*)(st + r * kStagePitch + 4 * cc + 16);
+      *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                       pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+    }
+  }
+  // Split jobs of a decode with an FP8 output: seed the combine's running amax.
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
+}
+
+template <bool DIRECT, bool PREFETCH, int CP>
+__global__ __launch_bounds__(kThreads) void decode_kernel4t(
+    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
+    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds4tBytes];
+  decode4t_body<DIRECT, PREFETCH, CP>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a,
+                                      (int)blockIdx.x, smem);
+}
+
 // One launch for more jobs than compute units, with a short last round: its
 // first n_head workgroups run decode_kernel8p's body over jobs [0, n_head),
 // the rest the jobs from n_head on in CST parts (2: decode8h_body's head
@@ -2308,6 +2681,17 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
   if (a.h_q == 64 && cs == 1 && !kv_fp8 && !(DIRECT && a.out_dtype == kOutFp8)) {
     hipLaunchKernelGGL((decode_kernel8p<DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices, a.q,
                        a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
+    return hipGetLastError();
+  }
+  // 64 heads in 4 or 8 parts, bf16 pool: one head tile per 4-wave workgroup
+  // (8 parts: and half its columns), none repeating another tile's QK^T.
+  if (a.h_q == 64 && (cs == 4 || cs == 8) && !kv_fp8) {
+    if (cs == 4)
+      hipLaunchKernelGGL((decode_kernel4t<DIRECT, PREFETCH, 1>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
+                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
+    else
+      hipLaunchKernelGGL((decode_kernel4t<DIRECT, PREFETCH, 2>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
+                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
     return hipGetLastError();
   }
   // 64 heads in two parts, bf16 pool: head halves that do not repeat QK^T.
