@@ -459,7 +459,8 @@ def pmc_summary(dirs):
 
 def kernel_label(s_q, S, pool, cus=256):
     """Which attention kernel(s) a launch runs (mirrors sparse_mla_decode's choice for 64
-    heads): the 8-wave kernel when the jobs take 2, 4 or 8 column parts; with one part,
+    heads): with a bf16 pool the head-tile kernels at 2, 4 or 8 parts, else the 8-wave
+    kernel's column parts; with one part,
     the paired 8-wave kernel (bf16 pool) or the 4-wave kernel (FP8 pool); a last round
     that would fill at most half of the CUs takes more column parts, in the same launch
     (bf16 pool: the mixed kernel) or a second one."""
@@ -468,6 +469,8 @@ def kernel_label(s_q, S, pool, cus=256):
     mode = "partial" if S > 1 else "direct"
 
     def one(c):
+        if c in (4, 8) and pool == "bf16":
+            return f"decode_kernel4t<bf16 pool, {mode}, {c} parts: head tiles{' x column halves' if c == 8 else ''}>"
         if c == 2 and pool == "bf16":
             return f"decode_kernel8h<bf16 pool, {mode}, 2 head halves>"
         if c >= 2:

@@ -67,14 +67,15 @@ int32_t smla_choose_num_splits(int32_t s_q, int32_t h_q, int32_t topk, int32_t n
   if (s_q < 1 || h_q < 1 || topk < 1 || num_cus < 1) return 0;
   const int32_t n_blk = n_blocks_of(topk);
   // By compute units per token x = num_cus / s_q: S = x / 8 when x >= 40, 4
-  // when x >= 8, 2 when x >= 4, else 1 (capped at the block count).  Split
-  // jobs then run as 2, 4 or 8 column-part workgroups (sparse_mla_decode picks
-  // the most that fit one round over the CUs).  This was the best measured S,
-  // or within 2% of it, at every batch size of a sweep on a 256-CU MI355X
-  // (s_q = 1 ... 128): more splits shorten a small batch's critical path,
-  // but every split adds a partial to write and merge.
+  // when x >= 16, 2 when x >= 8, else 1 (capped at the block count).  Jobs
+  // then run as 2, 4 or 8 workgroups, each owning part of the heads or of the
+  // output columns (sparse_mla_decode picks the most that fit one round over
+  // the CUs).  This was the best measured S at every batch size of a sweep on
+  // a 256-CU MI355X (s_q = 1 ... 128, within 2% at s_q = 24): more splits
+  // shorten a small batch's critical path, but every split adds a partial to
+  // write and merge.
   const int64_t cus = num_cus, t = s_q;
-  int32_t s = cus >= 40 * t ? (int32_t)(cus / (8 * t)) : cus >= 8 * t ? 4 : cus >= 4 * t ? 2 : 1;
+  int32_t s = cus >= 40 * t ? (int32_t)(cus / (8 * t)) : cus >= 16 * t ? 4 : cus >= 8 * t ? 2 : 1;
   const int32_t cap = n_blk < SMLA_MAX_SPLITS ? n_blk : SMLA_MAX_SPLITS;
   if (s > cap) s = cap;
   return s < 1 ? 1 : s;
@@ -191,8 +192,8 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   a.out_dtype = p->out_dtype;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   // Few jobs leave most compute units idle: then 2, 4 or 8 workgroups share each
-  // job, one per part of the 512 output columns (each computes the scores).
-  // Not for a direct FP8 output, whose scale needs every column of a token.
+  // job, each owning part of its heads or of its 512 output columns.  Not for a
+  // direct FP8 output, whose scale needs every column of a token.
   const int64_t jobs = (int64_t)p->s_q * (direct ? 1 : num_splits);
   const int32_t cus = device_cus();
   a.col_parts = (direct && p->out_dtype == SMLA_OUT_FP8_E4M3) ? 1

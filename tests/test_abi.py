@@ -58,9 +58,9 @@ def test_choose_num_splits_properties():
             assert 1 <= s <= max(1, min(n_blk, 64))
             if s > 1:
                 assert 2 * s_q * s <= 256      # split jobs keep two column parts in one round
-            if s_q > 64:
+            if s_q > 32:
                 assert s == 1
-    for s_q, expect in ((1, 10), (4, 8), (6, 5), (8, 4), (16, 4), (32, 4), (48, 2), (64, 2), (65, 1), (96, 1), (384, 1)):
+    for s_q, expect in ((1, 10), (4, 8), (6, 5), (8, 4), (16, 4), (17, 2), (32, 2), (33, 1), (64, 1), (96, 1), (384, 1)):
         assert smla.smla_choose_num_splits(s_q, 64, 640, 256) == expect, s_q
     assert smla.smla_choose_num_splits(32, 64, 640, 512) == 4      # scales with the CU count
     assert smla.smla_choose_num_splits(8, 64, 640, 512) == 8
