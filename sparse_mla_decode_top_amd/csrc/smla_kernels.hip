@@ -2040,10 +2040,16 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8h(
 // LDS (as decode8h_body's head tile) and each accumulates every slot into its
 // quarter of the workgroup's columns.  One frame per head for the four.  The
 // workgroups of a job are 8 block ids apart (one XCD, one L2 for the rows).
+// KV_FP8: the e4m3 code tile is gathered (wave w: rows [16w, +16)), expanded
+// to the bf16 tile exactly, and the row scale multiplies the score after QK^T
+// and the weight before PV, as in decode_kernel8.
 // ---------------------------------------------------------------------------
-constexpr int kLds4tBytes = 2 * kTileBytes + kWaves * 1024;
+// LDS of decode4t_body: the two tiles (FP8: two code tiles and the bf16 tile),
+// the weight exchange (1 KB a wave), then the per-block row scales (FP8).
+constexpr int kLds4tScale = 2 * kTileBytes + kWaves * 1024;
+constexpr int kLds4tBytes = kLds4tScale + 2 * kBlk * 4;
 
-template <bool DIRECT, bool PREFETCH, int CP>
+template <bool KV_FP8, bool DIRECT, bool PREFETCH, int CP>
 __device__ __forceinline__ void decode4t_body(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, const DecodeArgs& a, int block, uint8_t* smem) {
@@ -2056,6 +2062,7 @@ __device__ __forceinline__ void decode4t_body(
   // Per wave: its block weights (4 a lane, MFMA output order): bf16 hi terms
   // at +0, lo terms at +512, 8 bytes a lane.
   uint8_t (*const s_pex)[1024] = reinterpret_cast<uint8_t (*)[1024]>(smem + 2 * kTileBytes);
+  float (*const s_scale)[kBlk] = reinterpret_cast<float (*)[kBlk]>(smem + kLds4tScale);   // [2][kBlk] (FP8)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;              // slot quarter of the scores; column quarter of the output
@@ -2092,15 +2099,25 @@ __device__ __forceinline__ void decode4t_body(
     const uint32_t tile_lds0 = lds_addr(s_tile);
     bool framed = false;              // workgroup-uniform: the frames are set
 
-    // Wave w gathers rows [16w, 16w + 16) as two groups of 8 (lanes 8k..8k+7
-    // one row, chunk (l & 7) ^ (row & 7) of each octet): 18 DMAs a wave, a
-    // masked row copying the zero row.
+    // Wave w gathers rows [16w, 16w + 16), a masked row copying the zero row.
+    // bf16: two groups of 8 (lanes 8k..8k+7 one row, chunk (l & 7) ^ (row & 7)
+    // of each octet), 18 DMAs a wave.  FP8: 4 lanes a row (chunk l & 3 of each
+    // quartet), 9 DMAs a wave.
     auto row_src = [&](int idx_lane, int grp) -> const uint8_t* {
+      if (KV_FP8) {
+        const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
+        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
+      }
       const int row_idx = __shfl(idx_lane, 16 * wave + 8 * grp + (lane >> 3));
       return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
              (((lane & 7) ^ rsw(lane >> 3)) * 16);
     };
     auto issue_gather = [&](int idx_lane, int buf) {
+      if (KV_FP8) {
+        dma_quartets(row_src(idx_lane, 0),
+                     __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kCodeTileBytes + wave * 1024));
+        return;
+      }
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp)
         dma_octets(row_src(idx_lane, grp),
@@ -2137,12 +2154,19 @@ __device__ __forceinline__ void decode4t_body(
     int idx_nxt = load_idx(job.b0 + 1);
     bool valid_cur = valid_of(idx_cur);
     if (first) {
-      // Q rows landed (issued first; block b0's 18 DMAs and, with the
+      // Q rows landed (issued first; block b0's 18 DMAs (FP8: 9) and, with the
       // look-ahead, the next index load stay in flight).
-      if (PREFETCH)
-        asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      if (KV_FP8) {
+        if (PREFETCH)
+          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else {
+        if (PREFETCH)
+          asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      }
       lds_barrier();
       const uint32_t qt = lds_addr(s_tile) + kQOffset;
 #pragma unroll
@@ -2151,32 +2175,57 @@ __device__ __forceinline__ void decode4t_body(
         qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
       }
     }
+    // FP8: block b0's row scales (stored at the top of the block loop).
+    float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
 
     for (int b = job.b0; b < job.b1; ++b) {
       const int cur = (b - job.b0) & 1;
       wait_vmem_all();          // this wave's share of block b has landed
+      if (KV_FP8 && wave == 0) s_scale[cur][lane] = sc_cur;
       lds_barrier();            // ... and every wave's; block b-1 and its weights fully consumed
       // slot s of the block is valid iff bit s is set (the same in every wave)
       const uint64_t vmask = __ballot(valid_cur);
       const uint32_t vquart = (uint32_t)(vmask >> (16 * wave));
       const bool blk_any = vmask != 0ull;
 
-      // Block b+1: one DMA per QK^T k-step (group 0's 9, then group 1's; masked
-      // rows and rows past the job's last block copy the zero row).
+      // Block b+1: bf16, one DMA per QK^T k-step (group 0's 9, then group 1's);
+      // FP8, one per k-step pair.  Masked rows and rows past the job's last
+      // block copy the zero row.
       bool valid_nxt = false;
+      float sc_nxt = 0.f;
       const uint8_t* gsrc0 = g_zero_row;
       const uint8_t* gsrc1 = g_zero_row;
       uint32_t gbase0 = 0u, gbase1 = 0u;
       if (PREFETCH) {
         idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
         valid_nxt = valid_of(idx_nxt);
+        if (KV_FP8 && wave == 0 && valid_nxt) sc_nxt = a.kv_scale[idx_nxt];
         gsrc0 = row_src(idx_nxt, 0);
-        gsrc1 = row_src(idx_nxt, 1);
-        gbase0 = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + (2 * wave) * 1024);
-        gbase1 = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + (2 * wave + 1) * 1024);
+        if (KV_FP8) {
+          gbase0 = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kCodeTileBytes + wave * 1024);
+        } else {
+          gsrc1 = row_src(idx_nxt, 1);
+          gbase0 = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + (2 * wave) * 1024);
+          gbase1 = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + (2 * wave + 1) * 1024);
+        }
       }
       auto gather_dma = [&](const int d) __attribute__((always_inline)) {
         if (!PREFETCH) return;
+        if (KV_FP8) {
+          if ((d & 1) == 0) return;
+          switch (d >> 1) {
+            case 0: dma_one<4096, 64, 0>(gsrc0, gbase0); break;
+            case 1: dma_one<4096, 64, 1>(gsrc0, gbase0); break;
+            case 2: dma_one<4096, 64, 2>(gsrc0, gbase0); break;
+            case 3: dma_one<4096, 64, 3>(gsrc0, gbase0); break;
+            case 4: dma_one<4096, 64, 4>(gsrc0, gbase0); break;
+            case 5: dma_one<4096, 64, 5>(gsrc0, gbase0); break;
+            case 6: dma_one<4096, 64, 6>(gsrc0, gbase0); break;
+            case 7: dma_one<4096, 64, 7>(gsrc0, gbase0); break;
+            default: dma_one<4096, 64, 8>(gsrc0, gbase0); break;
+          }
+          return;
+        }
         switch (d) {
           case 0: dma_one<8192, 128, 0>(gsrc0, gbase0); break;
           case 1: dma_one<8192, 128, 1>(gsrc0, gbase0); break;
@@ -2200,7 +2249,32 @@ __device__ __forceinline__ void decode4t_body(
       };
       const int idx_after = load_idx(b + 2);
 
-      const uint32_t tl = lds_addr(s_tile + cur * kTileBytes);
+      const uint8_t* tile;
+      if (!KV_FP8) {
+        tile = s_tile + cur * kTileBytes;
+      } else {
+        // Expand block b's e4m3 codes into the bf16 tile (exact conversion).
+        uint8_t* btile = s_tile + 2 * kCodeTileBytes;
+        const uint8_t* ctile = s_tile + cur * kCodeTileBytes;
+#pragma unroll 3
+        for (int j = 0; j < 18; ++j) {
+          const int p = j * kThreads + tid;
+          const int o = p >> 9, r = (p >> 3) & 63;
+          const int c = 8 * o + ((p & 7) ^ rsw(r));
+          const int cc = c >> 1;
+          const u32x2 codes =
+              *(const u32x2*)(ctile + ((cc >> 2) * 256 + r * 4 + (cc & 3)) * 16 + (c & 1) * 8);
+          u32x4 ov;
+          ov[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
+          ov[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
+          ov[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
+          ov[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
+          *(u32x4*)(btile + p * 16) = ov;
+        }
+        lds_barrier();
+        tile = btile;
+      }
+      const uint32_t tl = lds_addr(tile);
       const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
                                  opaque(tl + kb1 + 65536)};
       auto kfrag = [&](int ks, int st) -> bf16x8 {
@@ -2243,9 +2317,14 @@ __device__ __forceinline__ void decode4t_body(
 #pragma unroll
       for (int a0 = 0; a0 < kAV; ++a0) vf[a0] = vfrag(a0 % kCt, a0 / kCt);
       const uint32_t vbits = vquart >> (4 * G);
+      f32x4 rsc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (KV_FP8) rsc = *(const f32x4*)&s_scale[cur][16 * wave + 4 * G];
       float tv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tv[i] = fmaf(sacc[i], scale_log2, ((vbits >> i) & 1u) ? 0.f : kMaskedScore);
+      for (int i = 0; i < 4; ++i) {
+        const float bias = ((vbits >> i) & 1u) ? 0.f : kMaskedScore;
+        tv[i] = KV_FP8 ? fmaf(sacc[i] * scale_log2, rsc[i], bias) : fmaf(sacc[i], scale_log2, bias);
+      }
       float m = fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3]));
       m = rows_max(m);
       m_seen = fmaxf(m_seen, m);
@@ -2265,8 +2344,9 @@ __device__ __forceinline__ void decode4t_body(
         const float tt = tv[e];
         const float fl = floorf(tt);
         const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
-        const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+        float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
         l_run += p;
+        if (KV_FP8) p *= rsc[e];
         pv[e] = p;
       }
       uint32_t ph[2], pl[2];
@@ -2302,6 +2382,7 @@ __device__ __forceinline__ void decode4t_body(
       }
 
       valid_cur = valid_nxt;
+      sc_cur = sc_nxt;
       idx_nxt = idx_after;
     }
     wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
@@ -2395,13 +2476,13 @@ __device__ __forceinline__ void decode4t_body(
   if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
 }
 
-template <bool DIRECT, bool PREFETCH, int CP>
+template <bool KV_FP8, bool DIRECT, bool PREFETCH, int CP>
 __global__ __launch_bounds__(kThreads) void decode_kernel4t(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds4tBytes];
-  decode4t_body<DIRECT, PREFETCH, CP>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a,
-                                      (int)blockIdx.x, smem);
+  decode4t_body<KV_FP8, DIRECT, PREFETCH, CP>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a,
+                                              (int)blockIdx.x, smem);
 }
 
 // One launch for more jobs than compute units, with a short last round: its
@@ -2683,15 +2764,21 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
                        a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
     return hipGetLastError();
   }
-  // 64 heads in 4 or 8 parts, bf16 pool: one head tile per 4-wave workgroup
-  // (8 parts: and half its columns), none repeating another tile's QK^T.
-  if (a.h_q == 64 && (cs == 4 || cs == 8) && !kv_fp8) {
-    if (cs == 4)
-      hipLaunchKernelGGL((decode_kernel4t<DIRECT, PREFETCH, 1>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
-                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
+  // 64 heads in 4 or 8 parts: one head tile per 4-wave workgroup (8 parts:
+  // and half its columns), none repeating another tile's QK^T.
+  if (a.h_q == 64 && (cs == 4 || cs == 8)) {
+#define SMLA_LAUNCH_4T(FP8, CPV)                                                                             \
+  hipLaunchKernelGGL((decode_kernel4t<FP8, DIRECT, PREFETCH, CPV>), grid, dim3(kThreads), 0, stream, a.indices, \
+                     a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a)
+    if (kv_fp8 && cs == 4)
+      SMLA_LAUNCH_4T(true, 1);
+    else if (kv_fp8)
+      SMLA_LAUNCH_4T(true, 2);
+    else if (cs == 4)
+      SMLA_LAUNCH_4T(false, 1);
     else
-      hipLaunchKernelGGL((decode_kernel4t<DIRECT, PREFETCH, 2>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
-                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
+      SMLA_LAUNCH_4T(false, 2);
+#undef SMLA_LAUNCH_4T
     return hipGetLastError();
   }
   // 64 heads in two parts, bf16 pool: head halves that do not repeat QK^T.
