@@ -471,8 +471,8 @@ def kernel_label(s_q, S, pool, cus=256):
     def one(c):
         if c in (4, 8):
             return f"decode_kernel4t<{pool} pool, {mode}, {c} parts: head tiles{' x column halves' if c == 8 else ''}>"
-        if c == 2 and pool == "bf16":
-            return f"decode_kernel8h<bf16 pool, {mode}, 2 head halves>"
+        if c == 2:
+            return f"decode_kernel8h<{pool} pool, {mode}, 2 head halves>"
         if c >= 2:
             return f"decode_kernel8<{pool} pool, {mode}, {c} column parts>"
         name = "decode_kernel8p" if pool == "bf16" else "decode_kernel"

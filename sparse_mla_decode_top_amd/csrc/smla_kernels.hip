@@ -1686,12 +1686,17 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
 // bf16 weights through LDS, and each accumulates every slot of the block into
 // its own quarter of the columns (128).  The four share one integer frame per
 // head, agreed on as in decode_kernel8p.  The job's two workgroups are 8 block
-// ids apart (one XCD, one L2 for the gathered rows).
+// ids apart (one XCD, one L2 for the gathered rows).  KV_FP8: waves 0-3
+// gather the e4m3 code tile (wave w: rows [16w, +16)), all waves expand it to
+// the bf16 tile, and the row scale multiplies the score after QK^T and the
+// weight before PV, as in decode_kernel8.
 // ---------------------------------------------------------------------------
-// LDS of decode8h_body: the two tiles, then the weight exchange (1 KB a wave).
-constexpr int kLds8hBytes = 2 * kTileBytes + kWaves8 * 1024;
+// LDS of decode8h_body: the two tiles (FP8: two code tiles and the bf16
+// tile), the weight exchange (1 KB a wave), then the per-block row scales.
+constexpr int kLds8hScale = 2 * kTileBytes + kWaves8 * 1024;
+constexpr int kLds8hBytes = kLds8hScale + 2 * kBlk * 4;
 
-template <bool DIRECT, bool PREFETCH>
+template <bool KV_FP8, bool DIRECT, bool PREFETCH>
 __device__ __forceinline__ void decode8h_body(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, const DecodeArgs& a, int block, uint8_t* smem) {
@@ -1702,6 +1707,7 @@ __device__ __forceinline__ void decode8h_body(
   // Per wave: its block weights (4 a lane, MFMA output order): bf16 hi terms
   // at +0, lo terms at +512, 8 bytes a lane.
   uint8_t (*const s_pex)[1024] = reinterpret_cast<uint8_t (*)[1024]>(smem + 2 * kTileBytes);
+  float (*const s_scale)[kBlk] = reinterpret_cast<float (*)[kBlk]>(smem + kLds8hScale);   // [2][kBlk] (FP8)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -1740,14 +1746,26 @@ __device__ __forceinline__ void decode8h_body(
     const uint32_t tile_lds0 = lds_addr(s_tile);
     bool framed = false;              // workgroup-uniform: the frames are set
 
-    // Wave w gathers rows [8w, 8w + 8) (as decode_kernel8p): 9 DMAs a wave,
-    // a masked row copying the zero row.
-    auto issue_gather = [&](int idx_lane, int buf) {
+    // bf16: wave w gathers rows [8w, 8w + 8) (as decode_kernel8p); FP8: waves
+    // 0-3 gather rows [16w, 16w + 16) of the code tile, 4 lanes a row.  9 DMAs
+    // a gathering wave, a masked row copying the zero row.
+    const bool gathers = !KV_FP8 || wave < 4;
+    auto row_src = [&](int idx_lane) -> const uint8_t* {
+      if (KV_FP8) {
+        const int row_idx = __shfl(idx_lane, 16 * (wave & 3) + (lane >> 2));
+        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
+      }
       const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
-      const uint32_t lds_base = tile_lds0 + buf * kTileBytes + wave * 1024;
-      const uint8_t* src = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-                           (((lane & 7) ^ rsw(lane >> 3)) * 16);
-      dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
+      return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+             (((lane & 7) ^ rsw(lane >> 3)) * 16);
+    };
+    auto issue_gather = [&](int idx_lane, int buf) {
+      if (!KV_FP8) {
+        dma_octets(row_src(idx_lane), __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kTileBytes + wave * 1024));
+      } else if (gathers) {
+        dma_quartets(row_src(idx_lane),
+                     __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kCodeTileBytes + wave * 1024));
+      }
     };
 
     // per-lane LDS byte offsets of the operand reads (the tile layout above)
@@ -1780,12 +1798,19 @@ __device__ __forceinline__ void decode8h_body(
     int idx_nxt = load_idx(job.b0 + 1);
     bool valid_cur = valid_of(idx_cur);
     if (first) {
-      // Q rows landed (issued first; block b0's 9 DMAs and, with the
-      // look-ahead, the next index load stay in flight).
-      if (PREFETCH)
-        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      // Q rows landed (issued first; block b0's 9 DMAs of a gathering wave
+      // and, with the look-ahead, the next index load stay in flight).
+      if (gathers) {
+        if (PREFETCH)
+          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else {
+        if (PREFETCH)
+          asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       lds_barrier();
       const uint32_t qt = lds_addr(s_tile) + kQOffset + hq * 2048;
 #pragma unroll
@@ -1794,10 +1819,13 @@ __device__ __forceinline__ void decode8h_body(
         qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
       }
     }
+    // FP8: block b0's row scales (stored at the top of the block loop).
+    float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
 
     for (int b = job.b0; b < job.b1; ++b) {
       const int cur = (b - job.b0) & 1;
       wait_vmem_all();          // this wave's share of block b has landed
+      if (KV_FP8 && wave == 0) s_scale[cur][lane] = sc_cur;
       lds_barrier();            // ... and every wave's; block b-1 and its weights fully consumed
       // slot s of the block is valid iff bit s is set (the same in every wave)
       const uint64_t vmask = __ballot(valid_cur);
@@ -1807,33 +1835,60 @@ __device__ __forceinline__ void decode8h_body(
       // Block b+1: one DMA per QK^T k-step pair (masked rows and rows past the
       // job's last block copy the zero row).
       bool valid_nxt = false;
+      float sc_nxt = 0.f;
       const uint8_t* gsrc = g_zero_row;
       uint32_t gbase = 0u;
       if (PREFETCH) {
         idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
         valid_nxt = valid_of(idx_nxt);
-        const int row_idx = __shfl(idx_nxt, 8 * wave + (lane >> 3));
-        gsrc = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-               (((lane & 7) ^ rsw(lane >> 3)) * 16);
-        gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + wave * 1024);
+        if (KV_FP8 && wave == 0 && valid_nxt) sc_nxt = a.kv_scale[idx_nxt];
+        gsrc = row_src(idx_nxt);
+        gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * (KV_FP8 ? kCodeTileBytes : kTileBytes) +
+                                               (KV_FP8 ? (wave & 3) : wave) * 1024);
       }
       auto gather_dma = [&](const int d) __attribute__((always_inline)) {
-        if (!PREFETCH) return;
+        if (!PREFETCH || !gathers) return;
+        constexpr int L = KV_FP8 ? 4096 : 8192, Gs = KV_FP8 ? 64 : 128;
         switch (d) {
-          case 0: dma_one<8192, 128, 0>(gsrc, gbase); break;
-          case 1: dma_one<8192, 128, 1>(gsrc, gbase); break;
-          case 2: dma_one<8192, 128, 2>(gsrc, gbase); break;
-          case 3: dma_one<8192, 128, 3>(gsrc, gbase); break;
-          case 4: dma_one<8192, 128, 4>(gsrc, gbase); break;
-          case 5: dma_one<8192, 128, 5>(gsrc, gbase); break;
-          case 6: dma_one<8192, 128, 6>(gsrc, gbase); break;
-          case 7: dma_one<8192, 128, 7>(gsrc, gbase); break;
-          default: dma_one<8192, 128, 8>(gsrc, gbase); break;
+          case 0: dma_one<L, Gs, 0>(gsrc, gbase); break;
+          case 1: dma_one<L, Gs, 1>(gsrc, gbase); break;
+          case 2: dma_one<L, Gs, 2>(gsrc, gbase); break;
+          case 3: dma_one<L, Gs, 3>(gsrc, gbase); break;
+          case 4: dma_one<L, Gs, 4>(gsrc, gbase); break;
+          case 5: dma_one<L, Gs, 5>(gsrc, gbase); break;
+          case 6: dma_one<L, Gs, 6>(gsrc, gbase); break;
+          case 7: dma_one<L, Gs, 7>(gsrc, gbase); break;
+          default: dma_one<L, Gs, 8>(gsrc, gbase); break;
         }
       };
       const int idx_after = load_idx(b + 2);
 
-      const uint32_t tl = lds_addr(s_tile + cur * kTileBytes);
+      const uint8_t* tile;
+      if (!KV_FP8) {
+        tile = s_tile + cur * kTileBytes;
+      } else {
+        // Expand block b's e4m3 codes into the bf16 tile (exact conversion).
+        uint8_t* btile = s_tile + 2 * kCodeTileBytes;
+        const uint8_t* ctile = s_tile + cur * kCodeTileBytes;
+#pragma unroll 3
+        for (int j = 0; j < 9; ++j) {
+          const int p = j * kThreads8 + tid;
+          const int o = p >> 9, r = (p >> 3) & 63;
+          const int c = 8 * o + ((p & 7) ^ rsw(r));
+          const int cc = c >> 1;
+          const u32x2 codes =
+              *(const u32x2*)(ctile + ((cc >> 2) * 256 + r * 4 + (cc & 3)) * 16 + (c & 1) * 8);
+          u32x4 ov;
+          ov[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
+          ov[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
+          ov[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
+          ov[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
+          *(u32x4*)(btile + p * 16) = ov;
+        }
+        lds_barrier();
+        tile = btile;
+      }
+      const uint32_t tl = lds_addr(tile);
       const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
                                  opaque(tl + kb1 + 65536)};
       auto kfrag = [&](int ks, int st) -> bf16x8 {
@@ -1874,9 +1929,14 @@ __device__ __forceinline__ void decode8h_body(
 #pragma unroll
       for (int a0 = 0; a0 < kAheadV; ++a0) vf[a0] = vfrag(a0, 0);
       const uint32_t vbits = vquart >> (4 * G);
+      f32x4 rsc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (KV_FP8) rsc = *(const f32x4*)&s_scale[cur][16 * sq + 4 * G];
       float tv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tv[i] = fmaf(sacc[i], scale_log2, ((vbits >> i) & 1u) ? 0.f : kMaskedScore);
+      for (int i = 0; i < 4; ++i) {
+        const float bias = ((vbits >> i) & 1u) ? 0.f : kMaskedScore;
+        tv[i] = KV_FP8 ? fmaf(sacc[i] * scale_log2, rsc[i], bias) : fmaf(sacc[i], scale_log2, bias);
+      }
       float m = fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3]));
       m = rows_max(m);
       m_seen = fmaxf(m_seen, m);
@@ -1896,8 +1956,9 @@ __device__ __forceinline__ void decode8h_body(
         const float tt = tv[e];
         const float fl = floorf(tt);
         const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
-        const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+        float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
         l_run += p;
+        if (KV_FP8) p *= rsc[e];
         pv[e] = p;
       }
       uint32_t ph[2], pl[2];
@@ -1934,6 +1995,7 @@ __device__ __forceinline__ void decode8h_body(
       }
 
       valid_cur = valid_nxt;
+      sc_cur = sc_nxt;
       idx_nxt = idx_after;
     }
     wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
@@ -2022,13 +2084,13 @@ __device__ __forceinline__ void decode8h_body(
   if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
 }
 
-template <bool DIRECT, bool PREFETCH>
+template <bool KV_FP8, bool DIRECT, bool PREFETCH>
 __global__ __launch_bounds__(kThreads8) void decode_kernel8h(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds8hBytes];
-  decode8h_body<DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a, (int)blockIdx.x,
-                                  smem);
+  decode8h_body<KV_FP8, DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a,
+                                          (int)blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2501,8 +2563,8 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8m(
   if (block < n_head)
     decode8p_body<DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, 0, a, block, smem);
   else if constexpr (CST == 2)
-    decode8h_body<DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, n_head, a, block - n_head,
-                                    smem);
+    decode8h_body<false, DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, n_head, a,
+                                           block - n_head, smem);
   else
     decode8_body<false, DIRECT, CST, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, n_head, a,
                                                block - n_head, smem);
@@ -2781,10 +2843,14 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
 #undef SMLA_LAUNCH_4T
     return hipGetLastError();
   }
-  // 64 heads in two parts, bf16 pool: head halves that do not repeat QK^T.
-  if (a.h_q == 64 && cs == 2 && !kv_fp8) {
-    hipLaunchKernelGGL((decode_kernel8h<DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices, a.q,
-                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
+  // 64 heads in two parts: head halves that do not repeat QK^T.
+  if (a.h_q == 64 && cs == 2) {
+    if (kv_fp8)
+      hipLaunchKernelGGL((decode_kernel8h<true, DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices,
+                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
+    else
+      hipLaunchKernelGGL((decode_kernel8h<false, DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices,
+                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
     return hipGetLastError();
   }
   // 64 heads in 2, 4 or 8 column parts: the 8-wave kernel (two waves per SIMD).
