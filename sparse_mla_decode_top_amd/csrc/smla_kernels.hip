@@ -7,6 +7,18 @@
 // the largest LSE) and cudnn-frontend PR #768 (near-equal block ranges with
 // the remainder on the leading splits; an empty split is O = 0, LSE = -inf).
 //
+// Kernels, by launch (64 heads unless stated; CS = workgroups a job takes):
+//   * decode_kernel8p (CS = 1, bf16 pool): 8 waves, all heads and columns.
+//   * decode_kernel8h (CS = 2): 8 waves, half of the heads each.
+//   * decode_kernel4t (CS = 4 or 8): 4 waves, one 16-head tile each (CS = 8:
+//     and half its columns).
+//   * decode_kernel8m: a mixed launch for more jobs than compute units.
+//   * decode_kernel (fewer heads, or CS = 1 with an FP8 pool or a direct FP8
+//     output): 4 waves, each workgroup 512 / CS output columns of all heads.
+// The head-part kernels let no workgroup repeat another's QK^T.  The notes
+// below describe decode_kernel; the others share its tile layout, gather,
+// softmax frame and partial protocol.
+//
 // decode kernel: CS in {1, 2, 4, 8} workgroups of 4 wave64s per (token,
 // split) job, each owning 512 / CS output columns (all of them compute the
 // scores; few jobs then still occupy many compute units).
@@ -39,18 +51,19 @@
 //     hi + lo carries p to about 2^-17 relative.
 //   * Outputs are staged through LDS and stored in whole-line pieces.
 //
-// decode_kernel8: the same job with 8 waves, two per SIMD, for 64 heads in 2,
-// 4 or 8 column parts.  The two waves on a SIMD own the same 16 heads and
-// split each block's slots, so the hardware overlaps one's softmax and LDS
-// reads with the other's MFMAs; the two slot halves of a head merge in the
-// epilogue as two splits would.
+// decode8_body (the 8-wave column-part layout; now the 4/8-part tail of the
+// mixed launch): 8 waves, two per SIMD, for 64 heads in 2, 4 or 8 column
+// parts.  The two waves on a SIMD own the same 16 heads and split each
+// block's slots, so the hardware overlaps one's softmax and LDS reads with
+// the other's MFMAs; the two slot halves of a head merge in the epilogue as
+// two splits would.
 //
-// decode_kernel8p: 8 waves for 64 heads in one column part (bf16 pool).  The
-// waves of a pair score one slot half each, trade their weights through LDS
-// and accumulate every slot into their own half of the columns, under one
+// decode_kernel8p / 8h / 4t: the waves that share a head tile score a part
+// of each block's slots each, trade their bf16 weights through LDS and
+// accumulate every slot into their own part of the columns, under one
 // shared frame per head.  With more jobs than compute units, a last round
-// that fills at most half of them takes 2, 4 or 8 column parts:
-// decode_kernel8m runs both bodies in one launch.
+// that fills at most half of them takes 2, 4 or 8 parts: decode_kernel8m
+// runs both in one launch.
 //
 // combine kernel: split-major partials -> final output (+ sink, cast).
 
@@ -868,7 +881,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 constexpr int kWaves8 = 8;
 constexpr int kThreads8 = 64 * kWaves8;
 
-// LDS of decode_kernel8: the two tiles, then the per-block scale and bias rows,
+// LDS of decode8_body: the two tiles, then the per-block scale and bias rows,
 // the epilogue's frame / denominator exchange, the LSEs and the restart flag.
 constexpr int kLds8Scale = 2 * kTileBytes;
 constexpr int kLds8Bias = kLds8Scale + 2 * kBlk * 4;
@@ -877,8 +890,10 @@ constexpr int kLds8Lse = kLds8Ml + 2 * 2 * 64 * 4;
 constexpr int kLds8Restart = kLds8Lse + 64 * 4;
 constexpr int kLds8Bytes = kLds8Restart + 16;
 
-// The body of decode_kernel8 for workgroup `block` of its launch, on the LDS at
-// `smem` (kLds8Bytes); a kernel of its own, or one half of a mixed launch.
+// The body of the 8-wave column-part layout for workgroup `block` of its
+// launch, on the LDS at `smem` (kLds8Bytes).  The head-tile kernels have
+// replaced it as a kernel of its own; it runs the 4- and 8-part tail of the
+// mixed launch (512-thread workgroups).
 template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
 __device__ __forceinline__ void decode8_body(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
@@ -1291,19 +1306,11 @@ __device__ __forceinline__ void decode8_body(
   if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
 }
 
-template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
-__global__ __launch_bounds__(kThreads8) void decode_kernel8(
-    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
-    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds8Bytes];
-  decode8_body<KV_FP8, DIRECT, CS, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a,
-                                             (int)blockIdx.x, smem);
-}
 
 // ---------------------------------------------------------------------------
 // decode_kernel8p: one 8-wave workgroup per job that owns all 512 output
 // columns (64 heads, bf16 pool), for launches with a single column part.
-// As in decode_kernel8, the two waves on a SIMD own the same 16 heads and
+// As in decode8_body, the two waves on a SIMD own the same 16 heads and
 // each scores one 32-slot half of every block.  Here they trade their bf16
 // weights through LDS, and each wave accumulates every slot of the block into
 // its own half of the columns (256): 64 accumulator registers a wave, which
@@ -1679,7 +1686,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
 
 // ---------------------------------------------------------------------------
 // decode8h_body: a job in two workgroups that each own 32 of its 64 heads and
-// all 512 output columns (bf16 pool).  Unlike decode_kernel8's two column
+// all 512 output columns.  Unlike decode8_body's two column
 // parts, the two head parts do not repeat each other's QK^T.  Wave w owns
 // head tile w & 1 (heads 32 part + 16 (w & 1) .. +15) and scores slot quarter
 // w >> 1 (16 slots) of every block; the four waves of a head tile trade their
@@ -1689,7 +1696,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
 // ids apart (one XCD, one L2 for the gathered rows).  KV_FP8: waves 0-3
 // gather the e4m3 code tile (wave w: rows [16w, +16)), all waves expand it to
 // the bf16 tile, and the row scale multiplies the score after QK^T and the
-// weight before PV, as in decode_kernel8.
+// weight before PV, as in decode8_body.
 // ---------------------------------------------------------------------------
 // LDS of decode8h_body: the two tiles (FP8: two code tiles and the bf16
 // tile), the weight exchange (1 KB a wave), then the per-block row scales.
@@ -2104,7 +2111,7 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8h(
 // workgroups of a job are 8 block ids apart (one XCD, one L2 for the rows).
 // KV_FP8: the e4m3 code tile is gathered (wave w: rows [16w, +16)), expanded
 // to the bf16 tile exactly, and the row scale multiplies the score after QK^T
-// and the weight before PV, as in decode_kernel8.
+// and the weight before PV, as in decode8_body.
 // ---------------------------------------------------------------------------
 // LDS of decode4t_body: the two tiles (FP8: two code tiles and the bf16 tile),
 // the weight exchange (1 KB a wave), then the per-block row scales (FP8).
@@ -2550,9 +2557,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel4t(
 // One launch for more jobs than compute units, with a short last round: its
 // first n_head workgroups run decode_kernel8p's body over jobs [0, n_head),
 // the rest the jobs from n_head on in CST parts (2: decode8h_body's head
-// halves; 4 or 8: decode_kernel8's column parts).  The tail's workgroups start as soon as compute units free up,
-// with no kernel boundary in between.  n_head is a multiple of 8, so the tail
-// keeps decode_kernel8's XCD grouping of a job's column parts.
+// halves; 4 or 8: decode8_body's column parts).  The tail's workgroups start
+// as soon as compute units free up, with no kernel boundary in between.
+// n_head is a multiple of 8, so the tail keeps the XCD grouping of a job's
+// parts.
 template <bool DIRECT, bool PREFETCH, int CST>
 __global__ __launch_bounds__(kThreads8) void decode_kernel8m(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
@@ -2853,15 +2861,9 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
                          a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
     return hipGetLastError();
   }
-  // 64 heads in 2, 4 or 8 column parts: the 8-wave kernel (two waves per SIMD).
-  const bool eight = a.h_q == 64 && cs >= 2;
-  if (eight && cs == 8)
-    SMLA_LAUNCH(decode_kernel8, kThreads8, 8);
-  else if (eight && cs == 4)
-    SMLA_LAUNCH(decode_kernel8, kThreads8, 4);
-  else if (eight)
-    SMLA_LAUNCH(decode_kernel8, kThreads8, 2);
-  else if (cs == 8)
+  // Fewer heads, or one part with an FP8 pool or a direct FP8 output: the
+  // 4-wave column-part kernel.
+  if (cs == 8)
     SMLA_LAUNCH(decode_kernel, kThreads, 8);
   else if (cs == 4)
     SMLA_LAUNCH(decode_kernel, kThreads, 4);

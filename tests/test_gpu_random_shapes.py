@@ -1,11 +1,13 @@
 """GPU parity over seeded random shapes: token counts, head counts, list lengths,
 pool sizes, split counts, padding, sink, pool and output formats drawn at
-random, so that every kernel the library picks (the 8-wave and the 4-wave
-attention kernels at 1, 2, 4 or 8 column parts, with and without the look-ahead
-gather) and both paths meet the oracle bars on shapes no fixed test names.  A
-second set draws more jobs than compute units (s_q from 129 to 390): the
-one-part kernel whose wave pairs trade weights, and the second launch that takes
-a last round of at most half the compute units with more column parts.
+random, so that every kernel the library picks (for 64 heads: the one-part
+kernel, the head halves at 2 parts and the head tiles at 4 or 8; for fewer heads
+the 4-wave column-part kernel at 1, 2, 4 or 8 parts; each with and without the
+look-ahead gather) and both paths meet the oracle bars on shapes no fixed test
+names.  A second set draws more jobs than compute units (s_q from 129 to 390):
+the one-part kernel whose wave pairs trade weights, and the last round of at
+most half the compute units in more parts (in the same launch for a bf16 pool
+and 64 heads, else in a second one).
 """
 import numpy as np
 import pytest
