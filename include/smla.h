@@ -104,7 +104,11 @@ typedef struct {
  *     epilogue.  `out` is required.
  *   - o_accum and lse_accum given: every job writes its partials (the FlashMLA
  *     partial protocol); if `out` is given the combine runs after it on the same
- *     stream, otherwise the caller combines (combine_splits).
+ *     stream, otherwise the caller combines (combine_splits).  With an FP8
+ *     `out`, the combine's first pass then stages the merged rows in split 0 of
+ *     o_accum for its second: on return, o_accum[0] holds the final O in f32
+ *     (sink applied, before the cast) instead of split 0's partial; the other
+ *     splits and lse_accum keep their partials.
  *   - num_splits > 1 with either accumulator NULL: SMLA_ERR_MISSING_WORKSPACE.
  *   - Giving only one of o_accum / lse_accum: SMLA_ERR_MISSING_WORKSPACE.
  */

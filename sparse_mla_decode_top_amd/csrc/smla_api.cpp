@@ -117,10 +117,12 @@ smla_status smla_validate(const smla_params* p, const void* q, const void* kv_po
 namespace {
 
 // The combine launch sequence; scale_ready: an FP8 output's out_scale already
-// holds the combine's starting value (-0.0).
+// holds the combine's starting value (-0.0).  merged: where an FP8 output's
+// amax pass leaves the merged rows for the encode pass (nullptr: the encode
+// pass merges the splits again).
 smla_status run_combine(const smla_params* p, int32_t num_splits, const float* o_accum, const float* lse_accum,
                         const float* sink, void* out, float* out_scale, float* lse_out, void* stream,
-                        bool scale_ready) {
+                        bool scale_ready, float* merged) {
   smla_status st = check_common_shape(p, num_splits);
   if (st != SMLA_OK) return st;
   if (o_accum == nullptr || lse_accum == nullptr) return SMLA_ERR_MISSING_WORKSPACE;
@@ -148,6 +150,7 @@ smla_status run_combine(const smla_params* p, int32_t num_splits, const float* o
   const int32_t cus = device_cus();
   a.heads_per_wg = 4 * rows <= cus ? -1 : rows <= 2 * cus ? 0 : 4;
   a.scale_ready = scale_ready ? 1 : 0;
+  a.merged = merged;
   return smla::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
@@ -158,7 +161,7 @@ extern "C" {
 smla_status combine_splits(const smla_params* p, int32_t num_splits, const float* o_accum,
                            const float* lse_accum, const float* sink, void* out, float* out_scale,
                            float* lse_out, void* stream) {
-  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, false);
+  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, false, nullptr);
 }
 
 smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* kv_pool, const float* kv_scale,
@@ -208,7 +211,11 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   }
   if (smla::launch_decode_partial(a, fp8, hs) != hipSuccess) return SMLA_ERR_HIP;
   if (out == nullptr) return SMLA_OK;   // partial-only: the caller combines
-  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, seed_scale);
+  // An FP8 output's two passes: the amax pass stages each merged row in split
+  // 0 of o_accum, whose partials it has just read, so the encode pass reads one
+  // row instead of num_splits.
+  float* merged = p->out_dtype == SMLA_OUT_FP8_E4M3 ? o_accum : nullptr;
+  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, seed_scale, merged);
 }
 
 }  // extern "C"

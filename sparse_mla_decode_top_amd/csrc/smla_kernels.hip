@@ -2731,13 +2731,46 @@ __device__ __forceinline__ float abs_max4(f32x4 v) {
   return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 }
 
+// The staged merged row of an FP8 output (a.merged), in merge_head's lane
+// layout: the amax pass stores what it merged, the encode pass loads it back
+// (the same fp32 values, so the codes equal a second merge's).
+template <int PARTS>
+__device__ __forceinline__ void store_merged(const CombineArgs& a, int t, int h, int col0, const Merged& m) {
+  const int lane = threadIdx.x & 63;
+  float* dst = a.merged + ((int64_t)t * a.h_q + h) * 512 + col0 + (PARTS == 4 ? 2 : 4) * lane;
+  if (PARTS == 4) {
+    *(f32x2*)dst = f32x2{m.lo[0], m.lo[1]};
+  } else {
+    *(f32x4*)dst = m.lo;
+    if (PARTS == 1) *(f32x4*)(dst + 256) = m.hi;
+  }
+}
+
+template <int PARTS>
+__device__ __forceinline__ Merged load_merged(const CombineArgs& a, int t, int h, int col0) {
+  const int lane = threadIdx.x & 63;
+  const float* src = a.merged + ((int64_t)t * a.h_q + h) * 512 + col0 + (PARTS == 4 ? 2 : 4) * lane;
+  Merged m;
+  m.hi = f32x4{0.f, 0.f, 0.f, 0.f};
+  m.lse = 0.f;                          // not used by the encode pass
+  if (PARTS == 4) {
+    const f32x2 x = *(const f32x2*)src;
+    m.lo = f32x4{x[0], x[1], 0.f, 0.f};
+  } else {
+    m.lo = *(const f32x4*)src;
+    if (PARTS == 1) m.hi = *(const f32x4*)(src + 256);
+  }
+  return m;
+}
+
 // HW waves per workgroup, whose amaxes meet in LDS, so a token sees fewer
 // atomics.  PARTS = 1: one wave per (token, head) row, HW = 4 spreading a small
 // batch over more compute units or HW = 16 keeping the atomics of a large one
 // few.  PARTS = 2 or 4 (HW = 4): one wave per 1 / PARTS of a row (wave u of
 // the grid: row u / PARTS, part u % PARTS); a token's h_q * PARTS waves fill
-// whole workgroups, so a workgroup never spans two tokens.
-template <int HW, int CHUNK, int PARTS = 1>
+// whole workgroups, so a workgroup never spans two tokens.  STAGED: store the
+// merged rows to a.merged for the encode pass.
+template <int HW, int CHUNK, int PARTS, bool STAGED>
 __global__ __launch_bounds__(64 * HW) void combine_fp8_amax_kernel(CombineArgs a) {
   __shared__ float s_amax[HW];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -2761,6 +2794,9 @@ __global__ __launch_bounds__(64 * HW) void combine_fp8_amax_kernel(CombineArgs a
     const Merged m = merge_head<CHUNK, PARTS>(a, t, h, col0);
     amax = wave_max(PARTS == 1 ? fmaxf(abs_max4(m.lo), abs_max4(m.hi)) : abs_max4(m.lo));
     if (lane == 0 && col0 == 0 && a.lse_out != nullptr) a.lse_out[(int64_t)t * a.h_q + h] = m.lse;
+    // Only this wave reads these columns of the row, and it has read every
+    // split of them: split 0's copy can take the merged values.
+    if (STAGED) store_merged<PARTS>(a, t, h, col0, m);
   }
   if (lane == 0) s_amax[wave] = amax;
   __syncthreads();
@@ -2774,8 +2810,9 @@ __global__ __launch_bounds__(64 * HW) void combine_fp8_amax_kernel(CombineArgs a
 }
 
 // PARTS = 1: HPW whole rows per workgroup; PARTS = 2 or 4 (HPW = 1): workgroup
-// PARTS r + j encodes part j of row r.
-template <int HPW, int CHUNK, int PARTS = 1>
+// PARTS r + j encodes part j of row r.  STAGED: the amax pass left the merged
+// rows in a.merged; otherwise they are merged again.
+template <int HPW, int CHUNK, int PARTS, bool STAGED>
 __global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bpt = (a.h_q + HPW - 1) / HPW;
@@ -2784,7 +2821,11 @@ __global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArg
   const int t = rb / bpt;
   const int h = (rb - t * bpt) * HPW + wave;
   if (h >= a.h_q) return;
-  const Merged m = merge_head<CHUNK, PARTS>(a, t, h, col0);
+  Merged m;
+  if (STAGED)
+    m = load_merged<PARTS>(a, t, h, col0);
+  else
+    m = merge_head<CHUNK, PARTS>(a, t, h, col0);
   const uint32_t v = __hip_atomic_load((const uint32_t*)a.out_scale + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float qscale;
   if (v & 0x80000000u) {
@@ -2922,6 +2963,24 @@ hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t st
 }
 
 namespace {
+// The FP8 output's amax and encode passes.
+template <int CHUNK, bool STAGED>
+void launch_combine_fp8(const CombineArgs& a, hipStream_t stream) {
+  const unsigned rows = (unsigned)(a.s_q * a.h_q);
+  const unsigned blocks4 = (unsigned)(a.s_q * ((a.h_q + 3) / 4));
+  if (a.heads_per_wg == -1) {                     // a quarter of a row per wave
+    hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 4, STAGED>), dim3(rows), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 4, STAGED>), dim3(4 * rows), dim3(64), 0, stream, a);
+  } else if (a.heads_per_wg == 0) {               // half a row per wave
+    hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 2, STAGED>), dim3(rows / 2), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 2, STAGED>), dim3(2 * rows), dim3(64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((combine_fp8_amax_kernel<16, CHUNK, 1, STAGED>), dim3((unsigned)(a.s_q * ((a.h_q + 15) / 16))),
+                       dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK, 1, STAGED>), dim3(blocks4), dim3(256), 0, stream, a);
+  }
+}
+
 // CHUNK: partial rows requested per pass (4, 8, 12 or 16), the smallest that
 // holds every split, so few loads repeat a row needlessly.
 template <int CHUNK>
@@ -2931,17 +2990,10 @@ hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
   if (a.out_dtype == kOutFp8) {
     if (!a.scale_ready)
       hipLaunchKernelGGL(combine_fp8_init_kernel, dim3((unsigned)((a.s_q + 255) / 256)), dim3(256), 0, stream, a);
-    if (a.heads_per_wg == -1) {                   // a quarter of a row per wave
-      hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 4>), dim3(rows), dim3(256), 0, stream, a);
-      hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 4>), dim3(4 * rows), dim3(64), 0, stream, a);
-    } else if (a.heads_per_wg == 0) {             // half a row per wave
-      hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 2>), dim3(rows / 2), dim3(256), 0, stream, a);
-      hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 2>), dim3(2 * rows), dim3(64), 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((combine_fp8_amax_kernel<16, CHUNK>), dim3((unsigned)(a.s_q * ((a.h_q + 15) / 16))),
-                         dim3(1024), 0, stream, a);
-      hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK>), dim3(blocks4), dim3(256), 0, stream, a);
-    }
+    if (a.merged != nullptr)
+      launch_combine_fp8<CHUNK, true>(a, stream);
+    else
+      launch_combine_fp8<CHUNK, false>(a, stream);
   } else if (a.heads_per_wg == -1) {              // a quarter of a row per wave
     hipLaunchKernelGGL((combine_kernel<1, CHUNK, 4>), dim3(4 * rows), dim3(64), 0, stream, a.o_accum,
                        a.lse_accum, a.s_q, a.h_q, a.num_splits, a);

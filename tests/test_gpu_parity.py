@@ -266,6 +266,36 @@ def test_partial_only_then_combine_matches_fused():
     assert np.array_equal(lse.cpu().numpy(), fused["lse"].astype(np.float32))
 
 
+@pytest.mark.parametrize("name,S", [("fp8_16", 8), ("fp8_1", 8), ("small6", 5), ("large96", 2)])
+def test_fp8_output_staged_merge_matches_two_merges(name, S):
+    """Inside sparse_mla_decode an FP8 output's amax pass leaves each merged row in
+    split 0 of o_accum and the encode pass reads it back; the standalone
+    combine_splits merges twice.  Codes, scales and LSEs agree bit for bit, split 0
+    then holds exactly the f32 combine's output and the other splits their partials
+    (shapes cover the quarter-row, half-row and whole-row combine layouts)."""
+    import sparse_mla_decode_top_amd as smla
+    dev = dev_for(name, 0)
+    s_q, h_q = dev.inp.s_q, dev.inp.h_q
+    print(f"[case] {name} S={S}", flush=True)
+    fused = H.run(dev, S, "fp8", "split")
+    part = H.run(dev, S, "f32", "partial")
+    o = torch.from_numpy(part["o_acc"]).cuda()
+    l = torch.from_numpy(part["lse_acc"]).cuda()
+    codes = torch.full((s_q, h_q, 512), 0x7F, device="cuda", dtype=torch.uint8)
+    scale = torch.full((s_q,), float("nan"), device="cuda")
+    lse8 = torch.full((s_q, h_q), float("nan"), device="cuda")
+    smla.combine_splits(o, l, S, codes, sink=dev.sink, out_scale=scale, lse_out=lse8)
+    out32 = torch.full((s_q, h_q, 512), float("nan"), device="cuda")
+    smla.combine_splits(o, l, S, out32, sink=dev.sink)
+    torch.cuda.synchronize()
+    assert np.array_equal(fused["codes"], codes.cpu().numpy())
+    assert np.array_equal(fused["scale"], scale.cpu().numpy().astype(np.float64))
+    assert np.array_equal(fused["lse"], lse8.cpu().numpy().astype(np.float64))
+    assert np.array_equal(fused["o_acc"][0], out32.cpu().numpy())
+    assert np.array_equal(fused["o_acc"][1:], part["o_acc"][1:])
+    assert np.array_equal(fused["lse_acc"], part["lse_acc"])
+
+
 def test_combine_against_oracle_combine():
     """combine_splits on generator-made partials (random O_s, LSE_s with -inf splits) vs the oracle's."""
     import sparse_mla_decode_top_amd as smla
