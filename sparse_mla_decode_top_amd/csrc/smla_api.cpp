@@ -149,6 +149,9 @@ smla_status run_combine(const smla_params* p, int32_t num_splits, const float* o
   const int64_t rows = (int64_t)p->s_q * p->h_q;
   const int32_t cus = device_cus();
   a.heads_per_wg = 4 * rows <= cus ? -1 : rows <= 2 * cus ? 0 : 4;
+  // The staged FP8 encode reads one row per (token, head): quarter rows up to
+  // four times as many rows as CUs (measured at 64 and 1,024 rows).
+  a.enc_quarter = rows <= 4 * (int64_t)cus ? 1 : 0;
   a.scale_ready = scale_ready ? 1 : 0;
   a.merged = merged;
   return smla::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;

@@ -43,6 +43,7 @@ struct CombineArgs {
   float* merged;              // FP8 output: [s_q][h_q][512] f32 staging of the merged O, written by the amax
                               // pass and read by the encode pass (split 0 of a caller's o_accum that the
                               // decode owns for the call), or nullptr: the encode pass merges again
+  int32_t enc_quarter;        // staged FP8 encode: a quarter of a row per wave (else 4 whole rows per workgroup)
 };
 
 // Each returns the launch status (hipSuccess or the runtime's error).
