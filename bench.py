@@ -473,8 +473,6 @@ def kernel_label(s_q, S, pool, cus=256):
             return f"decode_kernel4t<{pool} pool, {mode}, {c} parts: head tiles{' x column halves' if c == 8 else ''}>"
         if c == 2:
             return f"decode_kernel8h<{pool} pool, {mode}, 2 head halves>"
-        if c >= 2:
-            return f"decode_kernel8<{pool} pool, {mode}, {c} column parts>"
         name = "decode_kernel8p" if pool == "bf16" else "decode_kernel"
         return f"{name}<{pool} pool, {mode}, 1 column part>"
 
@@ -482,7 +480,7 @@ def kernel_label(s_q, S, pool, cus=256):
     if cs == 1 and jobs > cus and 0 < tail and 2 * tail <= cus:
         ct = 8 if 8 * tail <= cus else 4 if 4 * tail <= cus else 2
         if pool == "bf16" and (jobs - tail) % 8 == 0:
-            tail_body = "decode_kernel8h's in 2 head halves" if ct == 2 else f"decode_kernel8's in {ct} column parts"
+            tail_body = "decode_kernel8h's in 2 head halves" if ct == 2 else f"decode8_body in {ct} column parts"
             return (f"decode_kernel8m<bf16 pool, {mode}: decode_kernel8p's body over {jobs - tail} jobs, "
                     f"{tail_body} over the last {tail}>")
         return f"{one(1)} over {jobs - tail} jobs + {one(ct)} over the last {tail}"
