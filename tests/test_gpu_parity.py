@@ -457,6 +457,10 @@ def test_graph_capture_fp8_output_replays_match_eager():
     for _ in range(3):
         out.zero_()
         scale.fill_(123.0)
+        # the replay must rewrite the partials, and the encode pass must read the
+        # merged rows its own amax pass staged in o_accum[0]
+        o_acc.fill_(float("nan"))
+        lse_acc.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
