@@ -2764,9 +2764,9 @@ __device__ __forceinline__ Merged load_merged(const CombineArgs& a, int t, int h
 }
 
 // HW waves per workgroup, whose amaxes meet in LDS, so a token sees fewer
-// atomics.  PARTS = 1: one wave per (token, head) row, HW = 4 spreading a small
-// batch over more compute units or HW = 16 keeping the atomics of a large one
-// few.  PARTS = 2 or 4 (HW = 4): one wave per 1 / PARTS of a row (wave u of
+// atomics.  PARTS = 1: one wave per (token, head) row, HW = 16 keeping the
+// atomics of a large batch few.  PARTS = 2 or 4 (HW = 4), for small batches:
+// one wave per 1 / PARTS of a row (wave u of
 // the grid: row u / PARTS, part u % PARTS); a token's h_q * PARTS waves fill
 // whole workgroups, so a workgroup never spans two tokens.  STAGED: store the
 // merged rows to a.merged for the encode pass.
