@@ -78,6 +78,22 @@ def _e4m3_round_half_up(x):
     return _orig_e4m3_encode(x + np.sign(x) * np.abs(x) * 2.0 ** -30)
 
 
+def _fp8_f32_ratio_in_f64(O32):
+    O32 = np.asarray(O32, dtype=np.float32)
+    amax = np.abs(O32).reshape(O32.shape[0], -1).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    ratio = O32.astype(np.float64) / scale.astype(np.float64)[:, None, None]     # decided in float64
+    return O.e4m3_encode(ratio), scale
+
+
+def _fp8_f32_scale_in_f64(O32):
+    O32 = np.asarray(O32, dtype=np.float32)
+    amax = np.abs(O32).reshape(O32.shape[0], -1).max(axis=1).astype(np.float64)
+    scale = np.where(amax > 0, amax / 448.0, 1.0)                                # never rounded to float32
+    ratio = (O32 / scale[:, None, None]).astype(np.float32)
+    return O.e4m3_encode(ratio.astype(np.float64)), scale
+
+
 MUTANTS = {
     "lse_natural_log": ("attend_token", _attend_natural_log),
     "value_wrong_slice": ("attend_token", _attend_wrong_value_slice),
@@ -88,6 +104,8 @@ MUTANTS = {
     "partition_remainder_last": ("split_block_ranges", _ranges_remainder_last),
     "valid_off_by_one": ("valid_mask", _valid_off_by_one),
     "e4m3_ties_away": ("e4m3_encode", _e4m3_round_half_up),
+    "fp8_f32_ratio_in_f64": ("fp8_quantize_per_token_f32", _fp8_f32_ratio_in_f64),
+    "fp8_f32_scale_in_f64": ("fp8_quantize_per_token_f32", _fp8_f32_scale_in_f64),
 }
 
 PINS = [
@@ -101,6 +119,7 @@ PINS = [
     P.test_partition_worked_examples,
     P.test_dense_special_case_against_torch_sdpa,
     P.test_e4m3_encode_against_torch_in_range,
+    P.test_fp8_quantize_f32_against_torch_float32,
 ]
 
 

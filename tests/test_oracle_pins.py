@@ -346,6 +346,55 @@ def test_fp8_per_token_scale():
     assert np.array_equal(codes, c32) and np.allclose(scale, s32, rtol=1e-7)
 
 
+def _fp8_tie_heavy_tokens(seed=5, per_token=4096):
+    """Float32 tokens whose elements sit on exact e4m3 midpoints once divided by the
+    token's float32 scale (amax / 448, not a power of two), so that the rounding
+    decision depends on the precision in which O / scale is formed."""
+    rng = np.random.default_rng(seed)
+    vals = O.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (vals[1:] + vals[:-1]) / 2
+    toks = []
+    for _ in range(6):
+        amax = np.float32(448.0 * rng.uniform(0.3, 3.0))
+        s = np.float32(amax / np.float32(448.0))
+        m = rng.choice(mids, per_token) * rng.choice([-1.0, 1.0], per_token)
+        x = (m * np.float64(s)).astype(np.float32)
+        x = np.where(np.abs(x) < amax, x, np.float32(0.0))
+        x[0] = amax                                     # the token's amax is exactly amax
+        toks.append(x)
+    return np.stack(toks).reshape(6, -1, 512)
+
+
+def _torch_fp8_quantize_f32(O32):
+    """Per-token FP8 quantisation in torch float32: amax, amax / 448, O / scale, and
+    torch's own e4m3fn cast (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(O32, dtype=np.float32))
+    amax = t.abs().reshape(t.shape[0], -1).amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    ratio = (t / scale[:, None, None]).clamp(-448.0, 448.0)
+    return ratio.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), scale.numpy()
+
+
+def test_fp8_quantize_f32_against_torch_float32():
+    """The float32-decided quantisation against torch float32 arithmetic (IEEE division)
+    and torch's e4m3fn cast, on random tokens of several magnitudes and on tie-heavy
+    tokens where float32 and float64 decide differently."""
+    rng = np.random.default_rng(17)
+    rand = (rng.standard_normal((5, 64, 512)) * np.array([1e-3, 0.05, 1.0, 7.0, 300.0])[:, None, None])
+    rand = rand.astype(np.float32)
+    rand[2, 3, ::5] = -0.0
+    ties = _fp8_tie_heavy_tokens()
+    zero = np.zeros((1, 2, 512), dtype=np.float32)
+    for O32 in (rand, ties, zero):
+        codes, scale = O.fp8_quantize_per_token_f32(O32)
+        ref_codes, ref_scale = _torch_fp8_quantize_f32(O32)
+        assert scale.dtype == np.float32 and np.array_equal(scale, ref_scale)
+        assert np.array_equal(codes, ref_codes)
+    # the tie-heavy tokens do separate the two precisions (the pin is sensitive to them)
+    c64, _ = O.fp8_quantize_per_token(ties.astype(np.float64))
+    assert int((c64 != _torch_fp8_quantize_f32(ties)[0]).sum()) > 1000
+
+
 def test_fp8_pool_dequantisation():
     codes = np.array([[0x38, 0xB8, 0x00, 0x7E]], dtype=np.uint8)      # 1, -1, 0, 448
     got = O.dequantize_fp8_rows(codes, np.array([0.5]))
