@@ -119,6 +119,53 @@ def assert_lse_close(got, ref, tol=TOL_LSE):
         assert err <= tol, f"LSE max-abs error {err:.3g} > {tol}"
 
 
+# Planted rows (a KV row set to 20 x a query head) give that head log2-unit scores
+# near 700, and every other head of a token that gathers such a row scores tens of
+# units on it, where N(0, 1) inputs keep |LSE| within 9.4 .. 10.4 and |O| below 0.7
+# at every named shape (seeds 0-2).  Float32 rounds a score in proportion to the
+# sizes of its products (the spacing of float32 near 700 is 6e-5, above the 1e-5 LSE
+# bar by itself), and the summation order of O in proportion to the size of the
+# summed rows.  So the heads of tokens that gather a planted row are held to the
+# bars relative to their size (LSE: |LSE|; O between split counts: the row's largest
+# |O|; at least 1 either way); every other token keeps the absolute bars.
+def tokens_gathering(indices, rows):
+    """Boolean [s_q]: the tokens whose index list names any of `rows`."""
+    return np.isin(np.asarray(indices), np.asarray(list(rows))).any(axis=1)
+
+
+def assert_lse_close_planted(got, ref, planted, tol=TOL_LSE):
+    """assert_lse_close, with the heads of the `planted` tokens held to tol * max(1, |ref|).
+    Returns how many finite entries took the relative bar."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert not np.any(np.isnan(got)), "unwritten or NaN LSE"
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "-inf pattern differs"
+    fin = np.isfinite(ref)
+    big = fin & np.asarray(planted)[:, None]
+    small = fin & ~big
+    if small.any():
+        err = max_abs(got[small], ref[small])
+        assert err <= tol, f"LSE max-abs error {err:.3g} > {tol} (tokens without a planted row)"
+    if big.any():
+        rel = float(np.max(np.abs(got[big] - ref[big]) / np.maximum(1.0, np.abs(ref[big]))))
+        assert rel <= tol, f"relative LSE error {rel:.3g} > {tol} (tokens gathering a planted row)"
+    return int(big.sum())
+
+
+def assert_split_close_planted(got, base, planted, tol=TOL_SPLIT):
+    """Combined fp32 O of two split counts: the rows (heads) of the `planted` tokens are
+    held to tol times max(1, the row's largest |O|), every other row to the absolute tol."""
+    got = np.asarray(got, np.float64)
+    base = np.asarray(base, np.float64)
+    rowmax = np.abs(base).max(axis=-1, keepdims=True)
+    rel = np.asarray(planted)[:, None, None] & (rowmax > 1.0)
+    scale = np.where(rel, rowmax, 1.0)
+    err = np.abs(got - base) / scale
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, f"split-count difference {worst:.3g} > {tol}"
+    return int(rel.sum())
+
+
 def assert_o_close(got, ref, tol=TOL_O, rel=0.0):
     got = np.asarray(got, np.float64)
     assert not np.any(np.isnan(got)), "unwritten or NaN output"
