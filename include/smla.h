@@ -76,7 +76,14 @@ typedef struct {
 
 /*
  * sparse_mla_decode -- the decode step: per-(token, split) attention jobs and,
- * when an output is requested, the combine.
+ * when an output is requested, the combine.  The jobs, the block ranges and the
+ * partials follow FlashMLA PR #25, "What changes" (each (token, split) job walks
+ * its own KV block range and stores an fp32 O normalised by its own denominator
+ * plus a log2-space LSE, no cast); the empty split and the remainder rule follow
+ * cudnn-frontend PR #768, commit messages; the direct path is FlashMLA PR #25's
+ * unsplit path, whose epilogue casts ("What changes", last item).  With an FP8
+ * output the combine owns the amax of the recombined output (cudnn-frontend PR
+ * #768, commit messages).
  *
  *   q          [s_q][h_q][576] bf16, 16-byte aligned.
  *   kv_pool    [n_pool][kv_row_stride]: bf16 (SMLA_KV_BF16) or e4m3fn codes
@@ -104,13 +111,13 @@ typedef struct {
  *     epilogue.  `out` is required.
  *   - o_accum and lse_accum given: every job writes its partials (the FlashMLA
  *     partial protocol); if `out` is given the combine runs after it on the same
- *     stream, otherwise the caller combines (combine_splits).  With an FP8
- *     `out`, the combine's first pass then stages the merged rows in split 0 of
- *     o_accum for its second: on return, o_accum[0] holds the final O in f32
- *     (sink applied, before the cast) instead of split 0's partial; the other
- *     splits and lse_accum keep their partials.
+ *     stream, otherwise the caller combines (combine_splits).  On return
+ *     o_accum and lse_accum hold the partials in either case, so the caller may
+ *     combine them again.
  *   - num_splits > 1 with either accumulator NULL: SMLA_ERR_MISSING_WORKSPACE.
  *   - Giving only one of o_accum / lse_accum: SMLA_ERR_MISSING_WORKSPACE.
+ * An FP8 `out` of the split mode doubles as the combine's counters while the
+ * call runs (the first 8 bytes of each token's rows), until the codes land.
  */
 smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* kv_pool,
                               const float* kv_scale, const int32_t* indices, int32_t num_splits,
@@ -119,10 +126,13 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
 
 /*
  * combine_splits -- merge split partials (as written by sparse_mla_decode) into
- * the final output.  Same shapes and meaning as above; o_accum, lse_accum and
- * out are required; p->kv_dtype, topk, n_pool, kv_row_stride and
- * softmax_scale are not used.  A split whose LSE is -inf contributes nothing;
- * a (token, head) with every split at -inf gets O = 0 and LSE = -inf.
+ * the final output ("The Split-K Dispatch", "The LSE Combine Strategy": weights
+ * 2^(LSE_s - max LSE); FlashMLA PR #25, "What changes": the combine applies the
+ * sink, once).  Same shapes and meaning as above; o_accum, lse_accum and out
+ * are required and o_accum / lse_accum are only read; p->kv_dtype, topk,
+ * n_pool, kv_row_stride and softmax_scale are not used.  A split whose LSE is
+ * -inf contributes nothing; a (token, head) with every split at -inf gets
+ * O = 0 and LSE = -inf.
  */
 smla_status combine_splits(const smla_params* p, int32_t num_splits, const float* o_accum,
                            const float* lse_accum, const float* sink, void* out,
@@ -132,10 +142,11 @@ smla_status combine_splits(const smla_params* p, int32_t num_splits, const float
  * smla_choose_num_splits -- a split count for the shape that gives small decode
  * batches enough (token, split) jobs to fill `num_cus` compute units and keeps
  * large batches unsplit ("The Split-K Dispatch", "The Reasoning Behind the
- * Design": the split count adapts to the batch).  With x = num_cus / s_q
- * compute units per token: S = x / 8 when x >= 40, 4 when x >= 8, 2 when
- * x >= 4, else 1, capped at the block count (and SMLA_MAX_SPLITS).  Split jobs
- * then run as 2, 4 or 8 workgroups each (one per part of the output columns).
+ * Design", "Adaptive NSPLIT": the split count adapts to the batch).  With
+ * x = num_cus / s_q compute units per token: S = x / 8 (rounded down) when
+ * x >= 40, 4 when x >= 16, 2 when x >= 8, else 1, capped at the block count
+ * (and SMLA_MAX_SPLITS).  Jobs then run as 2, 4 or 8 workgroups each (one per
+ * part of the heads or of the output columns).
  * Deterministic in its arguments, so a captured graph stays valid.  Returns
  * >= 1, or 0 when an argument is non-positive.
  */
@@ -150,7 +161,9 @@ size_t smla_partial_bytes(int32_t s_q, int32_t h_q, int32_t num_splits);
 
 /*
  * smla_validate -- the host-side argument check sparse_mla_decode performs,
- * without launching anything.  Pointers are only tested for NULL and
+ * without launching anything (the host rules of FlashMLA PR #25, "Limitations /
+ * follow-ups": partial buffers only where supported; cudnn-frontend PR #768,
+ * commit messages: a split needs its LSE workspace and takes no caller stride).  Pointers are only tested for NULL and
  * alignment, never dereferenced, so host addresses may stand in for them.
  */
 smla_status smla_validate(const smla_params* p, const void* q, const void* kv_pool,

@@ -155,9 +155,7 @@ def sparse_mla_decode(q, kv_pool, indices, num_splits, softmax_scale, kv_scale=N
 
     q [s_q, h_q, 576] bf16; kv_pool [n_pool, row_stride] bf16, or uint8 e4m3 codes with
     kv_scale [n_pool] f32; indices [s_q, topk] int32.  The output dtype follows `out`
-    (bf16 / float32 / uint8 codes) unless `out_dtype` is given.  With an FP8 `out` and
-    partial buffers, o_accum[0] holds the final O in float32 on return (the combine's
-    staging), not split 0's partial.
+    (bf16 / float32 / uint8 codes) unless `out_dtype` is given.
     """
     import torch
     lib = load_library()

@@ -116,13 +116,12 @@ smla_status smla_validate(const smla_params* p, const void* q, const void* kv_po
 
 namespace {
 
-// The combine launch sequence; scale_ready: an FP8 output's out_scale already
-// holds the combine's starting value (-0.0).  merged: where an FP8 output's
-// amax pass leaves the merged rows for the encode pass (nullptr: the encode
-// pass merges the splits again).
+// The combine launch sequence; scale_ready: an FP8 output's out_scale and
+// token counters already hold the combine's starting values (seeded by the
+// attention kernel).
 smla_status run_combine(const smla_params* p, int32_t num_splits, const float* o_accum, const float* lse_accum,
                         const float* sink, void* out, float* out_scale, float* lse_out, void* stream,
-                        bool scale_ready, float* merged) {
+                        bool scale_ready) {
   smla_status st = check_common_shape(p, num_splits);
   if (st != SMLA_OK) return st;
   if (o_accum == nullptr || lse_accum == nullptr) return SMLA_ERR_MISSING_WORKSPACE;
@@ -149,11 +148,8 @@ smla_status run_combine(const smla_params* p, int32_t num_splits, const float* o
   const int64_t rows = (int64_t)p->s_q * p->h_q;
   const int32_t cus = device_cus();
   a.heads_per_wg = 4 * rows <= cus ? -1 : rows <= 2 * cus ? 0 : 4;
-  // The staged FP8 encode reads one row per (token, head): quarter rows up to
-  // four times as many rows as CUs (measured at 64 and 1,024 rows).
-  a.enc_quarter = rows <= 4 * (int64_t)cus ? 1 : 0;
   a.scale_ready = scale_ready ? 1 : 0;
-  a.merged = merged;
+  a.cus = cus;
   return smla::launch_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
@@ -164,7 +160,7 @@ extern "C" {
 smla_status combine_splits(const smla_params* p, int32_t num_splits, const float* o_accum,
                            const float* lse_accum, const float* sink, void* out, float* out_scale,
                            float* lse_out, void* stream) {
-  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, false, nullptr);
+  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, false);
 }
 
 smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* kv_pool, const float* kv_scale,
@@ -184,7 +180,7 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   a.lse_accum = lse_accum;
   a.out = out;
   const bool direct = o_accum == nullptr;
-  // split mode with an FP8 output to follow: the attention kernel seeds out_scale
+  // split mode with an FP8 output to follow: the attention kernel seeds out_scale and the token counters
   const bool seed_scale = !direct && out != nullptr && p->out_dtype == SMLA_OUT_FP8_E4M3;
   a.out_scale = (direct || seed_scale) ? out_scale : nullptr;
   a.lse_out = lse_out;
@@ -214,11 +210,7 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   }
   if (smla::launch_decode_partial(a, fp8, hs) != hipSuccess) return SMLA_ERR_HIP;
   if (out == nullptr) return SMLA_OK;   // partial-only: the caller combines
-  // An FP8 output's two passes: the amax pass stages each merged row in split
-  // 0 of o_accum, whose partials it has just read, so the encode pass reads one
-  // row instead of num_splits.
-  float* merged = p->out_dtype == SMLA_OUT_FP8_E4M3 ? o_accum : nullptr;
-  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, seed_scale, merged);
+  return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, seed_scale);
 }
 
 }  // extern "C"

@@ -38,12 +38,11 @@ struct CombineArgs {
   float* lse_out;
   int32_t s_q, h_q, num_splits;
   int32_t out_dtype;
-  int32_t heads_per_wg;       // -1: a quarter of a row per wave, 0: half a row, 4: four rows per workgroup
-  int32_t scale_ready;        // FP8 output: out_scale already holds -0.0 (set by the attention kernel)
-  float* merged;              // FP8 output: [s_q][h_q][512] f32 staging of the merged O, written by the amax
-                              // pass and read by the encode pass (split 0 of a caller's o_accum that the
-                              // decode owns for the call), or nullptr: the encode pass merges again
-  int32_t enc_quarter;        // staged FP8 encode: a quarter of a row per wave (else 4 whole rows per workgroup)
+  int32_t heads_per_wg;       // bf16 / f32 output: -1 a quarter of a row per wave, 0 half a row, 4 four rows
+                              // per workgroup
+  int32_t scale_ready;        // FP8 output: out_scale and the token counters already seeded (by the attention
+                              // kernel)
+  int32_t cus;                // compute units of the device (the FP8 one-launch combine fits one round)
 };
 
 // Each returns the launch status (hipSuccess or the runtime's error).

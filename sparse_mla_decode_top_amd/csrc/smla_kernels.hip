@@ -328,6 +328,19 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return code | sign;
 }
 
+// FP8 output through the combine (see the combine kernels below).  The two
+// counter words of token t: [0] workgroups counted in, [1] the bits
+// of the largest |O| seen (a non-negative float).
+__device__ __forceinline__ uint32_t* fp8_sync_words(void* out, int t, int h_q) {
+  return (uint32_t*)((uint8_t*)out + (int64_t)t * h_q * 512);
+}
+
+// Seeds token t's FP8 combine (one thread per token).
+__device__ __forceinline__ void seed_fp8_combine(float* out_scale, void* out, int t, int h_q) {
+  out_scale[t] = -0.0f;
+  *(u32x2*)fp8_sync_words(out, t, h_q) = u32x2{0u, 0u};
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
@@ -862,7 +875,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Split jobs of a decode with an FP8 output: the combine's running amax per
   // token starts from -0.0 (its "an amax, not yet a scale" form), stored here
   // so that the combine needs no launch of its own for it.
-  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0)
+    seed_fp8_combine(a.out_scale, a.out, t, h_q);
 }
 
 // ---------------------------------------------------------------------------
@@ -1302,8 +1316,9 @@ __device__ __forceinline__ void decode8_body(
     else if (a.lse_out != nullptr)
       a.lse_out[row0 + lane] = lse;
   }
-  // Split jobs of a decode with an FP8 output: seed the combine's running amax.
-  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
+  // Split jobs of a decode with an FP8 output: seed the combine's amax and counters.
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0)
+    seed_fp8_combine(a.out_scale, a.out, t, h_q);
 }
 
 
@@ -1671,8 +1686,8 @@ __device__ __forceinline__ void decode8p_body(
                                        pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
     }
   }
-  // Split jobs of a decode with an FP8 output: seed the combine's running amax.
-  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && tid == 0) a.out_scale[t] = -0.0f;
+  // Split jobs of a decode with an FP8 output: seed the combine's amax and counters.
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && tid == 0) seed_fp8_combine(a.out_scale, a.out, t, h_q);
 }
 
 template <bool DIRECT, bool PREFETCH>
@@ -2087,8 +2102,9 @@ __device__ __forceinline__ void decode8h_body(
                                        pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
     }
   }
-  // Split jobs of a decode with an FP8 output: seed the combine's running amax.
-  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
+  // Split jobs of a decode with an FP8 output: seed the combine's amax and counters.
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0)
+    seed_fp8_combine(a.out_scale, a.out, t, h_q);
 }
 
 template <bool KV_FP8, bool DIRECT, bool PREFETCH>
@@ -2541,8 +2557,9 @@ __device__ __forceinline__ void decode4t_body(
                                        pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
     }
   }
-  // Split jobs of a decode with an FP8 output: seed the combine's running amax.
-  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0) a.out_scale[t] = -0.0f;
+  // Split jobs of a decode with an FP8 output: seed the combine's amax and counters.
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0)
+    seed_fp8_combine(a.out_scale, a.out, t, h_q);
 }
 
 template <bool KV_FP8, bool DIRECT, bool PREFETCH, int CP>
@@ -2709,132 +2726,60 @@ __global__ __launch_bounds__(64 * HPW) void combine_kernel(const float* __restri
   if (a.lse_out != nullptr && lane == 0 && col0 == 0) a.lse_out[row] = m.lse;
 }
 
-// FP8 output, in three launches that need no scratch memory.  The token's
-// scale needs the amax over all of its heads, so the rows are merged twice:
-//   init:   out_scale[t] = -0.0 (sign bit set: "an amax, not yet a scale")
-//   amax:   one wave per (token, head) merges the row; per 16 heads the
-//           largest amax raises out_scale[t] to 0x80000000 | bits(amax) with
-//           an unsigned atomic max (the bits of non-negative floats order like
-//           the floats);
-//   encode: one wave per (token, head) merges the row again, turns the value
-//           it reads in out_scale[t] into the scale (amax / 448, or 1 for a
-//           zero amax, when the sign bit is set; the scale itself otherwise),
-//           writes the e4m3 codes, and the wave of head 0 stores the scale.
-//           Every wave of the token derives the same scale whichever of the
-//           two forms it reads.
+// FP8 output.  The token's scale needs the amax over all of its heads, and
+// no memory beyond the caller's buffers is used.  Before the combine, the
+// attention kernel (or combine_fp8_init_kernel, for the standalone combine)
+// seeds out_scale[t] = -0.0 ("not yet a scale") and zeroes the first 8 bytes
+// of the token's output rows, which the combine then uses as two counters
+// until it writes its codes there (fp8_sync_words).
+//
+// One launch (combine_fp8_kernel) when every workgroup of the launch can be
+// resident at once (at most one per compute unit): each workgroup merges its
+// rows, keeps them in registers, raises the token's amax word with an atomic
+// max and counts itself in with an acquire-release increment.  The workgroup
+// that counts last reads the final amax, stores the scale in out_scale[t];
+// the others wait for it to appear there.  Then every workgroup encodes its
+// rows.  Only atomics carry data between workgroups.
+//
+// Larger launches take two passes that merge the rows twice (no workgroup
+// waits for another):
+//   amax:   per workgroup the largest amax raises out_scale[t] to
+//           0x80000000 | bits(amax) with an unsigned atomic max (the bits of
+//           non-negative floats order like the floats);
+//   encode: turns the value it reads in out_scale[t] into the scale (amax /
+//           448, or 1 for a zero amax, when the sign bit is set; the scale
+//           itself otherwise), writes the codes; the wave of head 0 stores
+//           the scale.  Every wave derives the same scale from either form.
+
 __global__ __launch_bounds__(256) void combine_fp8_init_kernel(CombineArgs a) {
   const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t < a.s_q) a.out_scale[t] = -0.0f;
+  if (t < a.s_q) seed_fp8_combine(a.out_scale, a.out, t, a.h_q);
 }
 
 __device__ __forceinline__ float abs_max4(f32x4 v) {
   return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 }
 
-// The staged merged row of an FP8 output (a.merged), in merge_head's lane
-// layout: the amax pass stores what it merged, the encode pass loads it back
-// (the same fp32 values, so the codes equal a second merge's).
+// Wave u of a launch with PARTS waves per row merges part u % PARTS of row
+// u / PARTS (PARTS = 1: the whole row).
+struct RowPart {
+  int t, h, col0;
+};
 template <int PARTS>
-__device__ __forceinline__ void store_merged(const CombineArgs& a, int t, int h, int col0, const Merged& m) {
-  const int lane = threadIdx.x & 63;
-  float* dst = a.merged + ((int64_t)t * a.h_q + h) * 512 + col0 + (PARTS == 4 ? 2 : 4) * lane;
-  if (PARTS == 4) {
-    *(f32x2*)dst = f32x2{m.lo[0], m.lo[1]};
-  } else {
-    *(f32x4*)dst = m.lo;
-    if (PARTS == 1) *(f32x4*)(dst + 256) = m.hi;
-  }
+__device__ __forceinline__ RowPart row_part(const CombineArgs& a, int64_t u) {
+  const int64_t r = u / PARTS;
+  RowPart p;
+  p.col0 = (512 / PARTS) * (int)(u - r * PARTS);
+  p.t = (int)(r / a.h_q);
+  p.h = (int)(r - (int64_t)p.t * a.h_q);
+  return p;
 }
 
+// e4m3 codes of a merged part row under the token's scale.
 template <int PARTS>
-__device__ __forceinline__ Merged load_merged(const CombineArgs& a, int t, int h, int col0) {
+__device__ __forceinline__ void store_codes(const CombineArgs& a, const RowPart& p, const Merged& m, float qscale) {
   const int lane = threadIdx.x & 63;
-  const float* src = a.merged + ((int64_t)t * a.h_q + h) * 512 + col0 + (PARTS == 4 ? 2 : 4) * lane;
-  Merged m;
-  m.hi = f32x4{0.f, 0.f, 0.f, 0.f};
-  m.lse = 0.f;                          // not used by the encode pass
-  if (PARTS == 4) {
-    const f32x2 x = *(const f32x2*)src;
-    m.lo = f32x4{x[0], x[1], 0.f, 0.f};
-  } else {
-    m.lo = *(const f32x4*)src;
-    if (PARTS == 1) m.hi = *(const f32x4*)(src + 256);
-  }
-  return m;
-}
-
-// HW waves per workgroup, whose amaxes meet in LDS, so a token sees fewer
-// atomics.  PARTS = 1: one wave per (token, head) row, HW = 16 keeping the
-// atomics of a large batch few.  PARTS = 2 or 4 (HW = 4), for small batches:
-// one wave per 1 / PARTS of a row (wave u of
-// the grid: row u / PARTS, part u % PARTS); a token's h_q * PARTS waves fill
-// whole workgroups, so a workgroup never spans two tokens.  STAGED: store the
-// merged rows to a.merged for the encode pass.
-template <int HW, int CHUNK, int PARTS, bool STAGED>
-__global__ __launch_bounds__(64 * HW) void combine_fp8_amax_kernel(CombineArgs a) {
-  __shared__ float s_amax[HW];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int t, h, col0 = 0;
-  bool ok;
-  if (PARTS == 1) {
-    const int bpt = (a.h_q + HW - 1) / HW;
-    t = blockIdx.x / bpt;
-    h = (blockIdx.x - t * bpt) * HW + wave;
-    ok = h < a.h_q;
-  } else {
-    const int64_t u = (int64_t)blockIdx.x * HW + wave;
-    const int64_t r = u / PARTS;
-    col0 = (512 / PARTS) * (int)(u - r * PARTS);
-    t = (int)(r / a.h_q);
-    h = (int)(r - (int64_t)t * a.h_q);
-    ok = true;
-  }
-  float amax = 0.f;
-  if (ok) {
-    const Merged m = merge_head<CHUNK, PARTS>(a, t, h, col0);
-    amax = wave_max(PARTS == 1 ? fmaxf(abs_max4(m.lo), abs_max4(m.hi)) : abs_max4(m.lo));
-    if (lane == 0 && col0 == 0 && a.lse_out != nullptr) a.lse_out[(int64_t)t * a.h_q + h] = m.lse;
-    // Only this wave reads these columns of the row, and it has read every
-    // split of them: split 0's copy can take the merged values.
-    if (STAGED) store_merged<PARTS>(a, t, h, col0, m);
-  }
-  if (lane == 0) s_amax[wave] = amax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < HW; ++w) v = fmaxf(v, s_amax[w]);
-    __hip_atomic_fetch_max((uint32_t*)a.out_scale + t, 0x80000000u | __float_as_uint(v), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// PARTS = 1: HPW whole rows per workgroup; PARTS = 2 or 4 (HPW = 1): workgroup
-// PARTS r + j encodes part j of row r.  STAGED: the amax pass left the merged
-// rows in a.merged; otherwise they are merged again.
-template <int HPW, int CHUNK, int PARTS, bool STAGED>
-__global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bpt = (a.h_q + HPW - 1) / HPW;
-  const int rb = (int)blockIdx.x / PARTS;
-  const int col0 = (512 / PARTS) * ((int)blockIdx.x % PARTS);
-  const int t = rb / bpt;
-  const int h = (rb - t * bpt) * HPW + wave;
-  if (h >= a.h_q) return;
-  Merged m;
-  if (STAGED)
-    m = load_merged<PARTS>(a, t, h, col0);
-  else
-    m = merge_head<CHUNK, PARTS>(a, t, h, col0);
-  const uint32_t v = __hip_atomic_load((const uint32_t*)a.out_scale + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float qscale;
-  if (v & 0x80000000u) {
-    const float amax = __uint_as_float(v & 0x7FFFFFFFu);
-    qscale = amax > 0.f ? amax / 448.0f : 1.0f;
-  } else {
-    qscale = __uint_as_float(v);
-  }
-  uint8_t* orow = (uint8_t*)a.out + ((int64_t)t * a.h_q + h) * 512 + col0;
+  uint8_t* orow = (uint8_t*)a.out + ((int64_t)p.t * a.h_q + p.h) * 512 + p.col0;
   if (PARTS == 4) {                        // columns col0 + 2l, col0 + 2l + 1
     const uint32_t w2 = e4m3_encode(m.lo[0] / qscale) | (e4m3_encode(m.lo[1] / qscale) << 8);
     *(uint16_t*)(orow + 2 * lane) = (uint16_t)w2;
@@ -2848,7 +2793,94 @@ __global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArg
     *(uint32_t*)(orow + 4 * lane) = wlo;
     if (PARTS == 1) *(uint32_t*)(orow + 256 + 4 * lane) = whi;
   }
-  if (h == 0 && lane == 0 && col0 == 0) a.out_scale[t] = qscale;
+}
+
+// Polls a waiting workgroup makes for its token's scale before it gives up and
+// takes NaN (only reachable if the token's workgroups were not all resident).
+constexpr int kScaleSpinLimit = 1 << 16;
+
+// One-launch FP8 combine: HW waves per workgroup, PARTS waves per row; a
+// token's h_q * PARTS waves fill h_q * PARTS / HW whole workgroups.
+template <int HW, int CHUNK, int PARTS>
+__global__ __launch_bounds__(64 * HW) void combine_fp8_kernel(CombineArgs a) {
+  static_assert(HW == 4 || HW == 8 || HW == 16, "waves per workgroup");
+  __shared__ float s_amax[HW];
+  __shared__ float s_scale;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const RowPart p = row_part<PARTS>(a, (int64_t)blockIdx.x * HW + wave);
+  const Merged m = merge_head<CHUNK, PARTS>(a, p.t, p.h, p.col0);
+  if (lane == 0 && p.col0 == 0 && a.lse_out != nullptr) a.lse_out[(int64_t)p.t * a.h_q + p.h] = m.lse;
+  const float amax_w = wave_max(PARTS == 1 ? fmaxf(abs_max4(m.lo), abs_max4(m.hi)) : abs_max4(m.lo));
+  if (lane == 0) s_amax[wave] = amax_w;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < HW; ++w) v = fmaxf(v, s_amax[w]);
+    uint32_t* sync = fp8_sync_words(a.out, p.t, a.h_q);
+    uint32_t* scale_word = (uint32_t*)a.out_scale + p.t;
+    const uint32_t n_wg = (uint32_t)(a.h_q * PARTS / HW);
+    __hip_atomic_fetch_max(sync + 1, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Release: this workgroup's amax is in before its count; acquire: the
+    // last one to count in sees every amax.
+    const uint32_t before = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    float sc;
+    if (before == n_wg - 1) {
+      const float amax = __uint_as_float(__hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      sc = amax > 0.f ? amax / 448.0f : 1.0f;
+      __hip_atomic_store(scale_word, __float_as_uint(sc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      uint32_t bits = 0x80000000u;
+      for (int n = 0; n < kScaleSpinLimit && bits == 0x80000000u; ++n) {
+        __builtin_amdgcn_s_sleep(1);
+        bits = __hip_atomic_load(scale_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      sc = bits == 0x80000000u ? __builtin_nanf("") : __uint_as_float(bits);
+    }
+    s_scale = sc;
+  }
+  __syncthreads();
+  store_codes<PARTS>(a, p, m, s_scale);
+}
+
+// Two-pass FP8 combine, amax pass: HW waves per workgroup, whose amaxes meet
+// in LDS, so a token sees fewer atomics.  PARTS = 1: one wave per (token,
+// head) row, HW = 16 keeping the atomics of a large batch few.
+template <int HW, int CHUNK, int PARTS>
+__global__ __launch_bounds__(64 * HW) void combine_fp8_amax_kernel(CombineArgs a) {
+  __shared__ float s_amax[HW];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const RowPart p = row_part<PARTS>(a, (int64_t)blockIdx.x * HW + wave);
+  const Merged m = merge_head<CHUNK, PARTS>(a, p.t, p.h, p.col0);
+  const float amax = wave_max(PARTS == 1 ? fmaxf(abs_max4(m.lo), abs_max4(m.hi)) : abs_max4(m.lo));
+  if (lane == 0 && p.col0 == 0 && a.lse_out != nullptr) a.lse_out[(int64_t)p.t * a.h_q + p.h] = m.lse;
+  if (lane == 0) s_amax[wave] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < HW; ++w) v = fmaxf(v, s_amax[w]);
+    __hip_atomic_fetch_max((uint32_t*)a.out_scale + p.t, 0x80000000u | __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Two-pass FP8 combine, encode pass: HPW whole rows per workgroup, merged again.
+template <int HPW, int CHUNK>
+__global__ __launch_bounds__(64 * HPW) void combine_fp8_encode_kernel(CombineArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const RowPart p = row_part<1>(a, (int64_t)blockIdx.x * HPW + wave);
+  const Merged m = merge_head<CHUNK, 1>(a, p.t, p.h, 0);
+  const uint32_t v = __hip_atomic_load((const uint32_t*)a.out_scale + p.t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float qscale;
+  if (v & 0x80000000u) {
+    const float amax = __uint_as_float(v & 0x7FFFFFFFu);
+    qscale = amax > 0.f ? amax / 448.0f : 1.0f;
+  } else {
+    qscale = __uint_as_float(v);
+  }
+  store_codes<1>(a, p, m, qscale);
+  if (p.h == 0 && lane == 0) a.out_scale[p.t] = qscale;
 }
 
 }  // namespace
@@ -2963,35 +2995,28 @@ hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t st
 }
 
 namespace {
-// The FP8 output's amax and encode passes.
-template <int CHUNK, bool STAGED>
+// The FP8 output's combine.  One launch while the whole grid fits one
+// workgroup per compute unit (quarter rows per wave up to as many rows as
+// CUs, half rows up to twice as many, then whole rows, 4, 8 or 16 per
+// workgroup), else the two passes.
+template <int CHUNK>
 void launch_combine_fp8(const CombineArgs& a, hipStream_t stream) {
-  const unsigned rows = (unsigned)(a.s_q * a.h_q);
-  const unsigned blocks4 = (unsigned)(a.s_q * ((a.h_q + 3) / 4));
-  if constexpr (STAGED) {
-    // The amax pass merges in half rows up to twice as many rows as CUs, else
-    // in 16 whole rows per workgroup; the encode pass, one row read per
-    // (token, head), in quarter rows for small batches (measured at s_q = 1 and
-    // 16: 13.7 -> 13.4 us and 25.6 -> 25.3 us per step).
-    if (a.heads_per_wg != 4)
-      hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 2, true>), dim3(rows / 2), dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((combine_fp8_amax_kernel<16, CHUNK, 1, true>),
-                         dim3((unsigned)(a.s_q * ((a.h_q + 15) / 16))), dim3(1024), 0, stream, a);
-    if (a.enc_quarter)
-      hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 4, true>), dim3(4 * rows), dim3(64), 0, stream, a);
-    else
-      hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK, 1, true>), dim3(blocks4), dim3(256), 0, stream, a);
-  } else if (a.heads_per_wg == -1) {              // a quarter of a row per wave
-    hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 4, STAGED>), dim3(rows), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 4, STAGED>), dim3(4 * rows), dim3(64), 0, stream, a);
-  } else if (a.heads_per_wg == 0) {               // half a row per wave
-    hipLaunchKernelGGL((combine_fp8_amax_kernel<4, CHUNK, 2, STAGED>), dim3(rows / 2), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((combine_fp8_encode_kernel<1, CHUNK, 2, STAGED>), dim3(2 * rows), dim3(64), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((combine_fp8_amax_kernel<16, CHUNK, 1, STAGED>), dim3((unsigned)(a.s_q * ((a.h_q + 15) / 16))),
-                       dim3(1024), 0, stream, a);
-    hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK, 1, STAGED>), dim3(blocks4), dim3(256), 0, stream, a);
+  const int64_t rows = (int64_t)a.s_q * a.h_q;
+  const int64_t cus = a.cus;
+  const dim3 g4((unsigned)(rows / 4)), g8((unsigned)(rows / 8)), g16((unsigned)(rows / 16));
+  if (rows <= cus)
+    hipLaunchKernelGGL((combine_fp8_kernel<4, CHUNK, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+  else if (rows <= 2 * cus)
+    hipLaunchKernelGGL((combine_fp8_kernel<4, CHUNK, 2>), dim3((unsigned)(rows / 2)), dim3(256), 0, stream, a);
+  else if (rows <= 4 * cus)
+    hipLaunchKernelGGL((combine_fp8_kernel<4, CHUNK, 1>), g4, dim3(256), 0, stream, a);
+  else if (rows <= 8 * cus)
+    hipLaunchKernelGGL((combine_fp8_kernel<8, CHUNK, 1>), g8, dim3(512), 0, stream, a);
+  else if (rows <= 16 * cus)
+    hipLaunchKernelGGL((combine_fp8_kernel<16, CHUNK, 1>), g16, dim3(1024), 0, stream, a);
+  else {
+    hipLaunchKernelGGL((combine_fp8_amax_kernel<16, CHUNK, 1>), g16, dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL((combine_fp8_encode_kernel<4, CHUNK>), g4, dim3(256), 0, stream, a);
   }
 }
 
@@ -3004,10 +3029,7 @@ hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
   if (a.out_dtype == kOutFp8) {
     if (!a.scale_ready)
       hipLaunchKernelGGL(combine_fp8_init_kernel, dim3((unsigned)((a.s_q + 255) / 256)), dim3(256), 0, stream, a);
-    if (a.merged != nullptr)
-      launch_combine_fp8<CHUNK, true>(a, stream);
-    else
-      launch_combine_fp8<CHUNK, false>(a, stream);
+    launch_combine_fp8<CHUNK>(a, stream);
   } else if (a.heads_per_wg == -1) {              // a quarter of a row per wave
     hipLaunchKernelGGL((combine_kernel<1, CHUNK, 4>), dim3(4 * rows), dim3(64), 0, stream, a.o_accum,
                        a.lse_accum, a.s_q, a.h_q, a.num_splits, a);

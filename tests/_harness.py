@@ -175,6 +175,20 @@ def assert_o_close(got, ref, tol=TOL_O, rel=0.0):
     assert worst <= 0, f"O error exceeds bound by {worst:.3g} (max-abs {float(np.max(err)):.3g})"
 
 
+def assert_fp8_close(codes, scale, O_fin):
+    """FP8 output against the oracle: the per-token scale within TOL_O / 448 of amax / 448,
+    and each decoded value within half an e4m3 ulp of O / scale (plus TOL_O) of O."""
+    import oracle
+    s_q = O_fin.shape[0]
+    amax_ref = np.abs(O_fin).reshape(s_q, -1).max(axis=1)
+    assert np.all(np.abs(scale - amax_ref / 448.0) <= TOL_O / 448.0 + 1e-7 * scale), "fp8 scale"
+    dec = oracle.e4m3_decode(codes) * scale[:, None, None]
+    x_bound = np.abs(O_fin) / scale[:, None, None] + TOL_O / scale[:, None, None]
+    bound = e4m3_half_ulp(x_bound) * scale[:, None, None] + TOL_O
+    assert not np.any(np.isnan(dec)), "NaN fp8 code"
+    assert np.all(np.abs(dec - O_fin) <= bound), "fp8 value error beyond bound"
+
+
 def e4m3_half_ulp(x):
     """Half the spacing of e4m3fn values around |x| (saturating range included)."""
     a = np.maximum(np.abs(x), 2.0 ** -6)
