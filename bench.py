@@ -139,7 +139,11 @@ def build_layers(s_q, n_pool, torch, W, seed0=1000, dtype="bf16"):
 
 
 def time_steps(layers, S, steps, warmup, torch, smla):
-    """Step time from graph replays; returns (us_per_step, event_us_per_step)."""
+    """Step time from graph replays, exactly `warmup` untimed then `steps` timed steps.
+
+    One graph holds one step of every layer in turn and is replayed whole; a step count
+    that is not a multiple of the layer count ends with the one-step graphs of the first
+    layers.  Returns (wall us/step, event us/step, steps, warmup)."""
     s_q = layers[0].inp.s_q
     scale = layers[0].inp.scale
     o_acc = torch.empty((S, s_q, 64, 512), device="cuda") if S > 1 else None
@@ -159,28 +163,37 @@ def time_steps(layers, S, steps, warmup, torch, smla):
             step(L)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all):
         for L in layers:
             step(L)
+    g_one = []
+    for L in layers:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(L)
+        g_one.append(g)
     n = len(layers)
-    reps_w = max(1, -(-warmup // n))
-    reps = max(1, -(-steps // n))
-    for _ in range(reps_w):
-        g.replay()
+
+    def replay(k):
+        full, rem = divmod(k, n)
+        for _ in range(full):
+            g_all.replay()
+        for i in range(rem):
+            g_one[i].replay()
+
+    replay(warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(reps):
-        g.replay()
+    replay(steps)
     e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    k = reps * n
-    return (t1 - t0) * 1e6 / k, e0.elapsed_time(e1) * 1e3 / k, k, reps_w * n
+    return (t1 - t0) * 1e6 / steps, e0.elapsed_time(e1) * 1e3 / steps, steps, warmup
 
 
 def time_cold(layers, S, steps, torch, smla, flush_bytes=1 << 30):
@@ -214,6 +227,36 @@ def time_cold(layers, S, steps, torch, smla, flush_bytes=1 << 30):
     return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
 
 
+def time_cold_kernel(layers, S, steps, torch, smla, flush_bytes=1 << 30):
+    """Median duration of the attention kernel alone with every cache flushed before it
+    (as time_cold, with partial-only calls; the direct path when S == 1)."""
+    s_q = layers[0].inp.s_q
+    scale = layers[0].inp.scale
+    o_acc = torch.empty((S, s_q, 64, 512), device="cuda") if S > 1 else None
+    lse_acc = torch.empty((S, s_q, 64), device="cuda") if S > 1 else None
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+
+    def call(L):
+        smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, kv_scale=L.kv_scale, sink=L.sink, o_accum=o_acc,
+                               lse_accum=lse_acc, out=None if S > 1 else L.out,
+                               out_scale=None if S > 1 else L.out_scale)
+
+    for L in layers:
+        call(L)
+    stream = torch.cuda.current_stream()
+    evs = []
+    for i in range(steps):
+        flush.fill_(float(i & 7))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call(layers[i % len(layers)])
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del flush
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+
 def sleep_cycles_for(ms, torch):
     """torch.cuda._sleep argument that keeps the GPU busy about `ms` milliseconds."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -228,10 +271,12 @@ def sleep_cycles_for(ms, torch):
 
 def kernel_durations(layers, S, reps, torch, smla):
     """Mean duration (us) of the attention kernel and of the combine, from HIP events on
-    the stream they are launched on.  Each kernel is timed as a batch of `reps`
-    back-to-back launches bracketed by one event pair; a GPU sleep queued first keeps
-    the stream backed up so the launches run without host gaps.  S == 1 times the
-    direct path (one kernel per step)."""
+    the stream they are launched on.  Each figure is a batch of `reps` back-to-back calls
+    bracketed by one event pair; a GPU sleep queued first keeps the stream backed up so
+    the launches run without host gaps.  The attention kernel is timed alone (partial-only
+    calls); the combine as the difference between whole steps and partial-only calls, so
+    it is the combine the step runs (an FP8 output's included: its counters are seeded by
+    the attention kernel).  S == 1 times the direct path (one kernel per step)."""
     s_q = layers[0].inp.s_q
     scale = layers[0].inp.scale
     stream = torch.cuda.current_stream()
@@ -256,8 +301,10 @@ def kernel_durations(layers, S, reps, torch, smla):
         return main, 0.0
     main = batch(lambda L: smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, kv_scale=L.kv_scale,
                                                   sink=L.sink, o_accum=o_acc, lse_accum=lse_acc))
-    comb = batch(lambda L: smla.combine_splits(o_acc, lse_acc, S, L.out, sink=L.sink, out_scale=L.out_scale))
-    return main, comb
+    step = batch(lambda L: smla.sparse_mla_decode(L.q, L.kv, L.indices, S, scale, kv_scale=L.kv_scale,
+                                                  sink=L.sink, o_accum=o_acc, lse_accum=lse_acc, out=L.out,
+                                                  out_scale=L.out_scale))
+    return main, max(step - main, 0.0)
 
 
 def traffic_for(S):
@@ -274,8 +321,11 @@ def traffic_for(S):
 
 
 def cpu_baseline(layer, seconds):
+    """The float64 oracle (oracle.attend + apply_sink) on the same inputs, on the host
+    cores: the median step of `seconds` of repeats with the BLAS pool at its default
+    size, then of a third as long with one thread."""
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     inp = layer.inp
 
     class Pool:
@@ -285,18 +335,27 @@ def cpu_baseline(layer, seconds):
 
     q64 = inp.q.astype(np.float64)
     sink = inp.sink.astype(np.float64)
-    times = []
-    t_end = time.perf_counter() + seconds
-    while time.perf_counter() < t_end or len(times) < 3:
-        t0 = time.perf_counter()
-        O, L = oracle.attend(q64, Pool(), inp.indices, inp.n_pool, inp.scale)
-        oracle.apply_sink(O, L, sink)
-        times.append(time.perf_counter() - t0)
+
+    def median_step(sec):
+        times = []
+        t_end = time.perf_counter() + sec
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            O, L = oracle.attend(q64, Pool(), inp.indices, inp.n_pool, inp.scale)
+            oracle.apply_sink(O, L, sink)
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(times)
+
+    med, n = median_step(seconds)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(float(np.median(times)) * 1e6, 1), "unit": "us/step", "cores": int(threads),
+    with threadpool_limits(limits=1):
+        med1, n1 = median_step(seconds / 3)
+    return {"value": round(med * 1e6, 1), "unit": "us/step", "cores": int(threads),
             "kind": "oracle",
             "sample": f"whole step ({inp.s_q} token x 64 heads x 640 slots, float64), median of "
-                      f"{len(times)} runs in {seconds:.0f} s on {_CORES} host cores"}
+                      f"{n} runs in {seconds:.0f} s on {_CORES} host cores",
+            "value_1_thread": round(med1 * 1e6, 1),
+            "sample_1_thread": f"the same step with the BLAS pool limited to 1 thread, median of {n1} runs"}
 
 
 def measure(name, S_arg, steps, warmup, reps, torch, smla, W):
@@ -306,11 +365,23 @@ def measure(name, S_arg, steps, warmup, reps, torch, smla, W):
     us, ev_us, k, w = time_steps(layers, S, steps, warmup, torch, smla)
     main_us, comb_us = kernel_durations(layers, S, reps, torch, smla)
     cold_us = time_cold(layers, S, max(20, steps // 4), torch, smla)
+    cold_main_us = time_cold_kernel(layers, S, max(20, steps // 4), torch, smla)
     step_bytes = STEP_BYTES_PER_TOKEN if dtype == "bf16" else MAIN_BYTES_PER_TOKEN_FP8 + 64 * 512 + 4
     step_gbs = step_bytes * s_q / (ev_us * 1e-6) / 1e9
     return dict(name=name, s_q=s_q, n_pool=n_pool, S=S, us=us, ev_us=ev_us, steps=k, warmup=w,
                 main_us=main_us, comb_us=comb_us, step_tbps=step_gbs / 1e3, cold_us=cold_us,
+                cold_main_us=cold_main_us,
                 layers=len(layers)), layers
+
+
+def kernel_bytes(name, S):
+    """Algorithmic bytes per token of the attention kernel: the gathered rows, Q and the
+    indices, plus the output when the kernel writes it (the direct path, S = 1)."""
+    pool = WORKLOADS[name][2]
+    b = MAIN_BYTES_PER_TOKEN if pool == "bf16" else MAIN_BYTES_PER_TOKEN_FP8
+    if S == 1:
+        b += OUT_BYTES if pool == "bf16" else 64 * 512 + 4
+    return b
 
 
 def _csv_rows(directory, suffix):
@@ -589,12 +660,17 @@ def main():
     log(f"{args.workload}: {head['us']:.2f} us/step (events {head['ev_us']:.2f}), attention kernel "
         f"{head['main_us']:.2f} us, combine {head['comb_us']:.2f} us, cold step {head['cold_us']:.2f} us, S={S}")
     pool_dtype = WORKLOADS[args.workload][2]
-    main_bytes = (MAIN_BYTES_PER_TOKEN if pool_dtype == "bf16" else MAIN_BYTES_PER_TOKEN_FP8) * s_q
+    main_bytes = kernel_bytes(args.workload, S) * s_q
     achieved = main_bytes / (head["main_us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(S),
                 "kernel": kernel_label(s_q, S, pool_dtype),
                 "bytes_per_launch": main_bytes, "mean_launch_us": round(head["main_us"], 3),
+                "cache": "warm: back-to-back launches cycling over the layers, whose gathered rows stay in "
+                         "the last-level cache at this size; cold_* flush every cache before each launch",
+                "cold_launch_us": round(head["cold_main_us"], 3),
+                "cold_achieved": round(main_bytes / (head["cold_main_us"] * 1e-6) / 1e9, 1),
+                "cold_frac": round(main_bytes / (head["cold_main_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "mfma_frac": round(FLOPS_PER_TOKEN * s_q / (head["main_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5)}
     peaks = measured_peaks(torch)
     log(f"measured peaks: {peaks}")
@@ -614,10 +690,11 @@ def main():
                             torch, smla, W)
             del ls
             torch.cuda.empty_cache()
-            mb = (MAIN_BYTES_PER_TOKEN if WORKLOADS[name][2] == "bf16" else MAIN_BYTES_PER_TOKEN_FP8) * r["s_q"]
+            mb = kernel_bytes(name, r["S"]) * r["s_q"]
             sweep[name] = {"s_q": r["s_q"], "pool": WORKLOADS[name][2], "num_splits": r["S"],
                            "us_per_step": round(r["ev_us"], 2), "cold_us_per_step": round(r["cold_us"], 2),
                            "attention_kernel_us": round(r["main_us"], 2), "combine_us": round(r["comb_us"], 2),
+                           "cold_attention_kernel_us": round(r["cold_main_us"], 2),
                            "step_hbm_tbps": round(r["step_tbps"], 3),
                            "kernel_hbm_frac": round(mb / (r["main_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                            "kernel_mfma_frac": round(FLOPS_PER_TOKEN * r["s_q"] / (r["main_us"] * 1e-6) / 1e12
@@ -628,14 +705,17 @@ def main():
     line = {
         "metric": METRIC, "value": round(head["ev_us"], 3), "unit": "us/step", "n_gpus": 1,
         "steps": head["steps"], "warmup": head["warmup"], "ms_per_step": round(head["ev_us"] / 1e3, 6),
-        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if pool_dtype == "bf16" else "fp8_e4m3 (bf16 MFMA)",
         "data": "synthetic (seeded N(0,1) bf16 pools, uniform unique top-k indices)",
         "config": {"workload": f"{LABELS[args.workload]}: s_q={s_q}, h_q=64, d_qk=576, d_v=512, topk=640, "
                                f"pool {head['n_pool']} {pool_dtype} rows x {head['layers']} layers, sink on, "
                                f"num_splits={S}",
                    "global_batch": s_q, "num_splits": S,
-                   "timing": "HIP graph replay over the layers (warm: the rows all layers gather stay in the "
-                             "last-level cache at this size); cold_us_per_step flushes the caches before each step"},
+                   "timing": f"exactly {args.warmup} untimed then {args.steps} timed steps, HIP graph replay "
+                             "cycling over the layers; warm: the rows all layers gather stay in the 256 MB "
+                             "last-level cache at this size, so value and roofline are warm-cache figures; "
+                             "cold_us_per_step flushes every cache before each step"},
         "hbm_tbps": round(head["step_tbps"], 4),
         "cold_us_per_step": round(head["cold_us"], 3),
         "wall_us_per_step": round(head["us"], 3),

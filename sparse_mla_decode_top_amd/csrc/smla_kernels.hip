@@ -12,7 +12,8 @@
 //   * decode_kernel8h (CS = 2): 8 waves, half of the heads each.
 //   * decode_kernel4t (CS = 4 or 8): 4 waves, one 16-head tile each (CS = 8:
 //     and half its columns).
-//   * decode_kernel8m: a mixed launch for more jobs than compute units.
+//   * decode_kernel8m: a mixed launch for more jobs than compute units
+//     (decode_kernel8p's body, then decode_kernel8h's for a short last round).
 //   * decode_kernel (fewer heads, or CS = 1 with an FP8 pool or a direct FP8
 //     output): 4 waves, each workgroup 512 / CS output columns of all heads.
 // The head-part kernels let no workgroup repeat another's QK^T.  The notes
@@ -24,7 +25,9 @@
 // scores; few jobs then still occupy many compute units).
 //   * The 64 slots of a KV block share one LDS tile, gathered by index with
 //     16-byte direct-to-LDS loads (global_load_lds_dwordx4) in which 8 lanes
-//     fetch one contiguous 128-byte segment of a row; two tiles double-buffer
+//     fetch one contiguous 128-byte segment of a row (FP8 pool: 4 lanes a
+//     64-byte segment of e4m3 codes, converted to bf16 in registers as the
+//     MFMA operands are read); two tiles double-buffer
 //     the gather of block b+1 behind the compute of block b, its DMAs spread
 //     over block b's QK^T MFMAs.  Masked slots are never read: their tile
 //     rows are zero-filled, or copied from a zero row.
@@ -51,19 +54,14 @@
 //     hi + lo carries p to about 2^-17 relative.
 //   * Outputs are staged through LDS and stored in whole-line pieces.
 //
-// decode8_body (the 8-wave column-part layout; now the 4/8-part tail of the
-// mixed launch): 8 waves, two per SIMD, for 64 heads in 2, 4 or 8 column
-// parts.  The two waves on a SIMD own the same 16 heads and split each
-// block's slots, so the hardware overlaps one's softmax and LDS reads with
-// the other's MFMAs; the two slot halves of a head merge in the epilogue as
-// two splits would.
-//
 // decode_kernel8p / 8h / 4t: the waves that share a head tile score a part
 // of each block's slots each, trade their bf16 weights through LDS and
 // accumulate every slot into their own part of the columns, under one
-// shared frame per head.  With more jobs than compute units, a last round
-// that fills at most half of them takes 2, 4 or 8 parts: decode_kernel8m
-// runs both in one launch.
+// shared frame per head; the two waves of a SIMD in the 8-wave kernels
+// score different slots, so the hardware overlaps one's softmax and LDS
+// reads with the other's MFMAs.  With more jobs than compute units, a last
+// round that fills at most half of them takes 2, 4 or 8 parts (a bf16 pool
+// and 64 heads: 2, in the same launch, decode_kernel8m).
 //
 // combine kernel: split-major partials -> final output (+ sink, cast).
 
@@ -119,15 +117,79 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_row[1152];
 //   with the LDS bank-conflict counter over the kernel's exact address
 //   streams; several XOR patterns that look conflict free on paper are 2-way
 //   conflicted there.
-// The FP8 code tile is "quartet-major": code chunk c of row r at position
-//     (c >> 2) * 256 + r * 4 + (c & 3),
-// so 4 lanes fetch 64 contiguous bytes of a row.
+// The FP8 code tile has a layout of its own (below).
 // ---------------------------------------------------------------------------
 // Chunk-slot XOR of tile row r.
 __host__ __device__ constexpr int rsw(int r) { return r & 7; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ---------------------------------------------------------------------------
+// FP8 code tile (e4m3 pool rows), "quartet-major" and swizzled.  A row is 36
+// chunks of 16 codes, grouped in 9 quartets of 4 chunks (64 bytes).  Chunk c
+// of tile row r sits at 16-byte position
+//     (c >> 2) * 256 + r * 4 + ((c & 3) ^ csw(r)),   csw(r) = (r >> 2) & 3.
+// * Gather: one load instruction fills one quartet of 16 rows; lanes 4k..4k+3
+//   fetch the 64 contiguous bytes of one row, in swizzled order.
+// * The MFMA operands are read from the codes and converted to bf16 in
+//   registers (exact): K fragments as 8-byte reads along a row, V^T fragments
+//   with the gfx950 8-bit transpose read ds_read_b64_tr_b8.  In each group of
+//   16 lanes that read reads 8 bytes per lane and hands lane i, as its byte k,
+//   byte (i & 7) of what lane 2k + (i >> 3) read (measured on the MI355X): with
+//   lane j pointed at half (j & 1) of row R(j >> 1), lane i receives column i
+//   of rows R(0) .. R(7) -- 8 slots of one value column, the V^T operand.
+//   The XOR puts both read streams on distinct LDS banks (2 cycles per
+//   512-byte read).
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int csw(int r) { return (r >> 2) & 3; }
+
+// Byte offset within a quartet of the chunk that gathering lane l fetches: row
+// l >> 2 of a group of 16 rows starting at a multiple of 16.
+__device__ __forceinline__ int fp8_gather_chunk(int lane) { return ((lane & 3) ^ csw(lane >> 2)) * 16; }
+
+// Eight e4m3fn codes (two dwords, code k in byte k) as bf16 (exact for every code).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true));
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// Per-lane byte offsets of the FP8 operand reads (lane = 16 G + j).
+//   k[p]: K fragment of a k-step of parity p, row j of the slot tile (add
+//         1024 per slot tile and 4096 per k-step pair): dims 32 ks + 8G .. +8,
+//         i.e. chunk 2 p + (G >> 1), half G & 1.
+//   v[m]: V^T fragment of a column chunk c with c & 3 = m (add 4096 per
+//         quartet c >> 2 and 2048 per 32-slot k-step).  Its k-elements are
+//         the slots that the weight operand holds, as in the bf16 fragment:
+//         4G .. 4G + 3, then 16 + 4G .. 16 + 4G + 3 of the k-step; so lane j
+//         reads half j & 1 of slot 16 (j >> 3) + 4G + ((j >> 1) & 3), whose
+//         csw is G.
+struct Fp8Offsets {
+  int k[2];
+  int v[4];
+};
+__device__ __forceinline__ Fp8Offsets fp8_offsets(int lane) {
+  const int j = lane & 15, G = lane >> 4;
+  Fp8Offsets o;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) o.k[p] = j * 64 + (((2 * p + (G >> 1)) ^ csw(j)) * 16) + (G & 1) * 8;
+  const int vrow = (16 * (j >> 3) + 4 * G + ((j >> 1) & 3)) * 64 + (j & 1) * 8;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o.v[m] = vrow + ((m ^ G) * 16);
+  return o;
+}
+__device__ __forceinline__ bf16x8 fp8_kfrag(uint32_t addr) {
+  return e4m3x8_to_bf16(*(const __attribute__((address_space(3))) u32x2*)(uintptr_t)addr);
+}
+__device__ __forceinline__ bf16x8 fp8_vfrag(uint32_t addr) {
+  typedef int i32x2v __attribute__((ext_vector_type(2)));
+  const i32x2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2v*)(uintptr_t)addr);
+  return e4m3x8_to_bf16(u32x2{(uint32_t)r[0], (uint32_t)r[1]});
 }
 
 // Nine 16-byte direct-to-LDS loads from one row per lane.  The hardware adds
@@ -464,7 +526,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
         const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
         if (valid_of(row_idx)) {
-          const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + (lane & 3) * 16;
+          const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + fp8_gather_chunk(lane);
           dma_quartets(src, __builtin_amdgcn_readfirstlane(lds_base));
         } else {
           uint8_t* dst = s_tile + buf * kBufBytes + wave * 1024 + lane * 16;
@@ -478,6 +540,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int sw_k = rsw(hl);
     const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
     const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
+    const Fp8Offsets f8 = fp8_offsets(lane);                  // FP8 pool: K and V^T reads of the codes
     const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
     const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
     int vb[4];                                                  // column tile ct & 3
@@ -560,7 +623,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           }
         } else {
           const int row_idx = __shfl(idx_nxt, 16 * wave + (lane >> 2));
-          gsrc[0] = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
+          gsrc[0] = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+                    fp8_gather_chunk(lane);
           gbase[0] = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + wave * 1024);
         }
       }
@@ -585,51 +649,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       constexpr int kDmas = KV_FP8 ? 9 : 18;
       const int idx_after = load_idx(b + 2);
 
-      const uint8_t* tile;
-      if (!KV_FP8) {
-        tile = s_tile + cur * kTileBytes;
-      } else {
-        // Expand block b's e4m3 codes into the bf16 tile (exact conversion).
-        uint8_t* btile = s_tile + 2 * kCodeTileBytes;
-        const uint8_t* ctile = s_tile + cur * kCodeTileBytes;
-#pragma unroll 6
-        for (int j = 0; j < 18; ++j) {
-          const int p = j * kThreads + tid;           // bf16 chunk position
-          const int o = p >> 9, r = (p >> 3) & 63;
-          const int c = 8 * o + ((p & 7) ^ rsw(r));   // bf16 chunk of row r
-          const int cc = c >> 1;                      // code chunk holding it
-          const u32x2 codes =
-              *(const u32x2*)(ctile + ((cc >> 2) * 256 + r * 4 + (cc & 3)) * 16 + (c & 1) * 8);
-          // v_cvt_scalef32_pk_bf16_fp8 with scale 1 is exact for every e4m3fn code.
-          u32x4 ov;
-          ov[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
-          ov[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
-          ov[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
-          ov[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
-          *(u32x4*)(btile + p * 16) = ov;
-        }
-        lds_barrier();
-        tile = btile;
-      }
-
       // The block is processed as two halves of 32 slots (slot tiles 0-1 and
       // 2-3).  The softmax of one half is independent of the MFMAs that run
       // next to it, so its VALU work is issued in small steps between them:
       //   QK(h0) | QK(h1) + softmax(h0) | PV(h0) + softmax(h1) | PV(h1)
       // The first half with a valid slot fixes a head's frame.
-      const uint32_t tl = lds_addr(tile);
+      const uint32_t tl = lds_addr(s_tile + cur * kBufBytes);
       // four bases keep every offset within the 16-bit ds_read field
-      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
-                                 opaque(tl + kb1 + 65536)};
+      uint32_t kbase[4], vbase[4];
+      // V^T of this workgroup's columns: column tile ct (local) is global
+      // tile kCt * part + ct; 4 column tiles per 128-byte octet (bf16) or per
+      // 64-byte quartet (FP8 codes)
+      if constexpr (KV_FP8) {
+        kbase[0] = opaque(tl + f8.k[0]);
+        kbase[1] = opaque(tl + f8.k[1]);
+        kbase[2] = kbase[3] = 0u;
+        const uint32_t tlv = tl + job.part * (kCt / 4) * 4096;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + f8.v[m]);
+      } else {
+        kbase[0] = opaque(tl + kb0);
+        kbase[1] = opaque(tl + kb1);
+        kbase[2] = opaque(tl + kb0 + 65536);
+        kbase[3] = opaque(tl + kb1 + 65536);
+        const uint32_t tlv = tl + job.part * (kCt / 4) * 8192;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + vb[m]);
+      }
       auto kfrag = [&](int ks, int st) -> bf16x8 {
+        if constexpr (KV_FP8) return fp8_kfrag(kbase[ks & 1] + (ks >> 1) * 4096 + st * 1024);
         const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
         return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
       };
-      // V^T of this workgroup's columns: column tile ct (local) is global
-      // tile kCt * part + ct; 4 column tiles per 128-byte octet
-      const uint32_t tlv = tl + job.part * (kCt / 4) * 8192;
-      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
       auto vfrag = [&](int ct, int kk) -> bf16x8 {
+        if constexpr (KV_FP8) return fp8_vfrag(vbase[ct & 3] + (ct >> 2) * 4096 + kk * 2048);
         const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
         const i16x4 v1 =
@@ -879,454 +932,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     seed_fp8_combine(a.out_scale, a.out, t, h_q);
 }
 
-// ---------------------------------------------------------------------------
-// The attention kernel with 8 waves, two per SIMD (h_q = 64, CS >= 2).
-// Wave w owns heads [16 (w & 3), +16) and slots [32 (w >> 2), +32) of every
-// block.  The two waves that share a SIMD (w and w + 4) own the same heads and
-// split the slots, so while one runs its softmax, LDS reads or gather issue,
-// the SIMD's matrix core can run the other's MFMAs; the one-wave-per-SIMD
-// kernel above has to interleave those itself and keeps its MFMA pipe busy
-// only about half the time.  Each wave runs its own online softmax over its
-// slots with its own integer frame per head; the two halves of a head merge
-// their (M, l, O) through LDS at the end, as two splits would.  Two waves per
-// SIMD leave 256 registers a wave, so the accumulators of 16 heads take
-// 128 / CS of them: the kernel serves 2, 4 or 8 column parts.
-// ---------------------------------------------------------------------------
+// The 8-wave kernels below (two waves per SIMD): 64 heads, 512 threads.
 constexpr int kWaves8 = 8;
 constexpr int kThreads8 = 64 * kWaves8;
-
-// LDS of decode8_body: the two tiles, then the per-block scale and bias rows,
-// the epilogue's frame / denominator exchange, the LSEs and the restart flag.
-constexpr int kLds8Scale = 2 * kTileBytes;
-constexpr int kLds8Bias = kLds8Scale + 2 * kBlk * 4;
-constexpr int kLds8Ml = kLds8Bias + 2 * kBlk * 4;
-constexpr int kLds8Lse = kLds8Ml + 2 * 2 * 64 * 4;
-constexpr int kLds8Restart = kLds8Lse + 64 * 4;
-constexpr int kLds8Bytes = kLds8Restart + 16;
-
-// The body of the 8-wave column-part layout for workgroup `block` of its
-// launch, on the LDS at `smem` (kLds8Bytes).  The head-tile kernels have
-// replaced it as a kernel of its own; it runs the 4- and 8-part tail of the
-// mixed launch (512-thread workgroups).
-template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
-__device__ __forceinline__ void decode8_body(
-    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
-    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, const DecodeArgs& a, int block, uint8_t* smem) {
-  static_assert(CS >= 2, "the 8-wave layout needs at least two column parts");
-  constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
-  constexpr int kCols = 512 / CS;
-  constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
-  constexpr int kStageBytes = 64 * kStagePitch;   // the 64 staged head rows of one slot half
-  static_assert(2 * kStageBytes <= 2 * kTileBytes, "staging must fit in the tile buffers");
-  uint8_t* const s_tile = smem;                                                  // [2 * kTileBytes]
-  float (*const s_scale)[kBlk] = reinterpret_cast<float (*)[kBlk]>(smem + kLds8Scale);   // [2][kBlk]
-  // [2][kBlk]: 0 for a valid slot, kMaskedScore for a masked one
-  float (*const s_bias)[kBlk] = reinterpret_cast<float (*)[kBlk]>(smem + kLds8Bias);
-  // [slot half][frame M, denominator l][head]
-  float (*const s_ml)[2][64] = reinterpret_cast<float (*)[2][64]>(smem + kLds8Ml);
-  float* const s_lse = reinterpret_cast<float*>(smem + kLds8Lse);               // [64]
-  int& s_restart = *reinterpret_cast<int*>(smem + kLds8Restart);
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int hl = lane & 15;               // head within the head tile (MFMA column)
-  const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
-  const int hq = wave & 3;                // head tile: heads [16 hq, 16 hq + 16)
-  const int sg = wave >> 2;               // slot half: slots [32 sg, 32 sg + 32) of each block
-  const int head = 16 * hq + hl;
-
-  const Job job = decode_job<CS>(block, num_splits, n_blocks, job0, s_q * num_splits);
-  if (!job.live) return;                          // padding of the grid (whole workgroup)
-  const int t = job.t;
-  const int32_t* idx_row = indices + (int64_t)t * topk;
-
-  float M_run = kNoFrame;             // integer frame of this lane's head over this wave's slots
-  float m_seen = kMaskedScore;        // largest score seen so far
-  float l_run = 0.f;                  // this lane's share of the denominator
-  if (tid == 0) s_restart = 0;        // ordered before its readers by the loop barriers
-  f32x4 acc[kCt];                     // O^T: column tile ct -> columns kCols * part + 16ct + 4G + i
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (job.b0 < job.b1) {
-    auto load_idx = [&](int b) -> int {
-      return idx_row[min(b * kBlk + lane, topk - 1)];
-    };
-    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
-    auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
-    const float scale_log2 = a.scale_log2;
-    bf16x8 qf[18];                    // Q fragments: head, dims 32ks + 8G .. +8
-
-    const uint32_t tile_lds0 = lds_addr(s_tile);
-    constexpr int kBufBytes = KV_FP8 ? kCodeTileBytes : kTileBytes;
-    // Gather rows: bf16, wave w fills rows [8w, 8w + 8) (lanes 8k..8k+7 one
-    // row, chunk (l & 7) ^ (row & 7) of each octet); FP8, waves 0-3 fill rows
-    // [16w, 16w + 16) (4 lanes a row, chunk l & 3 of each quartet).
-    const bool gathers = !KV_FP8 || wave < 4;
-
-    // Every gathering lane issues its 9 DMAs (a masked row copies the zero row),
-    // so a gathering wave always has exactly 9 of them in flight (the first pass
-    // counts on it).
-    auto issue_gather = [&](int idx_lane, int buf) {
-      if (!KV_FP8) {
-        const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
-        const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
-        const uint8_t* src = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-                             (((lane & 7) ^ rsw(lane >> 3)) * 16);
-        dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
-      } else if (gathers) {
-        const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
-        const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
-        const uint8_t* src =
-            (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
-        dma_quartets(src, __builtin_amdgcn_readfirstlane(lds_base));
-      }
-    };
-
-    // per-lane LDS byte offsets of the operand reads (the tile layout above)
-    const int sw_k = rsw(hl);
-    const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
-    const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
-    const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
-    const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
-    int vb[4];                                                  // column tile ct & 3
-#pragma unroll
-    for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
-
-    // ---- prologue: Q rows (heads) [8w, 8w + 8) into LDS by wave w, at kQOffset
-    int idx_cur;
-    {
-      const int r0 = 8 * wave + (lane >> 3);
-      const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
-      const uint8_t* qbase = (const uint8_t*)(q_ptr + (int64_t)t * h_q * 576);
-      idx_cur = load_idx_and_q1(idx_row + min(job.b0 * kBlk + lane, topk - 1), qbase + (int64_t)r0 * 1152 + chunk,
-                                __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + wave * 1024));
-    }
-
-    auto run_pass = [&](const bool first) __attribute__((always_inline)) -> bool {
-    bool overflow = false;
-    if (!first) idx_cur = load_idx(job.b0);
-    idx_cur = slot_in(job.b0) ? idx_cur : -1;
-    issue_gather(idx_cur, 0);
-    int idx_nxt = load_idx(job.b0 + 1);
-    bool valid_cur = valid_of(idx_cur);
-    if (first) {
-      // Q rows landed.  They were issued first; behind them stay in flight, while
-      // the Q fragments are read: block b0's 9 DMAs (bf16: every wave; FP8: the
-      // gathering waves 0-3) and, with the look-ahead, the next index load.
-      if (gathers) {
-        if (PREFETCH)
-          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      } else {
-        if (PREFETCH)
-          asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      lds_barrier();
-      const uint32_t qt = lds_addr(s_tile) + kQOffset + hq * 2048;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
-        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
-      }
-    }
-    // FP8: block b0's row scales (read at the top of the block loop).
-    float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
-
-    for (int b = job.b0; b < job.b1; ++b) {
-      const int cur = (b - job.b0) & 1;
-      wait_vmem_all();          // this wave's share of block b has landed
-      if (wave == 0) {
-        s_bias[cur][lane] = valid_cur ? 0.f : kMaskedScore;
-        if (KV_FP8) s_scale[cur][lane] = sc_cur;
-      }
-      lds_barrier();            // ... and every wave's; block b-1 fully consumed
-
-      // Block b+1: one DMA per QK^T k-step pair (masked rows and rows past the
-      // job's last block copy the zero row).
-      bool valid_nxt = false;
-      float sc_nxt = 0.f;
-      const uint8_t* gsrc = g_zero_row;
-      uint32_t gbase = 0u;
-      if (PREFETCH) {
-        idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
-        valid_nxt = valid_of(idx_nxt);
-        if (KV_FP8 && wave == 0 && valid_nxt) sc_nxt = a.kv_scale[idx_nxt];
-        if (!KV_FP8) {
-          const int row_idx = __shfl(idx_nxt, 8 * wave + (lane >> 3));
-          gsrc = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-                 (((lane & 7) ^ rsw(lane >> 3)) * 16);
-          gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + wave * 1024);
-        } else {
-          const int row_idx = __shfl(idx_nxt, 16 * (wave & 3) + (lane >> 2));
-          gsrc = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
-          gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + (wave & 3) * 1024);
-        }
-      }
-      auto gather_dma = [&](const int d) __attribute__((always_inline)) {
-        if (!PREFETCH || !gathers) return;
-        constexpr int L = KV_FP8 ? 4096 : 8192, Gs = KV_FP8 ? 64 : 128;
-        switch (d) {
-          case 0: dma_one<L, Gs, 0>(gsrc, gbase); break;
-          case 1: dma_one<L, Gs, 1>(gsrc, gbase); break;
-          case 2: dma_one<L, Gs, 2>(gsrc, gbase); break;
-          case 3: dma_one<L, Gs, 3>(gsrc, gbase); break;
-          case 4: dma_one<L, Gs, 4>(gsrc, gbase); break;
-          case 5: dma_one<L, Gs, 5>(gsrc, gbase); break;
-          case 6: dma_one<L, Gs, 6>(gsrc, gbase); break;
-          case 7: dma_one<L, Gs, 7>(gsrc, gbase); break;
-          default: dma_one<L, Gs, 8>(gsrc, gbase); break;
-        }
-      };
-      const int idx_after = load_idx(b + 2);
-
-      const uint8_t* tile;
-      if (!KV_FP8) {
-        tile = s_tile + cur * kTileBytes;
-      } else {
-        // Expand block b's e4m3 codes into the bf16 tile (exact conversion).
-        uint8_t* btile = s_tile + 2 * kCodeTileBytes;
-        const uint8_t* ctile = s_tile + cur * kCodeTileBytes;
-#pragma unroll 3
-        for (int j = 0; j < 9; ++j) {
-          const int p = j * kThreads8 + tid;
-          const int o = p >> 9, r = (p >> 3) & 63;
-          const int c = 8 * o + ((p & 7) ^ rsw(r));
-          const int cc = c >> 1;
-          const u32x2 codes =
-              *(const u32x2*)(ctile + ((cc >> 2) * 256 + r * 4 + (cc & 3)) * 16 + (c & 1) * 8);
-          u32x4 ov;
-          ov[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
-          ov[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
-          ov[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
-          ov[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
-          *(u32x4*)(btile + p * 16) = ov;
-        }
-        lds_barrier();
-        tile = btile;
-      }
-
-      const uint32_t tl = lds_addr(tile);
-      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
-                                 opaque(tl + kb1 + 65536)};
-      auto kfrag = [&](int ks, int st) -> bf16x8 {
-        const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
-        return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
-      };
-      const uint32_t tlv = tl + job.part * (kCt / 4) * 8192;
-      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
-      auto vfrag = [&](int ct, int kk) -> bf16x8 {
-        const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
-        const i16x4 v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)(vp + 2048));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, v0);
-        const u32x2 w1 = __builtin_bit_cast(u32x2, v1);
-        return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-      };
-
-      // ---- S^T = K . Q^T over this wave's 2 slot tiles (2 sg, 2 sg + 1);
-      // MFMAs on one accumulator in k-step pairs (the faster issue order).
-      constexpr int kAheadK = 2, kRing = kAheadK + 2, kAheadV = kCt < 4 ? kCt : 4;
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      {
-        bf16x8 kf[kRing][2];
-#pragma unroll
-        for (int a0 = 0; a0 < kAheadK; ++a0)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) kf[a0][u] = kfrag(a0, 2 * sg + u);
-#pragma unroll
-        for (int j = 0; j < 9; ++j) {
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int ka = 2 * j + e + kAheadK;
-            if (ka < 18) {
-#pragma unroll
-              for (int u = 0; u < 2; ++u) kf[ka % kRing][u] = kfrag(ka, 2 * sg + u);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int ks = 2 * j + e;
-              sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % kRing][u], qf[ks], sacc[u], 0, 0, 0);
-            }
-          gather_dma(j);                // the next block's DMAs 0..8, one per k-step pair
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      // ---- softmax of this wave's 32 slots (lane: slots 32 sg + 16u + 4G + i).
-      // The first V^T fragments of PV are requested after the bias reads and
-      // before the softmax math, so their LDS latency hides behind it (LDS
-      // returns in order: the softmax waits only for the bias).
-      f32x4 bias[2], rsc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bias[u] = *(const f32x4*)&s_bias[cur][32 * sg + 16 * u + 4 * G];
-        if (KV_FP8) rsc[u] = *(const f32x4*)&s_scale[cur][32 * sg + 16 * u + 4 * G];
-      }
-      bf16x8 vf[kAheadV + 1];
-#pragma unroll
-      for (int a0 = 0; a0 < kAheadV; ++a0) vf[a0] = vfrag(a0, sg);
-      float tv[8];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          tv[4 * u + i] = KV_FP8 ? fmaf(sacc[u][i] * scale_log2, rsc[u][i], bias[u][i])
-                                 : fmaf(sacc[u][i], scale_log2, bias[u][i]);
-      float m = fmaxf(fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3])), fmaxf(fmaxf(tv[4], tv[5]), fmaxf(tv[6], tv[7])));
-      m = rows_max(m);
-      m_seen = fmaxf(m_seen, m);
-      if (M_run == kNoFrame && m > kMaskedScore) M_run = floorf(m);
-      overflow |= m > M_run + kFrameSlack;
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float tt = tv[e];
-        const float fl = floorf(tt);
-        const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
-        float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
-        l_run += p;
-        if (KV_FP8) p *= rsc[e >> 2][e & 3];
-        pv[e] = p;
-      }
-      uint32_t ph[4], pl[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t h2 = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
-        ph[j] = h2;
-        pl[j] = pack_bf16x2(pv[2 * j] - __uint_as_float(h2 << 16), pv[2 * j + 1] - __uint_as_float(h2 & 0xFFFF0000u));
-      }
-
-      // ---- O^T += V^T . P^T over this wave's slots (k-step sg of the block)
-      {
-        const bf16x8 pfh = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
-        const bf16x8 pfl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
-#pragma unroll
-        for (int ct = 0; ct < kCt; ++ct) {
-          if (ct + kAheadV < kCt) vf[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, sg);
-          __builtin_amdgcn_sched_barrier(0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfh, acc[ct], 0, 0, 0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfl, acc[ct], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      valid_cur = valid_nxt;
-      sc_cur = sc_nxt;
-      idx_nxt = idx_after;
-    }
-    wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
-    return overflow;
-    };
-
-    const bool overflow = run_pass(true);
-    if (__any(overflow) && lane == 0) s_restart = 1;
-    lds_barrier();              // also: every wave is past its last tile read
-    if (s_restart != 0) {
-      // a slot half without a valid slot keeps no frame (its weights stay 0)
-      M_run = m_seen > kMaskedScore ? floorf(m_seen) : kNoFrame;
-      l_run = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      run_pass(false);
-    }
-  }
-
-  // ---- epilogue: merge the two slot halves of every head ---------------------
-  // Each half has (frame M_h, denominator l_h, accumulator acc_h) relative to
-  // its own frame; with M = the larger frame of the halves that saw weight,
-  // f_h = 2^(M_h - M) (an exact power of two), l = l_0 f_0 + l_1 f_1 and
-  // O = (acc_0 f_0 + acc_1 f_1) / l.  Both waves of a head compute the same l
-  // and M from the exchanged values.
-  const float l_w = rows_sum(l_run);
-  if (G == 0) {
-    s_ml[sg][0][head] = M_run;
-    s_ml[sg][1][head] = l_w;
-  }
-  lds_barrier();              // the exchange, and every wave past its last tile read
-  float fscale;
-  {
-    const float M0 = s_ml[0][0][head], L0 = s_ml[0][1][head];
-    const float M1 = s_ml[1][0][head], L1 = s_ml[1][1][head];
-    const bool v0 = L0 > 0.f, v1 = L1 > 0.f;
-    const float M = v0 ? (v1 ? fmaxf(M0, M1) : M0) : M1;
-    const float f0 = v0 ? __builtin_amdgcn_ldexpf(1.0f, (int)fmaxf(M0 - M, -256.f)) : 0.f;
-    const float f1 = v1 ? __builtin_amdgcn_ldexpf(1.0f, (int)fmaxf(M1 - M, -256.f)) : 0.f;
-    const float l = L0 * f0 + L1 * f1;
-    const bool any = l > 0.f;
-    const float lse = any ? M + __builtin_amdgcn_logf(l) : kNegInf;
-    float oscale = any ? 1.0f / l : 0.f;
-    if (DIRECT && a.sink != nullptr && any) {
-      const float z = a.sink[head] * kLog2e - lse;
-      oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
-    }
-    fscale = (sg == 0 ? f0 : f1) * oscale;
-    if (sg == 0 && G == 0) s_lse[head] = lse;
-  }
-
-  // Staging: slot half h writes its scaled rows at s_tile + h * kStageBytes
-  // (row = head); after the barrier wave w sums the two halves of heads
-  // [8w, 8w + 8) and stores them in whole-line pieces.
-  {
-    uint8_t* stg = s_tile + sg * kStageBytes + head * kStagePitch + 16 * G;
-#pragma unroll
-    for (int ct = 0; ct < kCt; ++ct) *(f32x4*)(stg + 64 * ct) = acc[ct] * fscale;
-  }
-  lds_barrier();
-  const uint8_t* st0 = s_tile + 8 * wave * kStagePitch;
-  const uint8_t* st1 = st0 + kStageBytes;
-  const int64_t row0 = (DIRECT ? (int64_t)t * h_q : ((int64_t)job.s * s_q + t) * h_q) + 8 * wave;
-  const int col0 = job.part * kCols;
-  if (!DIRECT || a.out_dtype == kOutF32) {       // 1 KB of whole row pieces per instruction
-    float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + col0;
-#pragma unroll
-    for (int j = 0; j < 8 * kCols / 256; ++j) {
-      const int f = 256 * j + 4 * lane;
-      const int r = f / kCols, c = f % kCols;
-      *(f32x4*)(dst + r * 512 + c) =
-          *(const f32x4*)(st0 + r * kStagePitch + 4 * c) + *(const f32x4*)(st1 + r * kStagePitch + 4 * c);
-    }
-  } else {                                       // bf16 (a direct FP8 output never takes this kernel)
-    constexpr int kLanesPerRow = kCols / 8, kRowsPer = 64 / kLanesPerRow;
-    const int rr = lane / kLanesPerRow, cc = 8 * (lane % kLanesPerRow);
-    uint16_t* dst = (uint16_t*)a.out + row0 * 512 + col0 + cc;
-#pragma unroll
-    for (int j = 0; j < 8 / kRowsPer; ++j) {
-      const int r = kRowsPer * j + rr;
-      const f32x4 v0 = *(const f32x4*)(st0 + r * kStagePitch + 4 * cc) + *(const f32x4*)(st1 + r * kStagePitch + 4 * cc);
-      const f32x4 v1 =
-          *(const f32x4*)(st0 + r * kStagePitch + 4 * cc + 16) + *(const f32x4*)(st1 + r * kStagePitch + 4 * cc + 16);
-      *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
-                                       pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
-    }
-  }
-  if (lane < 8 && job.part == 0) {               // every column part holds the same LSE
-    const float lse = s_lse[8 * wave + lane];
-    if (!DIRECT)
-      a.lse_accum[row0 + lane] = lse;
-    else if (a.lse_out != nullptr)
-      a.lse_out[row0 + lane] = lse;
-  }
-  // Split jobs of a decode with an FP8 output: seed the combine's amax and counters.
-  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0)
-    seed_fp8_combine(a.out_scale, a.out, t, h_q);
-}
-
 
 // ---------------------------------------------------------------------------
 // decode_kernel8p: one 8-wave workgroup per job that owns all 512 output
 // columns (64 heads, bf16 pool), for launches with a single column part.
-// As in decode8_body, the two waves on a SIMD own the same 16 heads and
-// each scores one 32-slot half of every block.  Here they trade their bf16
+// The two waves on a SIMD own the same 16 heads and each scores one 32-slot
+// half of every block.  Here they trade their bf16
 // weights through LDS, and each wave accumulates every slot of the block into
 // its own half of the columns (256): 64 accumulator registers a wave, which
 // keeps two waves per SIMD without a second workgroup repeating QK^T.  The
@@ -1338,7 +952,6 @@ __device__ __forceinline__ void decode8_body(
 // ---------------------------------------------------------------------------
 // LDS of decode_kernel8p: the two tiles, then the weight exchange.
 constexpr int kLds8pBytes = 2 * kTileBytes + kWaves8 * 2048;
-static_assert(kLds8pBytes >= kLds8Bytes, "a mixed launch takes the larger LDS of its two bodies");
 
 // The body of decode_kernel8p for workgroup `block` of its launch, on the LDS
 // at `smem` (kLds8pBytes).
@@ -1701,20 +1314,20 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
 
 // ---------------------------------------------------------------------------
 // decode8h_body: a job in two workgroups that each own 32 of its 64 heads and
-// all 512 output columns.  Unlike decode8_body's two column
-// parts, the two head parts do not repeat each other's QK^T.  Wave w owns
+// all 512 output columns.  Unlike two column parts would, the two head
+// parts do not repeat each other's QK^T.  Wave w owns
 // head tile w & 1 (heads 32 part + 16 (w & 1) .. +15) and scores slot quarter
 // w >> 1 (16 slots) of every block; the four waves of a head tile trade their
 // bf16 weights through LDS, and each accumulates every slot of the block into
 // its own quarter of the columns (128).  The four share one integer frame per
 // head, agreed on as in decode_kernel8p.  The job's two workgroups are 8 block
 // ids apart (one XCD, one L2 for the gathered rows).  KV_FP8: waves 0-3
-// gather the e4m3 code tile (wave w: rows [16w, +16)), all waves expand it to
-// the bf16 tile, and the row scale multiplies the score after QK^T and the
-// weight before PV, as in decode8_body.
+// gather the e4m3 code tile (wave w: rows [16w, +16)), every wave reads its
+// operands from the codes, and the row scale multiplies the score after QK^T
+// and the weight before PV.
 // ---------------------------------------------------------------------------
-// LDS of decode8h_body: the two tiles (FP8: two code tiles and the bf16
-// tile), the weight exchange (1 KB a wave), then the per-block row scales.
+// LDS of decode8h_body: the two tiles (FP8: two code tiles), the weight
+// exchange (1 KB a wave), then the per-block row scales.
 constexpr int kLds8hScale = 2 * kTileBytes + kWaves8 * 1024;
 constexpr int kLds8hBytes = kLds8hScale + 2 * kBlk * 4;
 
@@ -1775,7 +1388,7 @@ __device__ __forceinline__ void decode8h_body(
     auto row_src = [&](int idx_lane) -> const uint8_t* {
       if (KV_FP8) {
         const int row_idx = __shfl(idx_lane, 16 * (wave & 3) + (lane >> 2));
-        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
+        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + fp8_gather_chunk(lane);
       }
       const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
       return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
@@ -1794,6 +1407,7 @@ __device__ __forceinline__ void decode8h_body(
     const int sw_k = rsw(hl);
     const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
     const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
+    const Fp8Offsets f8 = fp8_offsets(lane);                  // FP8 pool: K and V^T reads of the codes
     const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
     const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
     int vb[4];                                                  // column tile ct & 3
@@ -1885,41 +1499,32 @@ __device__ __forceinline__ void decode8h_body(
       };
       const int idx_after = load_idx(b + 2);
 
-      const uint8_t* tile;
-      if (!KV_FP8) {
-        tile = s_tile + cur * kTileBytes;
+      // Block b's operands: bf16 rows, or the e4m3 codes converted in registers.
+      const uint32_t tl = lds_addr(s_tile + cur * (KV_FP8 ? kCodeTileBytes : kTileBytes));
+      uint32_t kbase[4], vbase[4];
+      if constexpr (KV_FP8) {
+        kbase[0] = opaque(tl + f8.k[0]);
+        kbase[1] = opaque(tl + f8.k[1]);
+        kbase[2] = kbase[3] = 0u;
+        const uint32_t tlv = tl + sq * 2 * 4096;     // this wave's 128 columns
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + f8.v[m]);
       } else {
-        // Expand block b's e4m3 codes into the bf16 tile (exact conversion).
-        uint8_t* btile = s_tile + 2 * kCodeTileBytes;
-        const uint8_t* ctile = s_tile + cur * kCodeTileBytes;
-#pragma unroll 3
-        for (int j = 0; j < 9; ++j) {
-          const int p = j * kThreads8 + tid;
-          const int o = p >> 9, r = (p >> 3) & 63;
-          const int c = 8 * o + ((p & 7) ^ rsw(r));
-          const int cc = c >> 1;
-          const u32x2 codes =
-              *(const u32x2*)(ctile + ((cc >> 2) * 256 + r * 4 + (cc & 3)) * 16 + (c & 1) * 8);
-          u32x4 ov;
-          ov[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
-          ov[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
-          ov[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
-          ov[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
-          *(u32x4*)(btile + p * 16) = ov;
-        }
-        lds_barrier();
-        tile = btile;
+        kbase[0] = opaque(tl + kb0);
+        kbase[1] = opaque(tl + kb1);
+        kbase[2] = opaque(tl + kb0 + 65536);
+        kbase[3] = opaque(tl + kb1 + 65536);
+        const uint32_t tlv = tl + sq * 2 * 8192;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + vb[m]);
       }
-      const uint32_t tl = lds_addr(tile);
-      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
-                                 opaque(tl + kb1 + 65536)};
       auto kfrag = [&](int ks, int st) -> bf16x8 {
+        if constexpr (KV_FP8) return fp8_kfrag(kbase[ks & 1] + (ks >> 1) * 4096 + st * 1024);
         const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
         return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
       };
-      const uint32_t tlv = tl + sq * 2 * 8192;     // this wave's 128 columns
-      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
       auto vfrag = [&](int ct, int kk) -> bf16x8 {
+        if constexpr (KV_FP8) return fp8_vfrag(vbase[ct & 3] + (ct >> 2) * 4096 + kk * 2048);
         const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
         const i16x4 v1 =
@@ -2125,12 +1730,12 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8h(
 // LDS (as decode8h_body's head tile) and each accumulates every slot into its
 // quarter of the workgroup's columns.  One frame per head for the four.  The
 // workgroups of a job are 8 block ids apart (one XCD, one L2 for the rows).
-// KV_FP8: the e4m3 code tile is gathered (wave w: rows [16w, +16)), expanded
-// to the bf16 tile exactly, and the row scale multiplies the score after QK^T
-// and the weight before PV, as in decode8_body.
+// KV_FP8: the e4m3 code tile is gathered (wave w: rows [16w, +16)), the
+// operands are read from the codes, and the row scale multiplies the score
+// after QK^T and the weight before PV.
 // ---------------------------------------------------------------------------
-// LDS of decode4t_body: the two tiles (FP8: two code tiles and the bf16 tile),
-// the weight exchange (1 KB a wave), then the per-block row scales (FP8).
+// LDS of decode4t_body: the two tiles (FP8: two code tiles), the weight
+// exchange (1 KB a wave), then the per-block row scales (FP8).
 constexpr int kLds4tScale = 2 * kTileBytes + kWaves * 1024;
 constexpr int kLds4tBytes = kLds4tScale + 2 * kBlk * 4;
 
@@ -2191,7 +1796,7 @@ __device__ __forceinline__ void decode4t_body(
     auto row_src = [&](int idx_lane, int grp) -> const uint8_t* {
       if (KV_FP8) {
         const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
-        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + (lane & 3) * 16;
+        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + fp8_gather_chunk(lane);
       }
       const int row_idx = __shfl(idx_lane, 16 * wave + 8 * grp + (lane >> 3));
       return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
@@ -2213,6 +1818,7 @@ __device__ __forceinline__ void decode4t_body(
     const int sw_k = rsw(hl);
     const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
     const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
+    const Fp8Offsets f8 = fp8_offsets(lane);                  // FP8 pool: K and V^T reads of the codes
     const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
     const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
     int vb[4];                                                  // column tile ct & 3
@@ -2334,42 +1940,32 @@ __device__ __forceinline__ void decode4t_body(
       };
       const int idx_after = load_idx(b + 2);
 
-      const uint8_t* tile;
-      if (!KV_FP8) {
-        tile = s_tile + cur * kTileBytes;
+      // Block b's operands: bf16 rows, or the e4m3 codes converted in registers.
+      const uint32_t tl = lds_addr(s_tile + cur * (KV_FP8 ? kCodeTileBytes : kTileBytes));
+      uint32_t kbase[4], vbase[4];
+      if constexpr (KV_FP8) {
+        kbase[0] = opaque(tl + f8.k[0]);
+        kbase[1] = opaque(tl + f8.k[1]);
+        kbase[2] = kbase[3] = 0u;
+        const uint32_t tlv = tl + ((kCols * cpart + kWCols * wave) / 64) * 4096;     // this wave's columns start at column tile (kCols cpart + kWCols wave) / 16
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + f8.v[m]);
       } else {
-        // Expand block b's e4m3 codes into the bf16 tile (exact conversion).
-        uint8_t* btile = s_tile + 2 * kCodeTileBytes;
-        const uint8_t* ctile = s_tile + cur * kCodeTileBytes;
-#pragma unroll 3
-        for (int j = 0; j < 18; ++j) {
-          const int p = j * kThreads + tid;
-          const int o = p >> 9, r = (p >> 3) & 63;
-          const int c = 8 * o + ((p & 7) ^ rsw(r));
-          const int cc = c >> 1;
-          const u32x2 codes =
-              *(const u32x2*)(ctile + ((cc >> 2) * 256 + r * 4 + (cc & 3)) * 16 + (c & 1) * 8);
-          u32x4 ov;
-          ov[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, false));
-          ov[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], 1.0f, true));
-          ov[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, false));
-          ov[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], 1.0f, true));
-          *(u32x4*)(btile + p * 16) = ov;
-        }
-        lds_barrier();
-        tile = btile;
+        kbase[0] = opaque(tl + kb0);
+        kbase[1] = opaque(tl + kb1);
+        kbase[2] = opaque(tl + kb0 + 65536);
+        kbase[3] = opaque(tl + kb1 + 65536);
+        const uint32_t tlv = tl + ((kCols * cpart + kWCols * wave) / 64) * 8192;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + vb[m]);
       }
-      const uint32_t tl = lds_addr(tile);
-      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
-                                 opaque(tl + kb1 + 65536)};
       auto kfrag = [&](int ks, int st) -> bf16x8 {
+        if constexpr (KV_FP8) return fp8_kfrag(kbase[ks & 1] + (ks >> 1) * 4096 + st * 1024);
         const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
         return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
       };
-      // this wave's columns start at octet (kCols cpart + kWCols wave) / 64
-      const uint32_t tlv = tl + ((kCols * cpart + kWCols * wave) / 64) * 8192;
-      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
       auto vfrag = [&](int ct, int kk) -> bf16x8 {
+        if constexpr (KV_FP8) return fp8_vfrag(vbase[ct & 3] + (ct >> 2) * 4096 + kk * 2048);
         const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
         const i16x4 v1 =
@@ -2573,26 +2169,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel4t(
 
 // One launch for more jobs than compute units, with a short last round: its
 // first n_head workgroups run decode_kernel8p's body over jobs [0, n_head),
-// the rest the jobs from n_head on in CST parts (2: decode8h_body's head
-// halves; 4 or 8: decode8_body's column parts).  The tail's workgroups start
-// as soon as compute units free up, with no kernel boundary in between.
-// n_head is a multiple of 8, so the tail keeps the XCD grouping of a job's
-// parts.
-template <bool DIRECT, bool PREFETCH, int CST>
+// the rest the jobs from n_head on in two parts (decode8h_body's head halves).
+// The tail's workgroups start as soon as compute units free up, with no kernel
+// boundary in between.  n_head is a multiple of 8, so the tail keeps the XCD
+// grouping of a job's parts.
+template <bool DIRECT, bool PREFETCH>
 __global__ __launch_bounds__(kThreads8) void decode_kernel8m(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t n_head, DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds8pBytes];
   const int block = (int)blockIdx.x;
-  static_assert(kLds8pBytes >= kLds8hBytes, "the mixed launch's LDS holds either tail body");
+  static_assert(kLds8pBytes >= kLds8hBytes, "the mixed launch's LDS holds either body");
   if (block < n_head)
     decode8p_body<DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, 0, a, block, smem);
-  else if constexpr (CST == 2)
+  else
     decode8h_body<false, DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, n_head, a,
                                            block - n_head, smem);
-  else
-    decode8_body<false, DIRECT, CST, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, n_head, a,
-                                               block - n_head, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2821,11 +2413,13 @@ __global__ __launch_bounds__(64 * HW) void combine_fp8_kernel(CombineArgs a) {
     uint32_t* scale_word = (uint32_t*)a.out_scale + p.t;
     const uint32_t n_wg = (uint32_t)(a.h_q * PARTS / HW);
     __hip_atomic_fetch_max(sync + 1, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Release: this workgroup's amax is in before its count; acquire: the
-    // last one to count in sees every amax.
-    const uint32_t before = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    // Release: this workgroup's amax is in before its count.  The last one to
+    // count in then acquires, so it sees every amax (an acquire in every
+    // workgroup measured 1.2 us slower at 16 tokens: each invalidates its L2).
+    const uint32_t before = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     float sc;
     if (before == n_wg - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       const float amax = __uint_as_float(__hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       sc = amax > 0.f ? amax / 448.0f : 1.0f;
       __hip_atomic_store(scale_word, __float_as_uint(sc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2962,18 +2556,10 @@ hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream
   if (a.col_parts == 1 && n_jobs > cus && tail > 0 && 2 * tail <= cus && !(DIRECT && a.out_dtype == kOutFp8)) {
     const int cs_tail = 8 * tail <= cus ? 8 : 4 * tail <= cus ? 4 : 2;
     const int n_head = n_jobs - tail;
-    if (a.h_q == 64 && !kv_fp8 && n_head % 8 == 0) {     // both bodies in one launch
-      const dim3 grid((unsigned)(n_head + (tail + 7) / 8 * 8 * cs_tail));
-#define SMLA_LAUNCH_MIXED(CSV)                                                                                \
-  hipLaunchKernelGGL((decode_kernel8m<DIRECT, PREFETCH, CSV>), grid, dim3(kThreads8), 0, stream, a.indices, a.q, \
-                     a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, n_head, a)
-      if (cs_tail == 8)
-        SMLA_LAUNCH_MIXED(8);
-      else if (cs_tail == 4)
-        SMLA_LAUNCH_MIXED(4);
-      else
-        SMLA_LAUNCH_MIXED(2);
-#undef SMLA_LAUNCH_MIXED
+    if (a.h_q == 64 && !kv_fp8 && n_head % 8 == 0) {     // both bodies in one launch, the tail in 2 parts
+      const dim3 grid((unsigned)(n_head + (tail + 7) / 8 * 8 * 2));
+      hipLaunchKernelGGL((decode_kernel8m<DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices, a.q,
+                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, n_head, a);
       return hipGetLastError();
     }
     const hipError_t e = launch_jobs<DIRECT, PREFETCH>(a, kv_fp8, 1, 0, n_jobs - tail, stream);
