@@ -50,7 +50,8 @@ typedef enum {
   SMLA_ERR_UNSUPPORTED = 2,        /* h_q not in {16, 32, 64}, split_block != 64, too large */
   SMLA_ERR_MISSING_WORKSPACE = 3,  /* num_splits > 1 without o_accum and lse_accum */
   SMLA_ERR_MISALIGNED = 4,         /* a pointer or the row stride breaks 16-byte alignment */
-  SMLA_ERR_HIP = 5                 /* the HIP runtime rejected a launch */
+  SMLA_ERR_HIP = 5,                /* the HIP runtime rejected a launch */
+  SMLA_ERR_SCRATCH_TOO_SMALL = 6   /* sparse_mla_decode_noalloc: the partials exceed its scratch */
 } smla_status;
 
 typedef enum { SMLA_KV_BF16 = 0, SMLA_KV_FP8_E4M3 = 1 } smla_kv_dtype;
@@ -60,6 +61,9 @@ typedef enum { SMLA_OUT_BF16 = 0, SMLA_OUT_FP32 = 1, SMLA_OUT_FP8_E4M3 = 2 } sml
 #define SMLA_D_V 512           /* the value is the first 512 dimensions of the row */
 #define SMLA_SPLIT_BLOCK 64    /* slots per KV block, the unit of the split partition */
 #define SMLA_MAX_SPLITS 64
+/* Bytes of device scratch (one copy per GPU) that hold the split partials of
+ * sparse_mla_decode_noalloc. */
+#define SMLA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef struct {
   int32_t s_q;             /* query tokens, >= 1 */
@@ -123,6 +127,28 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
                               const float* kv_scale, const int32_t* indices, int32_t num_splits,
                               const float* sink, float* o_accum, float* lse_accum, void* out,
                               float* out_scale, float* lse_out, void* stream);
+
+/*
+ * sparse_mla_decode_noalloc -- sparse_mla_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split partials live in a scratch array
+ * of the library, SMLA_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends.  Same arguments and results as sparse_mla_decode without o_accum and
+ * lse_accum; `out` is required.  num_splits == 1 takes the direct path (no
+ * scratch); num_splits > 1 needs smla_partial_bytes(s_q, h_q, num_splits) plus
+ * at most 255 bytes of alignment within the scratch, else the call returns
+ * SMLA_ERR_SCRATCH_TOO_SMALL before anything is enqueued.
+ * The call allocates nothing: its first call on a device looks the scratch's
+ * address up (hipGetSymbolAddress) and keeps it for that device.  Every call
+ * on one GPU uses that GPU's one scratch, which keeps the last call's
+ * partials: calls ordered on one stream are safe, calls that overlap on one
+ * GPU (other streams, concurrent graph replays) race.  Nothing in it needs to
+ * start at zero: every job writes its partials before the combine reads them.
+ */
+smla_status sparse_mla_decode_noalloc(const smla_params* p, const void* q, const void* kv_pool,
+                                      const float* kv_scale, const int32_t* indices, int32_t num_splits,
+                                      const float* sink, void* out, float* out_scale, float* lse_out,
+                                      void* stream);
 
 /*
  * combine_splits -- merge split partials (as written by sparse_mla_decode) into

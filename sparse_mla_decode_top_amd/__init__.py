@@ -7,6 +7,6 @@ is an error: there is no CPU fallback.
 """
 from .binding import (  # noqa: F401
     SmlaError, KV_BF16, KV_FP8_E4M3, OUT_BF16, OUT_FP32, OUT_FP8_E4M3,
-    library_path, load_library, sparse_mla_decode, combine_splits,
+    library_path, load_library, sparse_mla_decode, sparse_mla_decode_noalloc, combine_splits,
     smla_choose_num_splits, smla_partial_bytes, smla_validate, smla_status_string,
 )

@@ -15,10 +15,12 @@ _LIB_NAME = "libsmla.so"
 KV_BF16, KV_FP8_E4M3 = 0, 1
 OUT_BF16, OUT_FP32, OUT_FP8_E4M3 = 0, 1, 2
 D_QK, D_V, SPLIT_BLOCK, MAX_SPLITS = 576, 512, 64, 64
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 STATUS_NAMES = {
     0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED",
     3: "SMLA_ERR_MISSING_WORKSPACE", 4: "SMLA_ERR_MISALIGNED", 5: "SMLA_ERR_HIP",
+    6: "SMLA_ERR_SCRATCH_TOO_SMALL",
 }
 
 
@@ -44,6 +46,8 @@ _vp = ctypes.c_void_p
 SIGNATURES = {
     "sparse_mla_decode": (ctypes.c_int, [ctypes.POINTER(SmlaParams), _vp, _vp, _vp, _vp, ctypes.c_int32,
                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "sparse_mla_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(SmlaParams), _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                                 _vp, _vp, _vp, _vp, _vp]),
     "combine_splits": (ctypes.c_int, [ctypes.POINTER(SmlaParams), ctypes.c_int32, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp]),
     "smla_choose_num_splits": (ctypes.c_int32, [ctypes.c_int32] * 4),
@@ -184,6 +188,37 @@ def sparse_mla_decode(q, kv_pool, indices, num_splits, softmax_scale, kv_scale=N
                                int(num_splits), _ptr(sink), _ptr(o_accum), _ptr(lse_accum), _ptr(out),
                                _ptr(out_scale), _ptr(lse_out), _stream_handle(stream, dev))
     _check(st, "sparse_mla_decode")
+
+
+def sparse_mla_decode_noalloc(q, kv_pool, indices, num_splits, softmax_scale, out, kv_scale=None, sink=None,
+                              out_scale=None, lse_out=None, out_dtype=None, stream=None):
+    """The decode step with its split partials in the library's own device scratch
+    (include/smla.h, sparse_mla_decode_noalloc): no workspace arguments, `out` required."""
+    import torch
+    lib = load_library()
+    s_q, h_q, dqk = q.shape
+    topk = indices.shape[1]
+    n_pool, row_stride = kv_pool.shape
+    kv_dtype = KV_FP8_E4M3 if kv_pool.dtype in (torch.uint8, torch.float8_e4m3fn) else KV_BF16
+    od = _out_dtype_of(out, out_dtype)
+    dev = q.device
+    if dqk != D_QK or indices.shape[0] != s_q:
+        raise SmlaError("shape mismatch between q and indices")
+    _need(q, "q", s_q * h_q * D_QK, (torch.bfloat16,), dev)
+    _need(kv_pool, "kv_pool", n_pool * row_stride, (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dev)
+    _need(kv_scale, "kv_scale", n_pool, (torch.float32,), dev)
+    _need(indices, "indices", s_q * topk, (torch.int32,), dev)
+    _need(sink, "sink", h_q, (torch.float32,), dev)
+    out_types = {OUT_BF16: (torch.bfloat16,), OUT_FP32: (torch.float32,),
+                 OUT_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn)}[od]
+    _need(out, "out", s_q * h_q * D_V, out_types, dev)
+    _need(out_scale, "out_scale", s_q, (torch.float32,), dev)
+    _need(lse_out, "lse_out", s_q * h_q, (torch.float32,), dev)
+    p = make_params(s_q, h_q, topk, n_pool, row_stride, softmax_scale, kv_dtype, od)
+    st = lib.sparse_mla_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(kv_scale), _ptr(indices),
+                                       int(num_splits), _ptr(sink), _ptr(out), _ptr(out_scale), _ptr(lse_out),
+                                       _stream_handle(stream, dev))
+    _check(st, "sparse_mla_decode_noalloc")
 
 
 def combine_splits(o_accum, lse_accum, num_splits, out, sink=None, out_scale=None, lse_out=None,

@@ -54,6 +54,7 @@ const char* smla_status_string(smla_status s) {
     case SMLA_ERR_MISSING_WORKSPACE: return "SMLA_ERR_MISSING_WORKSPACE";
     case SMLA_ERR_MISALIGNED: return "SMLA_ERR_MISALIGNED";
     case SMLA_ERR_HIP: return "SMLA_ERR_HIP";
+    case SMLA_ERR_SCRATCH_TOO_SMALL: return "SMLA_ERR_SCRATCH_TOO_SMALL";
   }
   return "SMLA_ERR_UNKNOWN";
 }
@@ -211,6 +212,27 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   if (smla::launch_decode_partial(a, fp8, hs) != hipSuccess) return SMLA_ERR_HIP;
   if (out == nullptr) return SMLA_OK;   // partial-only: the caller combines
   return run_combine(p, num_splits, o_accum, lse_accum, sink, out, out_scale, lse_out, stream, seed_scale);
+}
+
+smla_status sparse_mla_decode_noalloc(const smla_params* p, const void* q, const void* kv_pool,
+                                      const float* kv_scale, const int32_t* indices, int32_t num_splits,
+                                      const float* sink, void* out, float* out_scale, float* lse_out,
+                                      void* stream) {
+  if (out == nullptr) return SMLA_ERR_INVALID_ARG;
+  if (num_splits == 1)       // the direct path has no partials
+    return sparse_mla_decode(p, q, kv_pool, kv_scale, indices, 1, sink, nullptr, nullptr, out, out_scale, lse_out,
+                             stream);
+  const smla_status st = check_common_shape(p, num_splits);
+  if (st != SMLA_OK) return st;
+  // o_accum at the start of the scratch, lse_accum after it on a 256-byte boundary
+  const size_t rows = (size_t)num_splits * (size_t)p->s_q * (size_t)p->h_q;
+  const size_t lse_off = (rows * SMLA_D_V * 4 + 255) & ~(size_t)255;
+  if (lse_off + rows * 4 > SMLA_NOALLOC_SCRATCH_BYTES) return SMLA_ERR_SCRATCH_TOO_SMALL;
+  void* base = nullptr;
+  if (smla::noalloc_scratch(&base) != hipSuccess) return SMLA_ERR_HIP;
+  return sparse_mla_decode(p, q, kv_pool, kv_scale, indices, num_splits, sink, static_cast<float*>(base),
+                           reinterpret_cast<float*>(static_cast<uint8_t*>(base) + lse_off), out, out_scale, lse_out,
+                           stream);
 }
 
 }  // extern "C"

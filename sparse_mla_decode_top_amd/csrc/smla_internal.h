@@ -50,4 +50,8 @@ hipError_t launch_decode_partial(const DecodeArgs& a, bool kv_fp8, hipStream_t s
 hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
+// Device address of the current device's copy of the no-allocation entry
+// point's scratch (SMLA_NOALLOC_SCRATCH_BYTES); looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace smla

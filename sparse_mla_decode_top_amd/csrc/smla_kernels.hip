@@ -69,8 +69,16 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "smla.h"
 #include "smla_internal.h"
+
+// Split partials of sparse_mla_decode_noalloc: one copy on every GPU the
+// library runs on.  In host code `scratch` names a host-side stand-in, never
+// the device memory: only the address hipGetSymbolAddress returns for the
+// current device (noalloc_scratch below) is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[SMLA_NOALLOC_SCRATCH_BYTES];
 
 namespace smla {
 namespace {
@@ -2629,6 +2637,23 @@ hipError_t launch_combine_chunk(const CombineArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 }  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.num_splits <= 4) return launch_combine_chunk<4>(a, stream);

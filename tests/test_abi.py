@@ -161,6 +161,26 @@ def test_decode_rejects_before_launch():
     assert st == UNSUPPORTED
 
 
+def test_noalloc_rejects_before_launch():
+    """sparse_mla_decode_noalloc: a missing output, a bad shape and partials larger than
+    its scratch come back as status codes before anything touches the GPU."""
+    lib = B.load_library()
+    p = _p()
+    args = (A, A, None, A)
+    assert lib.sparse_mla_decode_noalloc(ctypes.byref(p), *args, 8, None, None, None, None, None) == INVALID
+    assert lib.sparse_mla_decode_noalloc(ctypes.byref(_p(h_q=8)), *args, 8, None, A, None, None, None) == UNSUPPORTED
+    assert lib.sparse_mla_decode_noalloc(ctypes.byref(p), *args, 0, None, A, None, None, None) == INVALID
+    big = _p(s_q=6)
+    assert smla.smla_partial_bytes(6, 64, 64) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.sparse_mla_decode_noalloc(ctypes.byref(big), *args, 64, None, A, None, None, None) == 6
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    assert "#define SMLA_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
+    assert B.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
 def test_peak_probe_exports_its_header():
     """libsmla_peak.so (bench.py's matrix-core probe) exports what include/smla_peak.h declares."""
     text = open(os.path.join(ROOT, "include", "smla_peak.h")).read()
