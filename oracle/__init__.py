@@ -1,4 +1,6 @@
-"""Float64 CPU oracle for split-KV sparse MLA decode (test infrastructure only).
+"""Float64 CPU oracles (test infrastructure only): split-KV sparse MLA decode
+(``smla_oracle``, re-exported here) and split-KV FP8 prefill attention
+(``oracle.prefill_oracle``).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path never does.
