@@ -197,6 +197,90 @@ smla_status smla_validate(const smla_params* p, const void* q, const void* kv_po
                           const float* o_accum, const float* lse_accum, const void* out,
                           const float* out_scale);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Split-KV FP8 prefill attention (cudnn-frontend PR #768, "split kv ports":
+ * the split-KV port of an FP8 SDPA prefill kernel with head dimension 128).
+ *
+ *   For batch b, query row i < seqlen_q[b] and query head h, over the keys
+ *   j < seqlen_kv[b] that the row may see (all of them, or, with `causal`,
+ *   j <= i + seqlen_kv[b] - seqlen_q[b]: the mask aligned to the bottom-right
+ *   corner), with KV head h / (h_q / h_kv):
+ *     s_ij = softmax_scale * <q_i, k_j>,  O_i = sum_j softmax(s)_ij v_j,
+ *     LSE_i = ln sum_j exp(s_ij)                          (natural log)
+ *   Q, K and V are e4m3fn codes times one float32 descale factor per tensor.
+ *   Under a split, each tile of q_tile query rows takes its masked KV range
+ *   (the keys its last row may see) in blocks of kv_block keys, cut into
+ *   split_kv near-equal chunks with the remainder on the leading chunks; every
+ *   row still applies its own mask inside its chunk.  A split writes its
+ *   partial O (normalised by its own denominator) and its LSE into split-major
+ *   slots; an empty chunk writes O = +0, LSE = -inf.  The combine merges the
+ *   splits (weights exp(LSE_s - max LSE)), applies the sink once (one extra key
+ *   of logit sink[h], natural-log units, with a zero value row), casts, and
+ *   owns the amax of the recombined output.  The returned LSE excludes the
+ *   sink.  A row that sees no key gets O = 0 and LSE = -inf.
+ * ---------------------------------------------------------------------------
+ */
+typedef struct {
+  int32_t batch;           /* B >= 1 */
+  int32_t h_q;             /* query heads, a multiple of h_kv, <= 256 */
+  int32_t h_kv;            /* KV heads >= 1 */
+  int32_t head_dim;        /* must be 128 */
+  int32_t max_s_q;         /* padded query rows per batch (Sq), >= 1 */
+  int32_t max_s_kv;        /* padded keys per batch (Skv), >= 1 */
+  int32_t causal;          /* 1: bottom-right causal mask, 0: none */
+  int32_t q_tile;          /* query rows per tile; must be 64 */
+  int32_t kv_block;        /* keys per KV block; must be 64 */
+  float softmax_scale;     /* multiplies q.k (e.g. 1/sqrt(128)) */
+  float descale_q, descale_k, descale_v;   /* per-tensor dequantisation factors */
+  int32_t out_dtype;       /* SMLA_OUT_BF16 or SMLA_OUT_FP32 */
+} smla_prefill_params;
+
+/*
+ * sdpa_fp8_prefill -- split-KV FP8 prefill attention and, when an output is
+ * requested, its combine.
+ *
+ *   q          [B][Sq][h_q][128] e4m3fn codes, 16-byte aligned.
+ *   k, v       [B][Skv][h_kv][128] e4m3fn codes, 16-byte aligned.
+ *   seqlen_q   [B] int32 device array: query rows present (values are clamped
+ *              into [0, Sq] on the device).
+ *   seqlen_kv  [B] int32 device array: keys present (clamped into [0, Skv]).
+ *   split_kv   1 .. SMLA_MAX_SPLITS.  smla_prefill_choose_splits() gives a
+ *              default for the shape.
+ *   sink       [h_q] f32 per-head sink logit, or NULL.
+ *   o_part     [split_kv][B][Sq][h_q][128] f32 split partials, 16-byte aligned,
+ *              or NULL; lse_part [split_kv][B][Sq][h_q] f32, or NULL.
+ *   out        [B][Sq][h_q][128] bf16 or f32 (out_dtype), 16-byte aligned, or
+ *              NULL (partial-only); rows i >= seqlen_q[b] are not written.
+ *   lse_out    [B][Sq][h_q] f32 final natural-log LSE (without the sink), or NULL.
+ *   amax_out   one f32: max |O| over the written rows, before the cast, or NULL.
+ * Modes as sparse_mla_decode: no partials and split_kv == 1 is the direct path
+ * (one kernel writes O, the sink and the amax fused in its epilogue); with
+ * partials every split writes them and, if `out` is given, the combine runs;
+ * split_kv > 1 without partials is SMLA_ERR_MISSING_WORKSPACE.
+ */
+smla_status sdpa_fp8_prefill(const smla_prefill_params* p, const void* q, const void* k, const void* v,
+                             const int32_t* seqlen_q, const int32_t* seqlen_kv, int32_t split_kv,
+                             const float* sink, float* o_part, float* lse_part, void* out, float* lse_out,
+                             float* amax_out, void* stream);
+
+/*
+ * smla_prefill_partial_bytes -- bytes of o_part plus lse_part:
+ * split_kv * batch * max_s_q * h_q * (128 * 4 + 4); 0 for a non-positive argument.
+ */
+size_t smla_prefill_partial_bytes(int32_t batch, int32_t max_s_q, int32_t h_q, int32_t split_kv);
+
+/*
+ * smla_prefill_choose_splits -- a split count that gives a grid of few query
+ * tiles enough workgroups for `num_cus` compute units: 1 when
+ * batch * ceil(max_s_q / 64) * h_q already fills two rounds, else the count
+ * that brings it to about two rounds, capped at the KV blocks of the longest
+ * range (ceil(max_s_kv / 64)) and at 16.  Deterministic.  Returns >= 1, or 0
+ * for a non-positive argument.
+ */
+int32_t smla_prefill_choose_splits(int32_t batch, int32_t max_s_q, int32_t max_s_kv, int32_t h_q,
+                                   int32_t num_cus);
+
 /* smla_status_string -- a static, human-readable name of a status code. */
 const char* smla_status_string(smla_status s);
 

@@ -39,6 +39,16 @@ class SmlaParams(ctypes.Structure):
     ]
 
 
+class SmlaPrefillParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("max_s_q", ctypes.c_int32), ("max_s_kv", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("q_tile", ctypes.c_int32), ("kv_block", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float),
+        ("descale_v", ctypes.c_float), ("out_dtype", ctypes.c_int32),
+    ]
+
+
 _lib = None
 _vp = ctypes.c_void_p
 
@@ -55,6 +65,10 @@ SIGNATURES = {
     "smla_validate": (ctypes.c_int, [ctypes.POINTER(SmlaParams), _vp, _vp, _vp, _vp, ctypes.c_int32,
                                      _vp, _vp, _vp, _vp]),
     "smla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sdpa_fp8_prefill": (ctypes.c_int, [ctypes.POINTER(SmlaPrefillParams), _vp, _vp, _vp, _vp, _vp,
+                                        ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "smla_prefill_partial_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 4),
+    "smla_prefill_choose_splits": (ctypes.c_int32, [ctypes.c_int32] * 5),
 }
 
 
@@ -243,3 +257,59 @@ def combine_splits(o_accum, lse_accum, num_splits, out, sink=None, out_scale=Non
     st = lib.combine_splits(ctypes.byref(p), int(num_splits), _ptr(o_accum), _ptr(lse_accum), _ptr(sink),
                             _ptr(out), _ptr(out_scale), _ptr(lse_out), _stream_handle(stream, dev))
     _check(st, "combine_splits")
+
+
+# ---------------------------------------------------------------------------
+# split-KV FP8 prefill
+# ---------------------------------------------------------------------------
+def smla_prefill_partial_bytes(batch, max_s_q, h_q, split_kv):
+    return int(load_library().smla_prefill_partial_bytes(batch, max_s_q, h_q, split_kv))
+
+
+def smla_prefill_choose_splits(batch, max_s_q, max_s_kv, h_q, num_cus=256):
+    return int(load_library().smla_prefill_choose_splits(batch, max_s_q, max_s_kv, h_q, num_cus))
+
+
+def make_prefill_params(batch, h_q, h_kv, max_s_q, max_s_kv, softmax_scale, descale_q=1.0, descale_k=1.0,
+                        descale_v=1.0, causal=True, out_dtype=OUT_BF16, head_dim=128, q_tile=64,
+                        kv_block=64):
+    return SmlaPrefillParams(batch=batch, h_q=h_q, h_kv=h_kv, head_dim=head_dim, max_s_q=max_s_q,
+                             max_s_kv=max_s_kv, causal=1 if causal else 0, q_tile=q_tile, kv_block=kv_block,
+                             softmax_scale=softmax_scale, descale_q=descale_q, descale_k=descale_k,
+                             descale_v=descale_v, out_dtype=out_dtype)
+
+
+def sdpa_fp8_prefill(q, k, v, seqlen_q, seqlen_kv, split_kv, softmax_scale, descale_q=1.0, descale_k=1.0,
+                     descale_v=1.0, causal=True, sink=None, o_part=None, lse_part=None, out=None, lse_out=None,
+                     amax_out=None, out_dtype=None, stream=None):
+    """FP8 prefill attention through the C ABI (include/smla.h, sdpa_fp8_prefill).
+
+    q [B, Sq, h_q, 128], k and v [B, Skv, h_kv, 128] uint8 e4m3 codes; seqlen_q / seqlen_kv [B]
+    int32; the output dtype follows `out` (bf16 / float32) unless `out_dtype` is given."""
+    import torch
+    lib = load_library()
+    B, sq_max, h_q, d = q.shape
+    skv_max, h_kv = k.shape[1], k.shape[2]
+    dev = q.device
+    if d != 128 or tuple(k.shape) != (B, skv_max, h_kv, 128) or tuple(v.shape) != tuple(k.shape):
+        raise SmlaError("q, k and v must be [B, S, heads, 128] with matching k / v")
+    od = _out_dtype_of(out, out_dtype)
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    _need(q, "q", q.numel(), codes, dev)
+    _need(k, "k", k.numel(), codes, dev)
+    _need(v, "v", v.numel(), codes, dev)
+    _need(seqlen_q, "seqlen_q", B, (torch.int32,), dev)
+    _need(seqlen_kv, "seqlen_kv", B, (torch.int32,), dev)
+    _need(sink, "sink", h_q, (torch.float32,), dev)
+    _need(o_part, "o_part", split_kv * B * sq_max * h_q * 128, (torch.float32,), dev)
+    _need(lse_part, "lse_part", split_kv * B * sq_max * h_q, (torch.float32,), dev)
+    _need(out, "out", B * sq_max * h_q * 128, {OUT_BF16: (torch.bfloat16,), OUT_FP32: (torch.float32,)}.get(
+        od, (torch.bfloat16,)), dev)
+    _need(lse_out, "lse_out", B * sq_max * h_q, (torch.float32,), dev)
+    _need(amax_out, "amax_out", 1, (torch.float32,), dev)
+    p = make_prefill_params(B, h_q, h_kv, sq_max, skv_max, softmax_scale, descale_q, descale_k, descale_v,
+                            causal, od)
+    st = lib.sdpa_fp8_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlen_q), _ptr(seqlen_kv),
+                              int(split_kv), _ptr(sink), _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse_out),
+                              _ptr(amax_out), _stream_handle(stream, dev))
+    _check(st, "sdpa_fp8_prefill")

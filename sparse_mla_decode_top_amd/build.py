@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsmla.so")
-SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "smla_api.cpp")]
+SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "smla_prefill.hip"),
+           os.path.join(CSRC, "smla_api.cpp")]
 # the peak probe (bench.py's measured matrix-core rate), a library of its own
 PEAK_LIB = os.path.join(HERE, "libsmla_peak.so")
 PEAK_SOURCES = [os.path.join(CSRC, "smla_peak.hip")]

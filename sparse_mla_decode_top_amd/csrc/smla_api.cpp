@@ -235,4 +235,88 @@ smla_status sparse_mla_decode_noalloc(const smla_params* p, const void* q, const
                            stream);
 }
 
+size_t smla_prefill_partial_bytes(int32_t batch, int32_t max_s_q, int32_t h_q, int32_t split_kv) {
+  if (batch < 1 || max_s_q < 1 || h_q < 1 || split_kv < 1) return 0;
+  return (size_t)split_kv * (size_t)batch * (size_t)max_s_q * (size_t)h_q * (size_t)(128 * 4 + 4);
+}
+
+int32_t smla_prefill_choose_splits(int32_t batch, int32_t max_s_q, int32_t max_s_kv, int32_t h_q,
+                                   int32_t num_cus) {
+  if (batch < 1 || max_s_q < 1 || max_s_kv < 1 || h_q < 1 || num_cus < 1) return 0;
+  // Workgroups of the unsplit launch: one per (batch, 64-row tile, head).
+  const int64_t tiles = (int64_t)batch * ((max_s_q + 63) / 64) * h_q;
+  const int64_t target = 2 * (int64_t)num_cus;
+  if (tiles >= target) return 1;
+  int64_t s = (target + tiles - 1) / tiles;
+  const int64_t blocks = (max_s_kv + 63) / 64;
+  if (s > blocks) s = blocks;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : (int32_t)s;
+}
+
+smla_status sdpa_fp8_prefill(const smla_prefill_params* p, const void* q, const void* k, const void* v,
+                             const int32_t* seqlen_q, const int32_t* seqlen_kv, int32_t split_kv,
+                             const float* sink, float* o_part, float* lse_part, void* out, float* lse_out,
+                             float* amax_out, void* stream) {
+  if (p == nullptr) return SMLA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->h_q < 1 || p->h_kv < 1 || p->max_s_q < 1 || p->max_s_kv < 1) return SMLA_ERR_INVALID_ARG;
+  if (p->head_dim != 128 || p->q_tile != 64 || p->kv_block != 64) return SMLA_ERR_UNSUPPORTED;
+  if (p->h_q % p->h_kv != 0 || p->h_q > 256) return SMLA_ERR_UNSUPPORTED;
+  if (p->causal != 0 && p->causal != 1) return SMLA_ERR_INVALID_ARG;
+  if (p->out_dtype != SMLA_OUT_BF16 && p->out_dtype != SMLA_OUT_FP32) return SMLA_ERR_UNSUPPORTED;
+  if (split_kv < 1) return SMLA_ERR_INVALID_ARG;
+  if (split_kv > SMLA_MAX_SPLITS) return SMLA_ERR_UNSUPPORTED;
+  if (!isfinite(p->softmax_scale) || !isfinite(p->descale_q) || !isfinite(p->descale_k) ||
+      !isfinite(p->descale_v))
+    return SMLA_ERR_INVALID_ARG;
+  if (q == nullptr || k == nullptr || v == nullptr || seqlen_q == nullptr || seqlen_kv == nullptr)
+    return SMLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return SMLA_ERR_MISALIGNED;
+  if ((reinterpret_cast<uintptr_t>(seqlen_q) & 3u) != 0 || (reinterpret_cast<uintptr_t>(seqlen_kv) & 3u) != 0)
+    return SMLA_ERR_MISALIGNED;
+  const bool has_o = o_part != nullptr, has_l = lse_part != nullptr;
+  if (has_o != has_l) return SMLA_ERR_MISSING_WORKSPACE;
+  if (split_kv > 1 && !has_o) return SMLA_ERR_MISSING_WORKSPACE;
+  if (!has_o && out == nullptr) return SMLA_ERR_INVALID_ARG;       // the direct path needs an output
+  if (has_o && !aligned16(o_part)) return SMLA_ERR_MISALIGNED;
+  if (has_l && (reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0) return SMLA_ERR_MISALIGNED;
+  if (out != nullptr && !aligned16(out)) return SMLA_ERR_MISALIGNED;
+  const int64_t n_tiles = (p->max_s_q + 63) / 64;
+  const int64_t n_work = (int64_t)p->batch * split_kv * n_tiles * p->h_q;
+  const int64_t rows = (int64_t)p->batch * p->max_s_q * p->h_q;
+  if (n_work > INT32_MAX - 8 || (int64_t)p->batch * p->max_s_q > INT32_MAX ||
+      (int64_t)p->batch * p->max_s_kv > INT32_MAX || rows * split_kv > ((int64_t)1 << 40))
+    return SMLA_ERR_UNSUPPORTED;
+  smla::PrefillArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.seqlen_q = seqlen_q;
+  a.seqlen_kv = seqlen_kv;
+  a.sink = sink;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.amax_out = out != nullptr ? amax_out : nullptr;    // partial-only: no output, no amax
+  a.batch = p->batch;
+  a.h_q = p->h_q;
+  a.h_kv = p->h_kv;
+  a.sq_max = p->max_s_q;
+  a.skv_max = p->max_s_kv;
+  a.num_splits = split_kv;
+  a.n_tiles = (int32_t)n_tiles;
+  a.causal = p->causal;
+  a.out_dtype = p->out_dtype;
+  a.scale_log2 = p->softmax_scale * p->descale_q * p->descale_k * 1.4426950408889634f;
+  a.descale_v = p->descale_v;
+  a.n_work = (int32_t)n_work;
+  a.cus = device_cus();
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!has_o) return smla::launch_prefill(a, false, hs) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+  if (smla::launch_prefill(a, true, hs) != hipSuccess) return SMLA_ERR_HIP;
+  if (out == nullptr) return SMLA_OK;
+  return smla::launch_prefill_combine(a, hs) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
 }  // extern "C"

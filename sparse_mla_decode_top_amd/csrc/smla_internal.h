@@ -45,10 +45,34 @@ struct CombineArgs {
   int32_t cus;                // compute units of the device (the FP8 one-launch combine fits one round)
 };
 
+// One launch of the FP8 prefill attention and its combine.  Device pointers only.
+struct PrefillArgs {
+  const uint8_t* q;           // [B][Sq][h_q][128] e4m3 codes
+  const uint8_t* k;           // [B][Skv][h_kv][128]
+  const uint8_t* v;           // [B][Skv][h_kv][128]
+  const int32_t* seqlen_q;    // [B]
+  const int32_t* seqlen_kv;   // [B]
+  const float* sink;          // [h_q] or nullptr
+  float* o_part;              // [S][B][Sq][h_q][128] (split mode)
+  float* lse_part;            // [S][B][Sq][h_q]      (split mode)
+  void* out;                  // [B][Sq][h_q][128] bf16 / f32, or nullptr
+  float* lse_out;             // [B][Sq][h_q] or nullptr
+  float* amax_out;            // one float or nullptr
+  int32_t batch, h_q, h_kv, sq_max, skv_max, num_splits, n_tiles;
+  int32_t causal, out_dtype;
+  float scale_log2;           // softmax_scale * descale_q * descale_k * log2(e)
+  float descale_v;
+  int32_t n_work;             // batch * num_splits * n_tiles * h_q workgroups of the attention launch
+  int32_t cus;
+};
+
 // Each returns the launch status (hipSuccess or the runtime's error).
 hipError_t launch_decode_partial(const DecodeArgs& a, bool kv_fp8, hipStream_t stream);
 hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// FP8 prefill: split (partials) or direct attention; then (out given) the combine.
+hipError_t launch_prefill(const PrefillArgs& a, bool split, hipStream_t stream);
+hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream);
 
 // Device address of the current device's copy of the no-allocation entry
 // point's scratch (SMLA_NOALLOC_SCRATCH_BYTES); looked up once per device.

@@ -1,0 +1,405 @@
+// HIP kernels for split-KV FP8 prefill attention on MI355X (gfx950, CDNA4).
+//
+// The operation follows cudnn-frontend PR #768 ("split kv ports", commit
+// messages and reviews): an FP8 SDPA prefill kernel with head dimension 128
+// whose split form cuts each query tile's masked KV range into SPLIT_KV
+// near-equal chunks of KV blocks (the remainder on the leading chunks; a chunk
+// past the end is empty: O = 0, LSE = -inf), writes split-major partial O and
+// LSE, and leaves the amax of the output to the combine, which owns the
+// recombined O.  The sink counts once, in the combine (or in the direct
+// epilogue when there is no split).
+//
+// prefill_kernel: one workgroup of 4 wave64s per (batch, 64-row query tile,
+// query head, split).  Wave w owns query rows [16w, 16w + 16) of the tile.
+//   * K and V blocks of 64 keys (e4m3, 8 KB each) are gathered with 16-byte
+//     direct-to-LDS loads (global_load_lds_dwordx4), double buffered: block
+//     b+1 is in flight while block b is computed.  Keys past the batch's key
+//     count copy a zero row, so no padding row is ever read.
+//   * S^T[key][row] = K . Q^T on the bf16 matrix core: Q (once) and the K
+//     fragments (8-byte LDS reads along a key row) are e4m3 codes converted to
+//     bf16 in registers, exactly.  Each lane holds 16 scores of one query row.
+//     The FP8 matrix core (v_mfma_f32_16x16x32_fp8_fp8) on the same codes was
+//     measured on the MI355X at about 2e-5 relative error in a score (the LSE of
+//     a row that sees one key is that key's score), twice the 1e-5 LSE bar; the
+//     bf16 form measured 7e-7 on the same inputs.
+//   * Softmax in log2 units against an integer frame M per row (the running
+//     floor of the row maximum): p = 2^(t - floor t) * 2^(floor t - M).  The
+//     bf16 rounding of 2^(t - floor t) does not depend on M, and a frame change
+//     rescales the accumulators by an exact power of two, so partials of any
+//     split count combine to the same value up to f32 summation order.
+//   * O^T[dim][row] += V^T . P^T on the bf16 matrix core, P as two bf16 terms
+//     (hi = bf16(p), lo = bf16(p - hi)).  V^T fragments come from the 8-bit
+//     transposing LDS read ds_read_b64_tr_b8 of the e4m3 V tile, converted to
+//     bf16 in registers (exact).  The P^T fragment is the lane's own scores:
+//     its k-elements are keys 4G .. 4G + 3 of one 16-key tile and 4G .. 4G + 3
+//     of the next, and the V^T reads fetch the same keys in the same order.
+//   * Epilogue: O = acc * descale_v / l, LSE = (M + log2 l) * ln 2.  Split:
+//     the partial and its LSE.  Direct: the sink, the cast, the LSE and the
+//     amax (one atomic max per wave on the bits of |O|, a non-negative float).
+//
+// The workgroups that read the same K/V (one batch, split and KV head: every
+// query tile and every query head of the head group) are numbered
+// consecutively and placed on one XCD: block ids go to the 8 XCDs round robin,
+// so logical workgroup (xcd * n + k) runs as block (k * 8 + xcd).
+//
+// prefill_combine_kernel: one wave per (batch, row, head); lane l merges
+// dimensions 2l, 2l + 1 over the splits, applies the sink, casts, and raises
+// the amax once per workgroup.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "smla.h"
+#include "smla_gfx950.h"
+#include "smla_internal.h"
+
+namespace smla {
+namespace {
+
+constexpr int kPRows = 64;              // query rows per tile: 4 waves x 16
+constexpr int kPKeys = 64;              // keys per KV block
+constexpr int kPDim = 128;              // head dimension (bytes per e4m3 row)
+constexpr int kPTile = kPKeys * kPDim;  // bytes of one K or V block in LDS
+constexpr float kPMasked = -3.0e38f;    // score of a masked key: its weight is exactly 0
+constexpr float kPNoFrame = 3.0e38f;    // frame of a row that has not seen a key yet
+constexpr float kLn2 = 0.69314718055994531f;
+
+enum { kPOutBf16 = 0, kPOutF32 = 1 };
+
+// Source of every key past the batch's key count.
+__device__ __attribute__((aligned(256))) uint8_t g_zero_kv[kPDim];
+
+// K / V block in LDS: key r is 128 bytes = 8 chunks of 16; chunk c sits at
+// 16-byte position r * 8 + (c ^ kvsw(r)).  Both read streams -- 8-byte K reads
+// of 16 keys x 2 chunks, and the V^T transpose reads of 32 keys x 1 chunk --
+// then touch all 16 groups of four LDS banks twice: 2 cycles per 512 bytes.
+__host__ __device__ constexpr int kvsw(int r) { return (r >> 1) & 7; }
+
+struct PrefillWork {
+  int b, s, hk, tile, h;
+};
+// Logical workgroup id -> work item; the ones sharing a (batch, split, KV head)
+// are consecutive.
+__device__ __forceinline__ PrefillWork prefill_work(const PrefillArgs& a, int logical) {
+  const int g = a.h_q / a.h_kv;
+  PrefillWork w;
+  int r = logical;
+  const int hg = r % g;
+  r /= g;
+  w.tile = r % a.n_tiles;
+  r /= a.n_tiles;
+  w.hk = r % a.h_kv;
+  r /= a.h_kv;
+  w.s = r % a.num_splits;
+  w.b = r / a.num_splits;
+  w.h = w.hk * g + hg;
+  return w;
+}
+
+__device__ __forceinline__ int clamp_len(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
+
+template <bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kPTile];   // [stage 0: K, V | stage 1: K, V]
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int j = lane & 15, G = lane >> 4;
+  // The split form's combine owns the amax: it starts at 0 (the combine's
+  // atomics come after this launch).
+  if (SPLIT && a.amax_out != nullptr && blockIdx.x == 0 && tid == 0) *a.amax_out = 0.0f;
+  const int per_xcd = (int)(gridDim.x >> 3);
+  const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (logical >= a.n_work) return;                      // padding of the grid
+  const PrefillWork w = prefill_work(a, logical);
+  const int sq = clamp_len(a.seqlen_q[w.b], a.sq_max);
+  const int skv = clamp_len(a.seqlen_kv[w.b], a.skv_max);
+  const int q0 = w.tile * kPRows;
+  if (q0 >= sq) return;                                 // a tile past this batch's rows
+
+  // The tile's masked KV range (the keys its last row may see) and this split's blocks of it.
+  const int shift = skv - sq;
+  const int last = min(sq, q0 + kPRows) - 1;
+  const int kv_end = CAUSAL ? clamp_len(last + shift + 1, skv) : skv;
+  const int n_blk = (kv_end + kPKeys - 1) / kPKeys;
+  int b0 = 0, b1 = n_blk;
+  if (SPLIT) {
+    const int base = n_blk / a.num_splits, rem = n_blk - base * a.num_splits;
+    b0 = w.s * base + min(w.s, rem);
+    b1 = b0 + base + (w.s < rem ? 1 : 0);
+  }
+
+  const int i = q0 + 16 * wave + j;                     // this lane's query row
+  const bool row_ok = i < sq;
+  const int vis = CAUSAL ? clamp_len(i + shift + 1, skv) : skv;   // keys [0, vis) visible to row i
+
+  float M = kPNoFrame;        // integer frame of row i (log2 units)
+  float l_run = 0.f;          // this lane's share of row i's denominator
+  f32x4 acc[8];               // O^T: dims 16 mt + 4G + e of row i
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (b0 < b1) {
+    // Q fragments (B operand of S^T = K . Q^T): row i, dims 32 ks + 8G .. +8,
+    // converted to bf16 once (exact).
+    bf16x8 qf[4];
+    {
+      const uint8_t* qrow =
+          a.q + ((int64_t)(w.b * a.sq_max + min(i, sq - 1)) * a.h_q + w.h) * kPDim + 8 * G;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[ks] = e4m3x8_to_bf16(*(const u32x2*)(qrow + 32 * ks));
+    }
+    const uint32_t lds0 = lds_addr(smem);
+    // Wave w gathers keys [16w, 16w + 16) of a block, K and V, in two groups of
+    // 8 keys: lane l fetches chunk (l & 7) ^ kvsw(key) of key 8 grp + (l >> 3),
+    // which lands in slot l & 7 of that key's row.
+    auto gather = [&](int kb, int st) {
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp) {
+        const int r = 16 * wave + 8 * grp + (lane >> 3);
+        const int key = kb * kPKeys + r;
+        const int c = (lane & 7) ^ kvsw(r);
+        const int64_t off = ((int64_t)(w.b * a.skv_max + key) * a.h_kv + w.hk) * kPDim + c * 16;
+        const bool ok = key < skv;
+        const uint8_t* ks = ok ? a.k + off : g_zero_kv + c * 16;
+        const uint8_t* vs = ok ? a.v + off : g_zero_kv + c * 16;
+        const uint32_t lk = __builtin_amdgcn_readfirstlane(lds0 + st * 2 * kPTile + (16 * wave + 8 * grp) * kPDim);
+        dma_one<0, 0, 0>(ks, lk);
+        dma_one<0, 0, 0>(vs, lk + kPTile);
+      }
+    };
+    // Per-lane LDS offsets of the operand reads.  K (k-step ks, key tile t):
+    // key 16t + j, chunk 2 ks + (G >> 1), half G & 1.  V^T (k-step kk, dim
+    // tile mt): lane j reads half j & 1 of key 32 kk + 16 (j >> 3) + 4G +
+    // ((j >> 1) & 3), chunk mt.
+    const int vr0 = 16 * (j >> 3) + 4 * G + ((j >> 1) & 3);
+    int vrow[2], vsw[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      vrow[kk] = (32 * kk + vr0) * kPDim + (j & 1) * 8;
+      vsw[kk] = kvsw(32 * kk + vr0);
+    }
+
+    gather(b0, 0);
+    for (int kb = b0; kb < b1; ++kb) {
+      const int st = (kb - b0) & 1;
+      wait_vmem_all();          // this wave's share of block kb has landed
+      lds_barrier();            // ... and every wave's; block kb - 1 fully read
+      if (kb + 1 < b1) gather(kb + 1, st ^ 1);
+      const uint32_t kt = lds0 + st * 2 * kPTile, vt = kt + kPTile;
+
+      // ---- S^T = K . Q^T: four key tiles of 16, four k-steps of 32 dims
+      f32x4 sacc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int r = 16 * t + j;
+          const uint32_t addr = kt + r * kPDim + (((2 * ks + (G >> 1)) ^ kvsw(r)) * 16) + (G & 1) * 8;
+          const bf16x8 kf = e4m3x8_to_bf16(*(const __attribute__((address_space(3))) u32x2*)(uintptr_t)addr);
+          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[t], 0, 0, 0);
+        }
+      }
+
+      // ---- softmax: lane scores of row i, keys kb*64 + 16t + 4G + e
+      float tv[16];
+      float m = kPMasked;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kb * kPKeys + 16 * t + 4 * G + e;
+          const float x = key < vis ? sacc[t][e] * a.scale_log2 : kPMasked;
+          tv[4 * t + e] = x;
+          m = fmaxf(m, x);
+        }
+      }
+      m = rows_max(m);                                   // the four lanes of row i
+      const bool any = m > kPMasked;
+      const float fm = floorf(m);
+      const float M_new = !any ? M : (M == kPNoFrame ? fm : fmaxf(M, fm));
+      if (any && M != kPNoFrame && M_new != M) {         // a new frame: rescale by an exact power of two
+        const float f = __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_amdgcn_fmed3f(M - M_new, -256.f, 0.f));
+        l_run *= f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) acc[mt] = acc[mt] * f;
+      }
+      M = M_new;
+      float pv[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float fl = floorf(tv[k]);
+        const float ex = __builtin_amdgcn_fmed3f(fl - M, -256.f, 256.f);
+        const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tv[k] - fl), (int)ex);
+        l_run += p;
+        pv[k] = p;
+      }
+      // P^T fragments of k-step kk: keys 4G .. +3 of tiles 2kk and 2kk + 1, hi and lo terms
+      bf16x8 ph[2], pl[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 h4, l4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = pv[8 * kk + 2 * q], x1 = pv[8 * kk + 2 * q + 1];
+          const uint32_t h2 = pack_bf16x2(x0, x1);
+          h4[q] = h2;
+          l4[q] = pack_bf16x2(x0 - __uint_as_float(h2 << 16), x1 - __uint_as_float(h2 & 0xFFFF0000u));
+        }
+        ph[kk] = __builtin_bit_cast(bf16x8, h4);
+        pl[kk] = __builtin_bit_cast(bf16x8, l4);
+      }
+
+      // ---- O^T += V^T . P^T: eight dim tiles of 16, two k-steps of 32 keys
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          typedef int i32x2v __attribute__((ext_vector_type(2)));
+          const uint32_t addr = vt + vrow[kk] + ((mt ^ vsw[kk]) * 16);
+          const i32x2v r =
+              __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2v*)(uintptr_t)addr);
+          const bf16x8 vf = e4m3x8_to_bf16(u32x2{(uint32_t)r[0], (uint32_t)r[1]});
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[kk], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kk], acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: row i's denominator over its four lanes; O = acc * descale_v / l
+  const float l = rows_sum(l_run);
+  const bool has = l > 0.f;
+  const float lse = has ? (M + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
+  float oscale = has ? a.descale_v / l : 0.f;
+  if (!SPLIT && a.sink != nullptr && has) oscale = oscale / (1.0f + __builtin_amdgcn_exp2f((a.sink[w.h] - lse) * kLog2e));
+  float amax = 0.f;
+  if (row_ok) {
+    const int64_t row = (int64_t)(w.b * a.sq_max + i) * a.h_q + w.h;
+    if (SPLIT) {
+      const int64_t prow = (int64_t)w.s * a.batch * a.sq_max * a.h_q + row;
+      float* dst = a.o_part + prow * kPDim + 4 * G;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) *(f32x4*)(dst + 16 * mt) = acc[mt] * oscale;
+      if (G == 0) a.lse_part[prow] = lse;
+    } else {
+      if (a.out_dtype == kPOutF32) {
+        float* dst = (float*)a.out + row * kPDim + 4 * G;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const f32x4 o = acc[mt] * oscale;
+          *(f32x4*)(dst + 16 * mt) = o;
+          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[0]), fabsf(o[1])), fmaxf(fabsf(o[2]), fabsf(o[3]))));
+        }
+      } else {
+        uint16_t* dst = (uint16_t*)a.out + row * kPDim + 4 * G;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const f32x4 o = acc[mt] * oscale;
+          *(u32x2*)(dst + 16 * mt) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[0]), fabsf(o[1])), fmaxf(fabsf(o[2]), fabsf(o[3]))));
+        }
+      }
+      if (G == 0 && a.lse_out != nullptr) a.lse_out[row] = lse;
+    }
+  }
+  if (!SPLIT && a.amax_out != nullptr) {
+    amax = wave_max(amax);
+    if (lane == 0)
+      __hip_atomic_fetch_max((uint32_t*)a.amax_out, __float_as_uint(amax), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The direct form's amax starts at 0 before the attention kernel's atomics.
+__global__ void prefill_amax_init_kernel(float* amax_out) { *amax_out = 0.0f; }
+
+// One wave per (batch, row, head): rows of the grid-stride loop r = wave_id,
+// wave_id + n_waves, ...; lane l merges dims 2l, 2l + 1.  The workgroup's amax
+// meets in LDS and raises amax_out once.
+__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
+  __shared__ float s_amax[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)a.batch * a.sq_max * a.h_q;
+  const int64_t pstride = rows;                                   // one split's rows
+  const int S = a.num_splits;
+  float amax = 0.f;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < rows; r += (int64_t)gridDim.x * 4) {
+    const int h = (int)(r % a.h_q);
+    const int64_t bi = r / a.h_q;
+    const int i = (int)(bi % a.sq_max);
+    const int b = (int)(bi / a.sq_max);
+    if (i >= clamp_len(a.seqlen_q[b], a.sq_max)) continue;        // a padding row (wave-uniform)
+    // weights: lane s holds split s's LSE (natural log)
+    float ws_own = 0.f, M = kNegInf;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int s = s0 + lane;
+      const float ls = s < S ? a.lse_part[(int64_t)s * pstride + r] : kNegInf;
+      M = fmaxf(M, wave_max(ls));
+    }
+    f32x2 o = {0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int s = s0 + lane;
+      const float ls = s < S ? a.lse_part[(int64_t)s * pstride + r] : kNegInf;
+      const float wl = (M == kNegInf || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
+      ws_own += wl;
+      const int n = min(64, S - s0);
+      for (int c = 0; c < n; ++c) {
+        const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), c));
+        const f32x2 x = *(const f32x2*)(a.o_part + ((int64_t)(s0 + c) * pstride + r) * kPDim + 2 * lane);
+        o = o + wc * x;
+      }
+    }
+    const float wsum = wave_sum(ws_own);
+    const bool none = M == kNegInf;
+    const float lse = none ? kNegInf : M + __builtin_amdgcn_logf(wsum) * kLn2;
+    float f = none ? 0.f : 1.0f / wsum;
+    if (a.sink != nullptr && !none) f = f / (1.0f + __builtin_amdgcn_exp2f((a.sink[h] - lse) * kLog2e));
+    o = o * f;
+    if (a.out_dtype == kPOutF32)
+      *(f32x2*)((float*)a.out + r * kPDim + 2 * lane) = o;
+    else
+      *(uint32_t*)((uint16_t*)a.out + r * kPDim + 2 * lane) = pack_bf16x2(o[0], o[1]);
+    if (lane == 0 && a.lse_out != nullptr) a.lse_out[r] = lse;
+    amax = fmaxf(amax, fmaxf(fabsf(o[0]), fabsf(o[1])));
+  }
+  if (a.amax_out == nullptr) return;
+  amax = wave_max(amax);
+  if (lane == 0) s_amax[wave] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float v = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+    __hip_atomic_fetch_max((uint32_t*)a.amax_out, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, bool split, hipStream_t stream) {
+  const unsigned grid = (unsigned)((a.n_work + 7) / 8 * 8);
+  if (!split && a.amax_out != nullptr) hipLaunchKernelGGL(prefill_amax_init_kernel, dim3(1), dim3(1), 0, stream, a.amax_out);
+  if (a.causal) {
+    if (split)
+      hipLaunchKernelGGL((prefill_kernel<true, true>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<true, false>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    if (split)
+      hipLaunchKernelGGL((prefill_kernel<false, true>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(grid), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.batch * a.sq_max * a.h_q;
+  const int64_t want = (rows + 3) / 4;
+  const int64_t cap = 4 * (int64_t)(a.cus > 0 ? a.cus : 256);    // at most 4 workgroups (and atomics) a CU
+  const unsigned grid = (unsigned)(want < cap ? want : cap);
+  hipLaunchKernelGGL(prefill_combine_kernel, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace smla

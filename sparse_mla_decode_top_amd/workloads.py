@@ -157,3 +157,74 @@ WORKLOADS = {
 def make_workload_inputs(w, seed):
     return make_inputs(w.s_q, w.h_q, w.n_pool, w.topk, seed, kv_dtype=w.kv_dtype,
                        sink=w.sink, pad=w.pad)
+
+
+# ---------------------------------------------------------------------------
+# Split-KV FP8 prefill inputs
+# ---------------------------------------------------------------------------
+@dataclass
+class PrefillInputs:
+    batch: int
+    h_q: int
+    h_kv: int
+    sq_max: int
+    skv_max: int
+    causal: bool
+    scale: float
+    q_codes: np.ndarray                # uint8 [B, Sq, h_q, 128]
+    k_codes: np.ndarray                # uint8 [B, Skv, h_kv, 128]
+    v_codes: np.ndarray
+    descale_q: float
+    descale_k: float
+    descale_v: float
+    seqlen_q: np.ndarray               # int32 [B]
+    seqlen_kv: np.ndarray              # int32 [B]
+    sink: np.ndarray = None            # float32 [h_q] or None
+
+
+def _quantize_per_tensor(x, valid):
+    """Per-tensor e4m3 codes of x: descale = amax / 448 over the valid entries (float32),
+    codes = RNE e4m3 of x / descale (clamped to +-448); padding entries get the NaN code."""
+    amax = float(np.abs(x[valid]).max()) if valid.any() else 1.0
+    descale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    y = np.clip(x / descale, -448.0, 448.0).astype(np.float32)
+    codes = _e4m3_codes_of(y)
+    codes[~valid] = 0x7F
+    return codes, float(descale)
+
+
+def make_prefill_inputs(batch, h_q, h_kv, sq_max, skv_max, seed, seqlen_q=None, seqlen_kv=None,
+                        causal=True, sink=True):
+    """One seeded prefill case.  numpy default_rng(seed), draws in the order q, k, v,
+    sink: standard normal float32, quantised per tensor to e4m3 (descale = amax / 448
+    over the rows present).  seqlen_q / seqlen_kv default to the padded sizes.  Rows
+    past a batch's length (padding) hold the e4m3 NaN code 0x7F, so a read of one
+    shows up in the output.  softmax scale = float32(1 / sqrt(128))."""
+    rng = np.random.default_rng(seed)
+    sq = np.full(batch, sq_max, np.int32) if seqlen_q is None else np.asarray(seqlen_q, np.int32)
+    skv = np.full(batch, skv_max, np.int32) if seqlen_kv is None else np.asarray(seqlen_kv, np.int32)
+    qv = rng.standard_normal((batch, sq_max, h_q, 128), dtype=np.float32)
+    kv = rng.standard_normal((batch, skv_max, h_kv, 128), dtype=np.float32)
+    vv = rng.standard_normal((batch, skv_max, h_kv, 128), dtype=np.float32)
+    qmask = np.zeros(qv.shape, bool)
+    kmask = np.zeros(kv.shape, bool)
+    for b in range(batch):
+        qmask[b, :sq[b]] = True
+        kmask[b, :skv[b]] = True
+    q_codes, dq = _quantize_per_tensor(qv, qmask)
+    k_codes, dk = _quantize_per_tensor(kv, kmask)
+    v_codes, dv = _quantize_per_tensor(vv, kmask)
+    sink_arr = rng.standard_normal(h_q, dtype=np.float32) if sink else None
+    return PrefillInputs(batch=batch, h_q=h_q, h_kv=h_kv, sq_max=sq_max, skv_max=skv_max, causal=causal,
+                         scale=float(np.float32(1.0 / np.sqrt(128.0))), q_codes=q_codes, k_codes=k_codes,
+                         v_codes=v_codes, descale_q=dq, descale_k=dk, descale_v=dv, seqlen_q=sq,
+                         seqlen_kv=skv, sink=sink_arr)
+
+
+# Prefill workloads: (batch, h_q, h_kv, Sq, Skv, causal).  "prefill_chunk" is a chunk of
+# 256 new tokens per sequence over an 8,192-token cache (the case a split-KV prefill
+# serves: few query tiles, long KV ranges); "prefill_full" a whole 4,096-token prompt.
+PREFILL_WORKLOADS = {
+    "prefill_chunk": (2, 32, 8, 256, 8192, True),
+    "prefill_full": (1, 32, 8, 4096, 4096, True),
+}
