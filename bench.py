@@ -21,7 +21,7 @@ Prints ONE JSON line (rank 0, N = 1):
   cold_us_per_step  the same step with the caches flushed before each step
   cpu_baseline the float64 oracle timed on the host cores on the same inputs
   sweep        the same measurement at s_q = 6, 16, 96, 384 and for the FP8
-               path (context)
+               path, and the split-KV FP8 prefill workloads (context)
 """
 import argparse
 import hashlib
@@ -384,6 +384,98 @@ def kernel_bytes(name, S):
     return b
 
 
+def prefill_work(name, W):
+    """Algorithmic flops and HBM bytes of one prefill step of a workload: 4 * 128
+    flops (QK^T and PV) per visible (row, key) pair and query head; bytes = the e4m3
+    Q, K, V read once plus the bf16 output (split partials are overhead, not counted)."""
+    B, hq, hk, sq, skv, causal = W.PREFILL_WORKLOADS[name]
+    pairs = 0
+    for i in range(sq):
+        pairs += min(skv, max(0, i + skv - sq + 1)) if causal else skv
+    flops = 4 * 128 * pairs * hq * B
+    nbytes = B * (sq * hq * 128 + 2 * skv * hk * 128 + sq * hq * 128 * 2)
+    return flops, nbytes
+
+
+def measure_prefill(name, steps, warmup, reps, torch, smla, W):
+    """Graph-replayed step (attention + combine), the attention kernel alone (event
+    batch), and the cold step, for one prefill workload."""
+    B, hq, hk, sq, skv, causal = W.PREFILL_WORKLOADS[name]
+    inp = W.make_prefill_inputs(B, hq, hk, sq, skv, 7, causal=causal)
+    c = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    q, k, v, lq, lk, sink = c(inp.q_codes), c(inp.k_codes), c(inp.v_codes), c(inp.seqlen_q), c(inp.seqlen_kv), \
+        c(inp.sink)
+    S = smla.smla_prefill_choose_splits(B, sq, skv, hq, 256)
+    o_part = torch.empty((S, B, sq, hq, 128), device="cuda") if S > 1 else None
+    lse_part = torch.empty((S, B, sq, hq), device="cuda") if S > 1 else None
+    out = torch.empty((B, sq, hq, 128), device="cuda", dtype=torch.bfloat16)
+    amax = torch.empty((1,), device="cuda")
+
+    def step(with_out=True):
+        smla.sdpa_fp8_prefill(q, k, v, lq, lk, S, inp.scale, inp.descale_q, inp.descale_k, inp.descale_v,
+                              causal=causal, sink=sink, o_part=o_part, lse_part=lse_part,
+                              out=out if (with_out or S == 1) else None, amax_out=amax)
+
+    step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / steps
+
+    def batch(fn):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cyc = sleep_cycles_for(5 + reps * 0.1, torch)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(cyc)
+        a0.record(stream)
+        for _ in range(reps):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) * 1e3 / reps
+
+    main_us = batch(lambda: step(with_out=False))
+    full_us = batch(step)
+    flush = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    evs = []
+    for i in range(max(10, steps // 4)):
+        flush.fill_(float(i & 7))
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        step()
+        a1.record(stream)
+        evs.append((a0, a1))
+    torch.cuda.synchronize()
+    del flush
+    cold_us = float(np.median([x.elapsed_time(y) * 1e3 for x, y in evs]))
+    flops, nbytes = prefill_work(name, W)
+    return {"batch": B, "h_q": hq, "h_kv": hk, "s_q": sq, "s_kv": skv, "causal": causal, "num_splits": S,
+            "us_per_step": round(step_us, 2), "cold_us_per_step": round(cold_us, 2),
+            "attention_kernel_us": round(main_us, 2), "combine_us": round(max(full_us - main_us, 0.0), 2),
+            "algorithmic_tflops": round(flops / (main_us * 1e-6) / 1e12, 1),
+            "kernel_mfma_frac": round(flops / (main_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "step_tflops": round(flops / (step_us * 1e-6) / 1e12, 1),
+            "kernel_hbm_frac": round(nbytes / (main_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "flops_per_step": flops, "bytes_per_step": nbytes}
+
+
 def _csv_rows(directory, suffix):
     import csv
     import glob
@@ -701,6 +793,13 @@ def main():
                                                      / BF16_PEAK_TFLOPS, 4)}
             log(f"{name}: {r['ev_us']:.2f} us/step, kernel {r['main_us']:.2f} us, cold step {r['cold_us']:.2f} us, "
                 f"S={r['S']}")
+        for name in W.PREFILL_WORKLOADS:
+            r = measure_prefill(name, max(20, args.steps // 4), args.warmup, max(20, args.kernel_reps // 4),
+                                torch, smla, W)
+            torch.cuda.empty_cache()
+            sweep[name] = r
+            log(f"{name}: {r['us_per_step']:.2f} us/step, kernel {r['attention_kernel_us']:.2f} us "
+                f"({r['algorithmic_tflops']} TFLOP/s), S={r['num_splits']}")
 
     line = {
         "metric": METRIC, "value": round(head["ev_us"], 3), "unit": "us/step", "n_gpus": 1,
