@@ -84,6 +84,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=100)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="measure only the split-KV FP8 prefill workloads and print their results as one JSON line")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only a plain 256 MiB device copy (calibrates the HBM byte counters)")
     ap.add_argument("--kernel-stats", metavar="DIR",
@@ -608,7 +610,7 @@ def pmc_summary(dirs):
         print(f"{k[:56]:56s} {c:32s} {len(disp):10d} {np.mean(sums):16.1f} {np.mean(maxs):16.1f}")
     # GRBM_GUI_ACTIVE comes summed over the 8 XCDs: a dispatch's active cycles are a
     # eighth of it (the MFMA loop probe then reads ~96% busy, as a pure MFMA loop should).
-    for k in sorted({k for k, _ in stats if "decode_kernel" in k or "mfma_loop" in k}):
+    for k in sorted({k for k, _ in stats if any(n in k for n in ("decode_kernel", "mfma_loop", "prefill_kernel"))}):
         busy = stats.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"))
         active = stats.get((k, "GRBM_GUI_ACTIVE"))
         mops = stats.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
@@ -744,6 +746,11 @@ def main():
     smla.load_library()
     if args.copy_only:
         copy_only(torch)
+        return
+    if args.prefill_only:
+        res = {name: measure_prefill(name, args.steps, args.warmup, args.kernel_reps, torch, smla, W)
+               for name in W.PREFILL_WORKLOADS}
+        print(json.dumps({"prefill": res}), flush=True)
         return
 
     head, layers = measure(args.workload, args.num_splits, args.steps, args.warmup, args.kernel_reps,
