@@ -51,7 +51,8 @@ MAIN_BYTES_PER_TOKEN = KV_BYTES + Q_BYTES + IDX_BYTES     # 813,568: the attenti
 MAIN_BYTES_PER_TOKEN_FP8 = 640 * (576 + 4) + Q_BYTES + IDX_BYTES   # e4m3 rows + row scales: 447,488
 STEP_BYTES_PER_TOKEN = MAIN_BYTES_PER_TOKEN + OUT_BYTES   # 879,104
 FLOPS_PER_TOKEN = 2 * 64 * 640 * (576 + 512)              # 89,128,960
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_mla_decode_top_amd", "csrc", "smla_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_mla_decode_top_amd", "csrc", f)
+                  for f in ("smla_kernels.hip", "smla_gfx950.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_kernel_single_token.json")
 
 WORKLOADS = {   # name -> (s_q, n_pool, pool dtype / output dtype, fixed num_splits or 0)
@@ -101,11 +102,14 @@ def parse_args():
 
 
 def source_hash():
-    """Hash of the kernel source's code: comments and whitespace removed, so that
-    only a change to the code makes a recorded traffic figure stale."""
+    """Hash of the decode kernels' code (their source and the shared device header):
+    comments and whitespace removed, so that only a change to the code makes a
+    recorded traffic figure stale."""
     import re
-    with open(KERNEL_SOURCE) as f:
-        text = f.read()
+    text = ""
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())

@@ -106,9 +106,12 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
   return __builtin_bit_cast(bf16x8, o);
 }
 
+// Two floats as packed bf16 (round to nearest even), `lo` in the low half: one
+// v_cvt_pk_bf16_f32 (two scalar conversions would take two and a merge).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
 }
 
 }  // namespace smla

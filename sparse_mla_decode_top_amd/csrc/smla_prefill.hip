@@ -127,7 +127,7 @@ template <bool CAUSAL, bool SPLIT, int STAGES, int HPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * 2 * kPTile];   // per stage: K, then V
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int j = lane & 15, G = lane >> 4;
   // The split form's combine owns the amax: it starts at 0 (the combine's
   // atomics come after this launch).
@@ -242,39 +242,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
 
       // ---- softmax per head: lane scores of row i, keys kb*64 + 16t + 4G + e
-      const bool full = kb * kPKeys + kPKeys <= vis_lo;   // every key of the block visible to every row
+      const bool full = kb * kPKeys + kPKeys <= vis_lo;   // every key of the block visible to every row (uniform)
       bf16x8 ph[HPW][2], pl[HPW][2];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
+        // (The empty volatile statements keep both branches as uniform jumps: the
+        // compiler would otherwise evaluate both sides and select.)
         float tv[16];
-        float m = kPMasked;
+        if (full) {
+          asm volatile("");
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+          for (int k = 0; k < 16; ++k) tv[k] = sacc[hh][k >> 2][k & 3] * a.scale_log2;
+        } else {
+          asm volatile("");
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = kb * kPKeys + 16 * t + 4 * G + e;
-            const float x = (full || key < vis) ? sacc[hh][t][e] * a.scale_log2 : kPMasked;
-            tv[4 * t + e] = x;
-            m = fmaxf(m, x);
+          for (int k = 0; k < 16; ++k) {
+            const int key = kb * kPKeys + 16 * (k >> 2) + 4 * G + (k & 3);
+            tv[k] = key < vis ? sacc[hh][k >> 2][k & 3] * a.scale_log2 : kPMasked;
           }
         }
+        float m = kPMasked;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) m = fmaxf(m, tv[k]);
         m = rows_max(m);                                 // the four lanes of row i
         const bool any = m > kPMasked;
         const float fm = floorf(m);
         const float M_new = !any ? M[hh] : (M[hh] == kPNoFrame ? fm : fmaxf(M[hh], fm));
-        if (any && M[hh] != kPNoFrame && M_new != M[hh]) {  // a new frame: rescale by an exact power of two
-          const float f = __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_amdgcn_fmed3f(M[hh] - M_new, -256.f, 0.f));
+        const bool moved = any && M[hh] != kPNoFrame && M_new != M[hh];
+        if (__builtin_amdgcn_ballot_w64(moved) != 0) {   // a row took a new frame: rescale by an exact power of two
+          asm volatile("");
+          const float f =
+              moved ? __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_amdgcn_fmed3f(M[hh] - M_new, -256.f, 0.f)) : 1.0f;
           l_run[hh] *= f;
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt) acc[hh][mt] = acc[hh][mt] * f;
         }
         M[hh] = M_new;
+        // p = 2^(t - floor t) * 2^(floor t - M), with the integer parts as saturating
+        // int32: a masked key (t = -3e38) and a row with no frame yet (M = 3e38)
+        // both give an exponent of -2^31, so p = 0.  Exact for |t| < 2^31.
+        int Mi;
+        asm("v_cvt_i32_f32 %0, %1" : "=v"(Mi) : "v"(M_new));
         float pv[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const float fl = floorf(tv[k]);
-          const float ex = __builtin_amdgcn_fmed3f(fl - M[hh], -256.f, 256.f);
-          const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tv[k] - fl), (int)ex);
+          int fi;
+          asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(fi) : "v"(tv[k]));
+          const int ex = __builtin_elementwise_sub_sat(fi, Mi);
+          const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(tv[k])), ex);
           l_run[hh] += p;
           pv[k] = p;
         }
