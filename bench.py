@@ -411,7 +411,7 @@ def measure_prefill(name, steps, warmup, reps, torch, smla, W):
     c = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     q, k, v, lq, lk, sink = c(inp.q_codes), c(inp.k_codes), c(inp.v_codes), c(inp.seqlen_q), c(inp.seqlen_kv), \
         c(inp.sink)
-    S = smla.smla_prefill_choose_splits(B, sq, skv, hq, 256)
+    S = smla.smla_prefill_choose_splits(B, sq, skv, hq, hk, 256)
     o_part = torch.empty((S, B, sq, hq, 128), device="cuda") if S > 1 else None
     lse_part = torch.empty((S, B, sq, hq), device="cuda") if S > 1 else None
     out = torch.empty((B, sq, hq, 128), device="cuda", dtype=torch.bfloat16)

@@ -272,13 +272,16 @@ size_t smla_prefill_partial_bytes(int32_t batch, int32_t max_s_q, int32_t h_q, i
 
 /*
  * smla_prefill_choose_splits -- a split count that gives a grid of few query
- * tiles enough workgroups for `num_cus` compute units: 1 when
- * batch * ceil(max_s_q / 64) * h_q already fills two rounds, else the count
- * that brings it to about two rounds, capped at the KV blocks of the longest
- * range (ceil(max_s_kv / 64)) and at 16.  Deterministic.  Returns >= 1, or 0
- * for a non-positive argument.
+ * tiles enough workgroups for `num_cus` compute units (a performance choice,
+ * cudnn-frontend PR #768 leaves SPLIT_KV to the caller).  The unsplit launch
+ * has batch * ceil(max_s_q / 64) * h_q / HPW workgroups, HPW = 2 query heads a
+ * workgroup when h_q / h_kv is even, else 1: 1 when that fills two rounds
+ * (two workgroups a compute unit), else the count that brings it to about two
+ * rounds, capped at the KV blocks of the longest range (ceil(max_s_kv / 64))
+ * and at 16.  Deterministic.  Returns >= 1, or 0 for a non-positive argument
+ * or h_q not a multiple of h_kv.
  */
-int32_t smla_prefill_choose_splits(int32_t batch, int32_t max_s_q, int32_t max_s_kv, int32_t h_q,
+int32_t smla_prefill_choose_splits(int32_t batch, int32_t max_s_q, int32_t max_s_kv, int32_t h_q, int32_t h_kv,
                                    int32_t num_cus);
 
 /* smla_status_string -- a static, human-readable name of a status code. */

@@ -68,7 +68,7 @@ SIGNATURES = {
     "sdpa_fp8_prefill": (ctypes.c_int, [ctypes.POINTER(SmlaPrefillParams), _vp, _vp, _vp, _vp, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "smla_prefill_partial_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 4),
-    "smla_prefill_choose_splits": (ctypes.c_int32, [ctypes.c_int32] * 5),
+    "smla_prefill_choose_splits": (ctypes.c_int32, [ctypes.c_int32] * 6),
 }
 
 
@@ -266,8 +266,8 @@ def smla_prefill_partial_bytes(batch, max_s_q, h_q, split_kv):
     return int(load_library().smla_prefill_partial_bytes(batch, max_s_q, h_q, split_kv))
 
 
-def smla_prefill_choose_splits(batch, max_s_q, max_s_kv, h_q, num_cus=256):
-    return int(load_library().smla_prefill_choose_splits(batch, max_s_q, max_s_kv, h_q, num_cus))
+def smla_prefill_choose_splits(batch, max_s_q, max_s_kv, h_q, h_kv, num_cus=256):
+    return int(load_library().smla_prefill_choose_splits(batch, max_s_q, max_s_kv, h_q, h_kv, num_cus))
 
 
 def make_prefill_params(batch, h_q, h_kv, max_s_q, max_s_kv, softmax_scale, descale_q=1.0, descale_k=1.0,

@@ -240,11 +240,13 @@ size_t smla_prefill_partial_bytes(int32_t batch, int32_t max_s_q, int32_t h_q, i
   return (size_t)split_kv * (size_t)batch * (size_t)max_s_q * (size_t)h_q * (size_t)(128 * 4 + 4);
 }
 
-int32_t smla_prefill_choose_splits(int32_t batch, int32_t max_s_q, int32_t max_s_kv, int32_t h_q,
+int32_t smla_prefill_choose_splits(int32_t batch, int32_t max_s_q, int32_t max_s_kv, int32_t h_q, int32_t h_kv,
                                    int32_t num_cus) {
-  if (batch < 1 || max_s_q < 1 || max_s_kv < 1 || h_q < 1 || num_cus < 1) return 0;
-  // Workgroups of the unsplit launch: one per (batch, 64-row tile, head).
-  const int64_t tiles = (int64_t)batch * ((max_s_q + 63) / 64) * h_q;
+  if (batch < 1 || max_s_q < 1 || max_s_kv < 1 || h_q < 1 || h_kv < 1 || num_cus < 1 || h_q % h_kv != 0) return 0;
+  // Workgroups of the unsplit launch: one per (batch, 64-row tile, head pair
+  // when a KV head serves an even number of query heads, else head).
+  const int64_t hpw = (h_q / h_kv) % 2 == 0 ? 2 : 1;
+  const int64_t tiles = (int64_t)batch * ((max_s_q + 63) / 64) * (h_q / hpw);
   const int64_t target = 2 * (int64_t)num_cus;
   if (tiles >= target) return 1;
   int64_t s = (target + tiles - 1) / tiles;

@@ -410,7 +410,8 @@ __global__ __launch_bounds__(1024) void prefill_combine_kernel(PrefillArgs a) {
     const float* op = a.o_part + r * kPDim + 2 * lane;
     f32x2 x[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) x[c] = *(const f32x2*)(op + (int64_t)min(c, S - 1) * rows * kPDim);
+    for (int c = 0; c < 8; ++c)
+      if (c < S) x[c] = *(const f32x2*)(op + (int64_t)c * rows * kPDim);
     float M = kNegInf;
     for (int s0 = 0; s0 < S; s0 += 64) {
       const int s = s0 + lane;
@@ -427,13 +428,14 @@ __global__ __launch_bounds__(1024) void prefill_combine_kernel(PrefillArgs a) {
         if (s0 + c0 > 0) {
 #pragma unroll
           for (int c = 0; c < 8; ++c)
-            x[c] = *(const f32x2*)(op + (int64_t)min(s0 + c0 + c, S - 1) * rows * kPDim);
+            if (s0 + c0 + c < S) x[c] = *(const f32x2*)(op + (int64_t)(s0 + c0 + c) * rows * kPDim);
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(c0 + c, 63)));
-          const f32x2 o2 = o + wc * x[c];
-          o = s0 + c0 + c < S ? o2 : o;
+          if (s0 + c0 + c < S) {
+            const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(c0 + c, 63)));
+            o = o + wc * x[c];
+          }
         }
       }
     }

@@ -70,6 +70,25 @@ def test_choose_num_splits_properties():
     assert smla.smla_choose_num_splits(16, 64, 640, 256) == smla.smla_choose_num_splits(16, 64, 640, 256)
 
 
+def test_prefill_choose_splits_rule():
+    """Workgroups of the unsplit prefill launch: batch x 64-row tiles x h_q / HPW (HPW = 2
+    when h_q / h_kv is even); S brings them to about two per compute unit, capped at the
+    KV blocks and at 16."""
+    c = smla.smla_prefill_choose_splits
+    assert c(2, 256, 8192, 32, 8, 256) == 4          # 128 workgroups unsplit
+    assert c(1, 4096, 4096, 32, 8, 256) == 1         # 1,024 already fill two rounds
+    assert c(1, 256, 8192, 6, 2, 256) == 16          # odd ratio: 24 workgroups -> 22, capped at 16
+    assert c(1, 64, 8192, 32, 32, 64) == 4           # one query head a KV head: 32 workgroups
+    assert c(1, 64, 8192, 32, 16, 64) == 8           # pairs: 16 workgroups
+    assert c(1, 64, 100, 2, 1, 256) == 2             # 1 workgroup -> capped at the 2 KV blocks
+    assert c(4, 64, 8192, 8, 8, 256) == 16           # 32 workgroups -> 16
+    assert c(1, 64, 8192, 64, 1, 256) == 16          # HPW 2: 32 workgroups -> 16
+    assert c(1, 64, 8192, 64, 1, 64) == 4            # scales with the CU count
+    assert c(1, 256, 8192, 6, 4, 256) == 0           # h_q not a multiple of h_kv
+    assert c(0, 256, 8192, 32, 8, 256) == 0
+    assert c(1, 256, 8192, 32, 0, 256) == 0
+
+
 def _p(**kw):
     base = dict(s_q=2, h_q=64, topk=640, n_pool=1000, kv_row_stride=576, softmax_scale=1 / 24,
                 kv_dtype=B.KV_BF16, out_dtype=B.OUT_BF16)

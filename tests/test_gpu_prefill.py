@@ -185,7 +185,7 @@ def test_prefill_workload_sampled_rows(name):
     print(f"[case] prefill workload {name}", flush=True)
     dev = Dev(W.make_prefill_inputs(B, hq, hk, sq, skv, 0, causal=causal))
     inp = dev.inp
-    S = smla.smla_prefill_choose_splits(B, sq, skv, hq, 256)
+    S = smla.smla_prefill_choose_splits(B, sq, skv, hq, hk, 256)
     res = run(dev, S, "bf16", "split" if S > 1 else "direct")
     q = P.dequantize(inp.q_codes, inp.descale_q)
     k = P.dequantize(inp.k_codes, inp.descale_k)
