@@ -2490,20 +2490,24 @@ hipError_t launch_decode_direct(const DecodeArgs& a, bool kv_fp8, hipStream_t st
 
 namespace {
 // The FP8 output's combine.  One launch while the whole grid fits one
-// workgroup per compute unit (quarter rows per wave up to as many rows as
-// CUs, half rows up to twice as many, then whole rows, 4, 8 or 16 per
-// workgroup), else the two passes.
+// workgroup per compute unit: quarter rows per wave, 2 rows a workgroup, up to
+// as many rows as CUs; half rows, 2 rows a workgroup, up to twice as many;
+// half rows, 8 a workgroup, up to 4x; then whole rows, 8 or 16 a workgroup.
+// A token's workgroups all count in on one counter, so fewer workgroups a
+// token mean fewer atomics in line there: 2 rows a workgroup at one token
+// (32 workgroups) measured 0.6 us faster than 1 (64), and 8 at 16 tokens 2 us
+// faster than 4.  Else the two passes.
 template <int CHUNK>
 void launch_combine_fp8(const CombineArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.s_q * a.h_q;
   const int64_t cus = a.cus;
   const dim3 g4((unsigned)(rows / 4)), g8((unsigned)(rows / 8)), g16((unsigned)(rows / 16));
   if (rows <= cus)
-    hipLaunchKernelGGL((combine_fp8_kernel<4, CHUNK, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((combine_fp8_kernel<8, CHUNK, 4>), dim3((unsigned)(rows / 2)), dim3(512), 0, stream, a);
   else if (rows <= 2 * cus)
     hipLaunchKernelGGL((combine_fp8_kernel<4, CHUNK, 2>), dim3((unsigned)(rows / 2)), dim3(256), 0, stream, a);
   else if (rows <= 4 * cus)
-    hipLaunchKernelGGL((combine_fp8_kernel<4, CHUNK, 1>), g4, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((combine_fp8_kernel<16, CHUNK, 2>), dim3((unsigned)(rows / 8)), dim3(1024), 0, stream, a);
   else if (rows <= 8 * cus)
     hipLaunchKernelGGL((combine_fp8_kernel<8, CHUNK, 1>), g8, dim3(512), 0, stream, a);
   else if (rows <= 16 * cus)

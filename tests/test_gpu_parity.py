@@ -317,9 +317,9 @@ def test_fp8_output_leaves_partials_and_matches_standalone_combine(name, S):
     """An FP8 output through sparse_mla_decode leaves o_accum / lse_accum holding exactly
     the partials of a partial-only run (the partial protocol), and its codes, scales and
     LSEs equal combine_splits run on those partials afterwards.  The shapes cover every
-    combine layout but two: one launch in quarter rows (64 rows), half rows (384) and
-    whole rows 4 per workgroup (1,024), and the two-pass form (6,144 rows); the encoder
-    test below covers 8 and 16 rows per workgroup.  The FP8
+    combine layout but two: one launch in quarter rows 2 per workgroup (64 rows), half
+    rows 2 per workgroup (384) and half rows 8 per workgroup (1,024), and the two-pass
+    form (6,144 rows); the encoder test below covers whole rows 8 and 16 per workgroup.  The FP8
     values are also held to the oracle bound of the FP8 workloads."""
     import sparse_mla_decode_top_amd as smla
     dev = dev_for(name, 0)
