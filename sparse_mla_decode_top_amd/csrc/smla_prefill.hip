@@ -49,9 +49,10 @@
 // consecutively and placed on one XCD: block ids go to the 8 XCDs round robin,
 // so logical workgroup (xcd * n + k) runs as block (k * 8 + xcd).
 //
-// prefill_combine_kernel: one wave per (batch, row, head); lane l merges
-// dimensions 2l, 2l + 1 over the splits, applies the sink, casts, and raises
-// the amax once per workgroup of 16 rows.
+// prefill_combine_kernel: one wave per 4 consecutive (batch, row, head) rows
+// in turn; a row's split LSEs come through scalar loads, and lane l merges
+// dimensions 2l, 2l + 1 over the splits, applies the sink, casts, and the
+// workgroup raises the amax once for its 64 rows.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -71,7 +72,11 @@ constexpr int kPTile = kPKeys * kPDim;  // bytes of one K or V block in LDS
 constexpr float kPMasked = -3.0e38f;    // score of a masked key: its weight is exactly 0
 constexpr float kPNoFrame = 3.0e38f;    // frame of a row that has not seen a key yet
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kPStages = 3;             // K/V blocks in LDS: one computed, up to two in flight (48 KB: 3 workgroups a CU)
+constexpr int kPStages = 3;
+// Rows a combine wave merges in turn: the workgroups (16 waves) then raise the
+// amax with 4x fewer atomics, which all land on one word (measured: with one
+// row a wave the amax atomics cost about 4 us of the chunked prefill's combine).
+constexpr int kPCombineRows = 4;             // K/V blocks in LDS: one computed, up to two in flight (48 KB: 3 workgroups a CU)
 
 enum { kPOutBf16 = 0, kPOutF32 = 1 };
 
@@ -392,65 +397,62 @@ __global__ void prefill_amax_init_kernel(float* amax_out) { *amax_out = 0.0f; }
 // the value already there.
 __global__ __launch_bounds__(1024) void prefill_combine_kernel(PrefillArgs a) {
   __shared__ float s_amax[16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t rows = (int64_t)a.batch * a.sq_max * a.h_q;      // one split's rows
   const int S = a.num_splits;
-  const int64_t r = (int64_t)blockIdx.x * 16 + wave;
   float amax = 0.f;
-  bool live = r < rows;
-  int h = 0;
-  if (live) {
-    h = (int)(r % a.h_q);
-    const int64_t bi = r / a.h_q;
-    const int i = (int)(bi % a.sq_max);
-    const int b = (int)(bi / a.sq_max);
-    live = i < clamp_len(a.seqlen_q[b], a.sq_max);               // not a padding row
-  }
-  if (live) {
-    const float* op = a.o_part + r * kPDim + 2 * lane;
-    f32x2 x[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (c < S) x[c] = *(const f32x2*)(op + (int64_t)c * rows * kPDim);
-    float M = kNegInf;
-    for (int s0 = 0; s0 < S; s0 += 64) {
-      const int s = s0 + lane;
-      M = fmaxf(M, wave_max(s < S ? a.lse_part[(int64_t)s * rows + r] : kNegInf));
+  for (int k = 0; k < kPCombineRows; ++k) {
+    const int64_t r = ((int64_t)blockIdx.x * 16 + wave) * kPCombineRows + k;    // this wave's row (uniform)
+    bool live = r < rows;
+    int h = 0;
+    if (live) {
+      h = (int)(r % a.h_q);
+      const int64_t bi = r / a.h_q;
+      const int i = (int)(bi % a.sq_max);
+      const int b = (int)(bi / a.sq_max);
+      live = i < clamp_len(a.seqlen_q[b], a.sq_max);               // not a padding row
     }
-    f32x2 o = {0.f, 0.f};
-    float ws_own = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 64) {
-      const int s = s0 + lane;
-      const float ls = s < S ? a.lse_part[(int64_t)s * rows + r] : kNegInf;
-      const float wl = (M == kNegInf || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
-      ws_own += wl;
-      for (int c0 = 0; c0 < min(64, S - s0); c0 += 8) {
-        if (s0 + c0 > 0) {
+    if (live) {
+      // The row's split LSEs are the same for every lane: scalar loads (the
+      // partials are only read here).
+      typedef const __attribute__((address_space(4))) float* clse_t;
+      const clse_t lse = (clse_t)(const void*)a.lse_part;
+      float M = kNegInf;
+      for (int s = 0; s < S; ++s) M = fmaxf(M, lse[(int64_t)s * rows + r]);
+      const float* op = a.o_part + r * kPDim + 2 * lane;
+      f32x2 o = {0.f, 0.f};
+      float wsum = 0.f;
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        f32x2 x[8];
+        float w[8];
 #pragma unroll
-          for (int c = 0; c < 8; ++c)
-            if (s0 + c0 + c < S) x[c] = *(const f32x2*)(op + (int64_t)(s0 + c0 + c) * rows * kPDim);
+        for (int c = 0; c < 8; ++c) {
+          if (s0 + c < S) {
+            x[c] = *(const f32x2*)(op + (int64_t)(s0 + c) * rows * kPDim);
+            const float ls = lse[(int64_t)(s0 + c) * rows + r];
+            w[c] = (M == kNegInf || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
+          }
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          if (s0 + c0 + c < S) {
-            const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(c0 + c, 63)));
-            o = o + wc * x[c];
+          if (s0 + c < S) {
+            o = o + w[c] * x[c];
+            wsum += w[c];
           }
         }
       }
+      const bool none = M == kNegInf;
+      const float lse_r = none ? kNegInf : M + __builtin_amdgcn_logf(wsum) * kLn2;
+      float f = none ? 0.f : 1.0f / wsum;
+      if (a.sink != nullptr && !none) f = f / (1.0f + __builtin_amdgcn_exp2f((a.sink[h] - lse_r) * kLog2e));
+      o = o * f;
+      if (a.out_dtype == kPOutF32)
+        *(f32x2*)((float*)a.out + r * kPDim + 2 * lane) = o;
+      else
+        *(uint32_t*)((uint16_t*)a.out + r * kPDim + 2 * lane) = pack_bf16x2(o[0], o[1]);
+      if (lane == 0 && a.lse_out != nullptr) a.lse_out[r] = lse_r;
+      amax = fmaxf(amax, fmaxf(fabsf(o[0]), fabsf(o[1])));
     }
-    const float wsum = wave_sum(ws_own);
-    const bool none = M == kNegInf;
-    const float lse = none ? kNegInf : M + __builtin_amdgcn_logf(wsum) * kLn2;
-    float f = none ? 0.f : 1.0f / wsum;
-    if (a.sink != nullptr && !none) f = f / (1.0f + __builtin_amdgcn_exp2f((a.sink[h] - lse) * kLog2e));
-    o = o * f;
-    if (a.out_dtype == kPOutF32)
-      *(f32x2*)((float*)a.out + r * kPDim + 2 * lane) = o;
-    else
-      *(uint32_t*)((uint16_t*)a.out + r * kPDim + 2 * lane) = pack_bf16x2(o[0], o[1]);
-    if (lane == 0 && a.lse_out != nullptr) a.lse_out[r] = lse;
-    amax = fmaxf(fabsf(o[0]), fabsf(o[1]));
   }
   if (a.amax_out == nullptr) return;
   amax = wave_max(amax);
@@ -494,7 +496,8 @@ hipError_t launch_prefill(const PrefillArgs& a, bool split, hipStream_t stream) 
 
 hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.batch * a.sq_max * a.h_q;
-  hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(1024), 0, stream, a);
+  const int64_t per_wg = 16 * kPCombineRows;
+  hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((rows + per_wg - 1) / per_wg)), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
