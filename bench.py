@@ -738,8 +738,8 @@ def main():
         pmc_summary(args.pmc_summary)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
-              file=sys.stderr, flush=True)
+        print(f"bench.py measures one GPU only (the kernels and the launch plan are one GPU's); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr, flush=True)
         sys.exit(2)
     import torch
     import sparse_mla_decode_top_amd as smla
