@@ -72,11 +72,11 @@ constexpr int kPTile = kPKeys * kPDim;  // bytes of one K or V block in LDS
 constexpr float kPMasked = -3.0e38f;    // score of a masked key: its weight is exactly 0
 constexpr float kPNoFrame = 3.0e38f;    // frame of a row that has not seen a key yet
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kPStages = 3;
+constexpr int kPStages = 3;             // K/V blocks in LDS: one computed, up to two in flight (48 KB)
 // Rows a combine wave merges in turn: the workgroups (16 waves) then raise the
 // amax with 4x fewer atomics, which all land on one word (measured: with one
 // row a wave the amax atomics cost about 4 us of the chunked prefill's combine).
-constexpr int kPCombineRows = 4;             // K/V blocks in LDS: one computed, up to two in flight (48 KB: 3 workgroups a CU)
+constexpr int kPCombineRows = 4;
 
 enum { kPOutBf16 = 0, kPOutF32 = 1 };
 
