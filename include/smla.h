@@ -257,7 +257,9 @@ typedef struct {
  * Modes as sparse_mla_decode: no partials and split_kv == 1 is the direct path
  * (one kernel writes O, the sink and the amax fused in its epilogue); with
  * partials every split writes them and, if `out` is given, the combine runs;
- * split_kv > 1 without partials is SMLA_ERR_MISSING_WORKSPACE.
+ * split_kv > 1 without partials is SMLA_ERR_MISSING_WORKSPACE.  The score
+ * scale softmax_scale * descale_q * descale_k must be positive and at least
+ * 2^-100 (in float32, times log2 e), else SMLA_ERR_INVALID_ARG.
  */
 smla_status sdpa_fp8_prefill(const smla_prefill_params* p, const void* q, const void* k, const void* v,
                              const int32_t* seqlen_q, const int32_t* seqlen_kv, int32_t split_kv,

@@ -271,6 +271,9 @@ smla_status sdpa_fp8_prefill(const smla_prefill_params* p, const void* q, const 
   if (!isfinite(p->softmax_scale) || !isfinite(p->descale_q) || !isfinite(p->descale_k) ||
       !isfinite(p->descale_v))
     return SMLA_ERR_INVALID_ARG;
+  // the score scale in log2 units: the kernel needs it positive and not tiny
+  const float scale_log2 = p->softmax_scale * p->descale_q * p->descale_k * 1.4426950408889634f;
+  if (!(scale_log2 >= 0x1p-100f) || !isfinite(scale_log2)) return SMLA_ERR_INVALID_ARG;
   if (q == nullptr || k == nullptr || v == nullptr || seqlen_q == nullptr || seqlen_kv == nullptr)
     return SMLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return SMLA_ERR_MISALIGNED;
@@ -310,7 +313,7 @@ smla_status sdpa_fp8_prefill(const smla_prefill_params* p, const void* q, const 
   a.n_tiles = (int32_t)n_tiles;
   a.causal = p->causal;
   a.out_dtype = p->out_dtype;
-  a.scale_log2 = p->softmax_scale * p->descale_q * p->descale_k * 1.4426950408889634f;
+  a.scale_log2 = scale_log2;
   a.descale_v = p->descale_v;
   a.n_work = (int32_t)n_work;
   a.cus = device_cus();

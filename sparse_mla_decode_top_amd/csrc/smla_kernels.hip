@@ -40,11 +40,9 @@
 //     32-slot halves so that the softmax of one half is issued between the
 //     MFMAs of the other.
 //   * Softmax in log2 units against an integer frame M per head: each weight
-//     is p = 2^(t - floor t) * 2^(floor t - M).  Its bf16 rounding does not
-//     depend on M, so the partials of different split counts combine to the
-//     same value up to fp32 summation order.  M is the floor of the head's
-//     first non-empty half-block maximum and never moves inside a pass, so
-//     the accumulators are touched by MFMAs only (they stay in AGPRs).  A
+//     is p = 2^(t - M), one v_exp_f32.  M is the floor of the head's first
+//     non-empty half-block maximum and never moves inside a pass, so the
+//     accumulators are touched by MFMAs only (they stay in AGPRs).  A
 //     later score above M + 64 would risk overflow: the job then runs once
 //     more with M = floor of the largest score seen, which bounds every p by
 //     2.  The denominator sums the unrounded fp32 weights.
@@ -91,8 +89,8 @@ constexpr int kTileBytes = kBlk * 1152;          // 64 bf16 rows of 576
 constexpr int kCodeTileBytes = kBlk * 576;       // 64 e4m3 rows of 576
 constexpr int kQOffset = kTileBytes;             // LDS byte offset of the staged Q rows
 constexpr float kFrameSlack = 64.0f;     // scores may exceed a head's frame M by this much
-// Score of a masked slot: finite, so that the branch-free weight below gives
-// exactly 0 for it (floor and fraction stay defined), and below any real score.
+// Score of a masked slot: finite and below any real score; its weight
+// 2^(t - M) is exactly 0 for every frame.
 constexpr float kMaskedScore = -3.0e38f;
 // Frame of a head that has not seen a valid slot yet: every weight is then 0.
 constexpr float kNoFrame = 3.0e38f;
@@ -614,8 +612,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
       // Softmax of half hh in 15 steps (called with constant hh and k):
       //   0: scores (log2 units, masked slots at kMaskedScore)   1-2: head max, frame
-      //   3-10: one weight each (2^(t - floor t) * 2^(floor t - M), p = 0 for a
-      //   masked slot or a head without a frame)   11-14: one bf16 hi/lo pair each.
+      //   3-10: one weight each (2^(t - M), p = 0 for a masked slot or a head
+      //   without a frame)   11-14: one bf16 hi/lo pair each.
       float tv[2][8], pv[2][8], mh[2];
       uint32_t ph[2][4], pl[2][4];
       auto sm_step = [&](const int hh, const int k) __attribute__((always_inline)) {
@@ -640,9 +638,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         } else if (k <= 10) {
           const int e = k - 3;
           const float tt = tv[hh][e];
-          const float fl = floorf(tt);
-          const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
-          float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+          float p = __builtin_amdgcn_exp2f(tt - M_run);
           l_run += p;
           if (KV_FP8) p *= rsc[2 * hh + (e >> 2)][e & 3];
           pv[hh][e] = p;
@@ -1081,9 +1077,7 @@ __device__ __forceinline__ void decode8p_body(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float tt = tv[e];
-        const float fl = floorf(tt);
-        const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
-        const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+        const float p = __builtin_amdgcn_exp2f(tt - M_run);
         l_run += p;
         pv[e] = p;
       }
@@ -1489,9 +1483,7 @@ __device__ __forceinline__ void decode8h_body(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float tt = tv[e];
-        const float fl = floorf(tt);
-        const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
-        float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+        float p = __builtin_amdgcn_exp2f(tt - M_run);
         l_run += p;
         if (KV_FP8) p *= rsc[e];
         pv[e] = p;
@@ -1931,9 +1923,7 @@ __device__ __forceinline__ void decode4t_body(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float tt = tv[e];
-        const float fl = floorf(tt);
-        const float ex = __builtin_amdgcn_fmed3f(fl - M_run, -256.f, 256.f);
-        float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(tt - fl), (int)ex);
+        float p = __builtin_amdgcn_exp2f(tt - M_run);
         l_run += p;
         if (KV_FP8) p *= rsc[e];
         pv[e] = p;

@@ -254,27 +254,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       bf16x8 ph[HPW][2], pl[HPW][2];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        // (The empty volatile statements keep both branches as uniform jumps: the
+        // The row maximum is taken on the raw scores: the scale is positive (the
+        // host rejects any other), so the largest scaled score is the scale times
+        // the largest raw one, and each weight takes one fma for its exponent.
+        // (The empty volatile statements keep the branches as uniform jumps: the
         // compiler would otherwise evaluate both sides and select.)
-        float tv[16];
+        const float c = a.scale_log2;
+        float sv[16];
         if (full) {
           asm volatile("");
 #pragma unroll
-          for (int k = 0; k < 16; ++k) tv[k] = sacc[hh][k >> 2][k & 3] * a.scale_log2;
+          for (int k = 0; k < 16; ++k) sv[k] = sacc[hh][k >> 2][k & 3];
         } else {
           asm volatile("");
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
             const int key = kb * kPKeys + 16 * (k >> 2) + 4 * G + (k & 3);
-            tv[k] = key < vis ? sacc[hh][k >> 2][k & 3] * a.scale_log2 : kPMasked;
+            sv[k] = key < vis ? sacc[hh][k >> 2][k & 3] : kPMasked;
           }
         }
-        float m = kPMasked;
+        float mr = kPMasked;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) m = fmaxf(m, tv[k]);
-        m = rows_max(m);                                 // the four lanes of row i
-        const bool any = m > kPMasked;
-        const float fm = floorf(m);
+        for (int k = 0; k < 16; ++k) mr = fmaxf(mr, sv[k]);
+        mr = rows_max(mr);                               // the four lanes of row i
+        const bool any = mr > kPMasked;
+        const float fm = floorf(mr * c);
         const float M_new = !any ? M[hh] : (M[hh] == kPNoFrame ? fm : fmaxf(M[hh], fm));
         const bool moved = any && M[hh] != kPNoFrame && M_new != M[hh];
         if (__builtin_amdgcn_ballot_w64(moved) != 0) {   // a row took a new frame: rescale by an exact power of two
@@ -286,18 +290,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           for (int mt = 0; mt < 8; ++mt) acc[hh][mt] = acc[hh][mt] * f;
         }
         M[hh] = M_new;
-        // p = 2^(t - floor t) * 2^(floor t - M), with the integer parts as saturating
-        // int32: a masked key (t = -3e38) and a row with no frame yet (M = 3e38)
-        // both give an exponent of -2^31, so p = 0.  Exact for |t| < 2^31.
-        int Mi;
-        asm("v_cvt_i32_f32 %0, %1" : "=v"(Mi) : "v"(M_new));
+        // p = 2^(s c - M) < 2.  A masked key (s = -3e38) gets p = 0, since the host
+        // keeps the scale at 2^-100 or more, and so does every key of a row with
+        // no frame yet (M = 3e38).
+        const float nM = -M_new;
         float pv[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          int fi;
-          asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(fi) : "v"(tv[k]));
-          const int ex = __builtin_elementwise_sub_sat(fi, Mi);
-          const float p = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(tv[k])), ex);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sv[k], c, nM));
           l_run[hh] += p;
           pv[k] = p;
         }

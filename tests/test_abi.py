@@ -180,6 +180,25 @@ def test_decode_rejects_before_launch():
     assert st == UNSUPPORTED
 
 
+@pytest.mark.parametrize("scale,dq,dk,expect", [
+    (0.0, 1.0, 1.0, INVALID),              # the score scale must be positive
+    (-0.088, 1.0, 1.0, INVALID),
+    (0.088, -1.0, 1.0, INVALID),
+    (1e-20, 1e-20, 1.0, INVALID),          # 1e-40: below 2^-100
+    (float("inf"), 1.0, 1.0, INVALID),
+    (0.088, 1.0, float("nan"), INVALID),
+    (0.088, -1.0, -1.0, OK),               # a positive product is accepted
+])
+def test_prefill_score_scale_checked_before_launch(scale, dq, dk, expect):
+    """sdpa_fp8_prefill rejects a score scale softmax_scale * descale_q * descale_k that is not
+    positive and at least 2^-100 before anything touches the GPU.  An accepted scale is shown with
+    split_kv = 2 and no partials, which the next check rejects, still before any launch."""
+    lib = B.load_library()
+    p = B.make_prefill_params(1, 8, 8, 64, 64, scale, dq, dk)
+    st = lib.sdpa_fp8_prefill(ctypes.byref(p), A, A, A, A, A, 2, None, None, None, A, None, None, None)
+    assert st == (MISSING_WS if expect == OK else expect)
+
+
 def test_noalloc_rejects_before_launch():
     """sparse_mla_decode_noalloc: a missing output, a bad shape and partials larger than
     its scratch come back as status codes before anything touches the GPU."""
