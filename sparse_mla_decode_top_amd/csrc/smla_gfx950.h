@@ -1,6 +1,7 @@
 // gfx950 (CDNA4) device primitives shared by the library's kernels: vector
 // types, direct-to-LDS loads, LDS barriers, wave reductions on DPP and the row
-// swaps, bf16 packing and exact e4m3 -> bf16 conversion.  Device code only.
+// swaps, bf16 and f16 packing and exact e4m3 -> bf16 / f16 conversion.  Device
+// code only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,6 +15,7 @@ typedef float f32x4 __attribute__((__vector_size__(16)));
 typedef float f32x2 __attribute__((__vector_size__(8)));
 typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+typedef _Float16 f16x8 __attribute__((__vector_size__(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -104,6 +106,24 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
   o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false));
   o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true));
   return __builtin_bit_cast(bf16x8, o);
+}
+
+// Eight e4m3fn codes as f16 (exact for every code: e4m3 values are f16 values).
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(u32x2 w) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true));
+  return __builtin_bit_cast(f16x8, o);
+}
+
+// Two floats as packed f16 (round to nearest even), `lo` in the low half: one
+// v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, f16x2v));
 }
 
 // Two floats as packed bf16 (round to nearest even), `lo` in the low half: one

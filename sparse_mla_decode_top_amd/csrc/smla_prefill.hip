@@ -30,17 +30,21 @@
 //     a row that sees one key is that key's score), twice the 1e-5 LSE bar; the
 //     bf16 form measured 7e-7 on the same inputs.
 //   * Softmax in log2 units against an integer frame M per row (the running
-//     floor of the row maximum): p = 2^(t - floor t) * 2^(floor t - M).  The
-//     bf16 rounding of 2^(t - floor t) does not depend on M, and a frame change
-//     rescales the accumulators by an exact power of two, so partials of any
-//     split count combine to the same value up to f32 summation order.
-//   * O^T[dim][row] += V^T . P^T on the bf16 matrix core, P as two bf16 terms
-//     (hi = bf16(p), lo = bf16(p - hi)).  V^T fragments come from the 8-bit
-//     transposing LDS read ds_read_b64_tr_b8 of the e4m3 V tile, converted to
-//     bf16 in registers (exact).  The P^T fragment is the lane's own scores:
-//     its k-elements are keys 4G .. 4G + 3 of one 16-key tile and 4G .. 4G + 3
-//     of the next, and the V^T reads fetch the same keys in the same order.
-//   * Epilogue: O = acc * descale_v / l, LSE = (M + log2 l) * ln 2.  Split:
+//     floor of the row maximum): the weight is p = 2^(t - M + 14), one fma and
+//     one v_exp_f32, so p < 2^15.  A frame change rescales the accumulators by
+//     an exact power of two.
+//   * O^T[dim][row] += V^T . P^T on the f16 matrix core, P as one f16 term.
+//     V^T fragments come from the 8-bit transposing LDS read ds_read_b64_tr_b8
+//     of the e4m3 V tile, converted to f16 in registers (exact: every e4m3
+//     value is an f16 value).  f16 keeps p to 2^-12 relative, which holds O
+//     within about 1e-3 of the exact result for values of the inputs' size
+//     (one bf16 term, 2^-9, does not: rows that see few keys reach 7e-3).  The
+//     2^14 keeps every weight above 2^-28 of its row's largest out of f16's
+//     subnormals, where the rounding would depend on the frame and so on the
+//     split count.  The P^T fragment is the lane's own scores: its k-elements
+//     are keys 4G .. 4G + 3 of one 16-key tile and 4G .. 4G + 3 of the next,
+//     and the V^T reads fetch the same keys in the same order.
+//   * Epilogue: O = acc * descale_v / l, LSE = (M - 14 + log2 l) * ln 2.  Split:
 //     the partial and its LSE.  Direct: the sink, the cast, the LSE and the
 //     amax (one atomic max per wave on the bits of |O|, a non-negative float).
 //
@@ -68,6 +72,9 @@ namespace {
 constexpr int kPRows = 64;              // query rows per tile: 4 waves x 16
 constexpr int kPKeys = 64;              // keys per KV block
 constexpr int kPDim = 128;              // head dimension (bytes per e4m3 row)
+// Weights are taken as 2^(t - M + kPWeightShift): below 2^15 for f16, and
+// out of its subnormals down to 2^-28 of the row's largest weight.
+constexpr float kPWeightShift = 14.0f;
 constexpr int kPTile = kPKeys * kPDim;  // bytes of one K or V block in LDS
 constexpr float kPMasked = -3.0e38f;    // score of a masked key: its weight is exactly 0
 constexpr float kPNoFrame = 3.0e38f;    // frame of a row that has not seen a key yet
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
       // ---- softmax per head: lane scores of row i, keys kb*64 + 16t + 4G + e
       const bool full = kb * kPKeys + kPKeys <= vis_lo;   // every key of the block visible to every row (uniform)
-      bf16x8 ph[HPW][2], pl[HPW][2];
+      f16x8 ph[HPW][2];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
         // The row maximum is taken on the raw scores: the scale is positive (the
@@ -290,10 +297,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           for (int mt = 0; mt < 8; ++mt) acc[hh][mt] = acc[hh][mt] * f;
         }
         M[hh] = M_new;
-        // p = 2^(s c - M) < 2.  A masked key (s = -3e38) gets p = 0, since the host
-        // keeps the scale at 2^-100 or more, and so does every key of a row with
-        // no frame yet (M = 3e38).
-        const float nM = -M_new;
+        // p = 2^(s c - M + kPWeightShift) < 2^15.  A masked key (s = -3e38) gets
+        // p = 0, since the host keeps the scale at 2^-100 or more, and so does
+        // every key of a row with no frame yet (M = 3e38).
+        const float nM = kPWeightShift - M_new;
         float pv[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -301,24 +308,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           l_run[hh] += p;
           pv[k] = p;
         }
-        // P^T fragments of k-step kk: keys 4G .. +3 of tiles 2kk and 2kk + 1, hi and lo terms
+        // P^T fragments of k-step kk: keys 4G .. +3 of tiles 2kk and 2kk + 1, in f16
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          u32x4 h4, l4;
+          u32x4 h4;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float x0 = pv[8 * kk + 2 * q], x1 = pv[8 * kk + 2 * q + 1];
-            const uint32_t h2 = pack_bf16x2(x0, x1);
-            h4[q] = h2;
-            l4[q] = pack_bf16x2(x0 - __uint_as_float(h2 << 16), x1 - __uint_as_float(h2 & 0xFFFF0000u));
-          }
-          ph[hh][kk] = __builtin_bit_cast(bf16x8, h4);
-          pl[hh][kk] = __builtin_bit_cast(bf16x8, l4);
+          for (int q = 0; q < 4; ++q) h4[q] = pack_f16x2(pv[8 * kk + 2 * q], pv[8 * kk + 2 * q + 1]);
+          ph[hh][kk] = __builtin_bit_cast(f16x8, h4);
         }
       }
 
       // ---- O^T += V^T . P^T: eight dim tiles of 16, two k-steps of 32 keys; one
-      // converted V^T fragment feeds every head of the wave, hi and lo terms
+      // converted V^T fragment feeds every head of the wave
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -327,12 +328,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           const uint32_t addr = vt + vrow[kk] + ((mt ^ vsw[kk]) * 16);
           const i32x2v r =
               __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2v*)(uintptr_t)addr);
-          const bf16x8 vf = e4m3x8_to_bf16(u32x2{(uint32_t)r[0], (uint32_t)r[1]});
+          const f16x8 vf = e4m3x8_to_f16(u32x2{(uint32_t)r[0], (uint32_t)r[1]});
 #pragma unroll
-          for (int hh = 0; hh < HPW; ++hh) {
-            acc[hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[hh][kk], acc[hh][mt], 0, 0, 0);
-            acc[hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[hh][kk], acc[hh][mt], 0, 0, 0);
-          }
+          for (int hh = 0; hh < HPW; ++hh)
+            acc[hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[hh][kk], acc[hh][mt], 0, 0, 0);
         }
       }
     }
@@ -345,7 +344,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int h = w.h + hh;
     const float l = rows_sum(l_run[hh]);
     const bool has = l > 0.f;
-    const float lse = has ? (M[hh] + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
+    const float lse = has ? (M[hh] - kPWeightShift + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
     float oscale = has ? a.descale_v / l : 0.f;
     if (!SPLIT && a.sink != nullptr && has)
       oscale = oscale / (1.0f + __builtin_amdgcn_exp2f((a.sink[h] - lse) * kLog2e));
