@@ -598,8 +598,8 @@ def hbm_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
 def pmc_summary(dirs):
     """Per kernel and counter: the mean over dispatches of the counter summed (and maxed)
     over its hardware instances.  For the attention kernel also: the MFMA busy share
-    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) and the executed bf16 MFMA flops
-    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) and the executed bf16 and f16 MFMA
+    flops SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F16 x 512."""
     per = {}                       # (kernel, counter) -> {dispatch: [values]}
     for d in dirs:
         for r in _csv_rows(d, "counter_collection.csv"):
@@ -618,12 +618,15 @@ def pmc_summary(dirs):
         busy = stats.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"))
         active = stats.get((k, "GRBM_GUI_ACTIVE"))
         mops = stats.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+        mops16 = stats.get((k, "SQ_INSTS_VALU_MFMA_MOPS_F16"))
         if busy and active:
             cyc = active[0] / 8
             print(f"{k[:56]}: MFMA busy {busy[0]:.0f} SIMD-cycles over {cyc:.0f} active cycles x 1024 SIMDs "
                   f"= {100.0 * busy[0] / (cyc * 1024):.1f}%")
         if mops:
             print(f"{k[:56]}: executed bf16 MFMA flops per dispatch {mops[0] * 512:.4g}")
+        if mops16:
+            print(f"{k[:56]}: executed f16 MFMA flops per dispatch {mops16[0] * 512:.4g}")
 
 
 def kernel_label(s_q, S, pool, cus=256):
