@@ -546,6 +546,8 @@ def summarize_kernel_stats(directory):
         print(f"{k[:64]:64s} {nb:7d} {nc:6d} {ns / nc / 1e3:9.3f}")
     for label, calls, us in per_call:
         print(f"batch of {calls} calls ({label}): kernel time per call {us:.3f} us")
+    if not per_call:
+        print("(none: no batch repeats a call 20 times; the averages above are over all calls)")
 
 
 def _counter_per_dispatch(directory, counter):
