@@ -200,3 +200,47 @@ def test_prefill_workload_sampled_rows(name):
             O_r = O_r / (1.0 + np.exp(float(inp.sink[h]) - L_r))[:, None]
             H.assert_o_close(res["O"][b, rows, h], O_r, rel=2.0 ** -8)
             H.assert_lse_close(res["lse"][b, rows, h], L_r)
+
+
+@pytest.mark.parametrize("S,path", [(3, "split"), (1, "direct")])
+def test_prefill_graph_capture_replays_match_eager(S, path):
+    """sdpa_fp8_prefill captured into a HIP graph (split: attention + combine; direct: the
+    amax reset + attention): every replay, with eager work in between, equals the eager
+    call bit for bit, the amax included."""
+    import sparse_mla_decode_top_amd as smla
+    dev = dev_for("gqa8_long")
+    inp = dev.inp
+    B, sq, hq = inp.batch, inp.sq_max, inp.h_q
+    o_part = lse_part = None
+    if path == "split":
+        o_part = torch.empty((S, B, sq, hq, 128), device="cuda")
+        lse_part = torch.empty((S, B, sq, hq), device="cuda")
+    out = torch.empty((B, sq, hq, 128), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((B, sq, hq), device="cuda")
+    amax = torch.empty((1,), device="cuda")
+
+    def step():
+        smla.sdpa_fp8_prefill(dev.q, dev.k, dev.v, dev.sq, dev.skv, S, inp.scale, inp.descale_q, inp.descale_k,
+                              inp.descale_v, causal=inp.causal, sink=dev.sink, o_part=o_part, lse_part=lse_part,
+                              out=out, lse_out=lse, amax_out=amax)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), amax.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        lse.zero_()
+        amax.fill_(1e30)                 # a stale larger value: the replay must reset it
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]) and torch.equal(amax, ref[2])
