@@ -633,18 +633,18 @@ def pmc_summary(dirs):
 
 def kernel_label(s_q, S, pool, cus=256):
     """Which attention kernel(s) a launch runs (mirrors sparse_mla_decode's choice for 64
-    heads): with a bf16 pool the head-tile kernels at 2, 4 or 8 parts, else the 8-wave
-    kernel's column parts; with one part,
+    heads): the head-tile kernel at 4, 8 or 16 parts, the head-half kernel at 2; with one part,
     the paired 8-wave kernel (bf16 pool) or the 4-wave kernel (FP8 pool); a last round
     that would fill at most half of the CUs takes more column parts, in the same launch
     (bf16 pool: the mixed kernel) or a second one."""
     jobs = s_q * S
-    cs = 8 if 8 * jobs <= cus else 4 if 4 * jobs <= cus else 2 if 2 * jobs <= cus else 1
+    cs = 16 if 16 * jobs <= cus else 8 if 8 * jobs <= cus else 4 if 4 * jobs <= cus else 2 if 2 * jobs <= cus else 1
     mode = "partial" if S > 1 else "direct"
 
     def one(c):
-        if c in (4, 8):
-            return f"decode_kernel4t<{pool} pool, {mode}, {c} parts: head tiles{' x column halves' if c == 8 else ''}>"
+        if c in (4, 8, 16):
+            cols = {4: "", 8: " x column halves", 16: " x column quarters"}[c]
+            return f"decode_kernel4t<{pool} pool, {mode}, {c} parts: head tiles{cols}>"
         if c == 2:
             return f"decode_kernel8h<{pool} pool, {mode}, 2 head halves>"
         name = "decode_kernel8p" if pool == "bf16" else "decode_kernel"
@@ -654,9 +654,8 @@ def kernel_label(s_q, S, pool, cus=256):
     if cs == 1 and jobs > cus and 0 < tail and 2 * tail <= cus:
         ct = 8 if 8 * tail <= cus else 4 if 4 * tail <= cus else 2
         if pool == "bf16" and (jobs - tail) % 8 == 0:
-            tail_body = "decode_kernel8h's in 2 head halves" if ct == 2 else f"decode8_body in {ct} column parts"
             return (f"decode_kernel8m<bf16 pool, {mode}: decode_kernel8p's body over {jobs - tail} jobs, "
-                    f"{tail_body} over the last {tail}>")
+                    f"decode_kernel8h's in 2 head halves over the last {tail}>")
         return f"{one(1)} over {jobs - tail} jobs + {one(ct)} over the last {tail}"
     return one(cs)
 

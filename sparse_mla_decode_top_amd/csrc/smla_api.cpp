@@ -200,6 +200,7 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   const int64_t jobs = (int64_t)p->s_q * (direct ? 1 : num_splits);
   const int32_t cus = device_cus();
   a.col_parts = (direct && p->out_dtype == SMLA_OUT_FP8_E4M3) ? 1
+                : p->h_q == 64 && 16 * jobs <= cus               ? 16
                 : 8 * jobs <= cus                                ? 8
                 : 4 * jobs <= cus                                ? 4
                 : 2 * jobs <= cus                                ? 2

@@ -1643,7 +1643,7 @@ template <bool KV_FP8, bool DIRECT, bool PREFETCH, int CP>
 __device__ __forceinline__ void decode4t_body(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, const DecodeArgs& a, int block, uint8_t* smem) {
-  static_assert(CP == 1 || CP == 2, "one head tile takes 1 or 2 column parts");
+  static_assert(CP == 1 || CP == 2 || CP == 4, "one head tile takes 1, 2 or 4 column parts");
   constexpr int kCols = 512 / CP;                 // columns of the workgroup
   constexpr int kWCols = kCols / 4;               // columns of a wave
   constexpr int kCt = kWCols / 16;                // column tiles of 16 owned by a wave
@@ -1721,9 +1721,17 @@ __device__ __forceinline__ void decode4t_body(
     const Fp8Offsets f8 = fp8_offsets(lane);                  // FP8 pool: K and V^T reads of the codes
     const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
     const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
-    int vb[4];                                                  // column tile ct & 3
+    const int vrow8 = f8.v[0] - G * 16;                         // FP8: the lane's V^T row offset
+    // The wave's first column tile within its 64-column segment: 0, or 2 for the
+    // odd waves when a wave owns 32 columns (four column parts).
+    const int c0 = kWCols < 64 ? ((kWCols / 16) * wave) & 3 : 0;
+    int vb[4], vb8[4];                                          // the wave's column tile ct & 3
 #pragma unroll
-    for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
+    for (int m = 0; m < 4; ++m) {
+      const int cm = (c0 + m) & 3;
+      vb[m] = vrow + (((2 * cm + ((lane & 3) >> 1)) ^ sw_v) * 16);
+      vb8[m] = vrow8 + ((cm ^ G) * 16);
+    }
 
     // ---- prologue: the head tile's 16 Q rows into LDS at kQOffset; wave w
     // stages rows [8 (w & 1), +8) (waves 2-3 repeat waves 0-1's rows, same
@@ -1847,9 +1855,9 @@ __device__ __forceinline__ void decode4t_body(
         kbase[0] = opaque(tl + f8.k[0]);
         kbase[1] = opaque(tl + f8.k[1]);
         kbase[2] = kbase[3] = 0u;
-        const uint32_t tlv = tl + ((kCols * cpart + kWCols * wave) / 64) * 4096;     // this wave's columns start at column tile (kCols cpart + kWCols wave) / 16
+        const uint32_t tlv = tl + ((kCols * cpart + kWCols * wave) / 64) * 4096;     // the 64-column segment of the wave's first column
 #pragma unroll
-        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + f8.v[m]);
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + vb8[m]);
       } else {
         kbase[0] = opaque(tl + kb0);
         kbase[1] = opaque(tl + kb1);
@@ -2399,20 +2407,25 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
                        a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
     return hipGetLastError();
   }
-  // 64 heads in 4 or 8 parts: one head tile per 4-wave workgroup (8 parts:
-  // and half its columns), none repeating another tile's QK^T.
-  if (a.h_q == 64 && (cs == 4 || cs == 8)) {
+  // 64 heads in 4, 8 or 16 parts: one head tile per 4-wave workgroup (8 and 16
+  // parts: and a half or a quarter of its columns), none repeating another
+  // tile's QK^T.
+  if (a.h_q == 64 && (cs == 4 || cs == 8 || cs == 16)) {
 #define SMLA_LAUNCH_4T(FP8, CPV)                                                                             \
   hipLaunchKernelGGL((decode_kernel4t<FP8, DIRECT, PREFETCH, CPV>), grid, dim3(kThreads), 0, stream, a.indices, \
                      a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a)
     if (kv_fp8 && cs == 4)
       SMLA_LAUNCH_4T(true, 1);
-    else if (kv_fp8)
+    else if (kv_fp8 && cs == 8)
       SMLA_LAUNCH_4T(true, 2);
+    else if (kv_fp8)
+      SMLA_LAUNCH_4T(true, 4);
     else if (cs == 4)
       SMLA_LAUNCH_4T(false, 1);
-    else
+    else if (cs == 8)
       SMLA_LAUNCH_4T(false, 2);
+    else
+      SMLA_LAUNCH_4T(false, 4);
 #undef SMLA_LAUNCH_4T
     return hipGetLastError();
   }
