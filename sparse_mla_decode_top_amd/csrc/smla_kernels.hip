@@ -10,15 +10,15 @@
 // Kernels, by launch (64 heads unless stated; CS = workgroups a job takes):
 //   * decode_kernel8p (CS = 1, bf16 pool): 8 waves, all heads and columns.
 //   * decode_kernel8h (CS = 2): 8 waves, half of the heads each.
-//   * decode_kernel4t (CS = 4 or 8): 4 waves, one 16-head tile each (CS = 8:
-//     and half its columns).
+//   * decode_kernel4t (CS = 4, 8 or 16): 4 waves, one 16-head tile each (CS =
+//     8 or 16: and a half or a quarter of its columns).  The head-part kernels
+//     repeat a head tile's QK^T only across its column parts.
 //   * decode_kernel8m: a mixed launch for more jobs than compute units
 //     (decode_kernel8p's body, then decode_kernel8h's for a short last round).
 //   * decode_kernel (fewer heads, or CS = 1 with an FP8 pool or a direct FP8
 //     output): 4 waves, each workgroup 512 / CS output columns of all heads.
-// The head-part kernels let no workgroup repeat another's QK^T.  The notes
-// below describe decode_kernel; the others share its tile layout, gather,
-// softmax frame and partial protocol.
+// The notes below describe decode_kernel; the others share its tile layout,
+// gather, softmax frame and partial protocol.
 //
 // decode kernel: CS in {1, 2, 4, 8} workgroups of 4 wave64s per (token,
 // split) job, each owning 512 / CS output columns (all of them compute the
