@@ -62,6 +62,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "smla.h"
 #include "smla_gfx950.h"
 #include "smla_internal.h"
@@ -219,20 +221,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // tile mt): lane j reads half j & 1 of key 32 kk + 16 (j >> 3) + 4G +
     // ((j >> 1) & 3), chunk mt.
     const int vr0 = 16 * (j >> 3) + 4 * G + ((j >> 1) & 3);
-    int vrow[2], vsw[2];
+    // V^T read offsets of the 16 (k-step, dim tile) fragments, one register each
+    // (opaque, so that the compiler keeps them whole instead of re-adding a row
+    // and a chunk part at every read); the stage goes in as an immediate.
+    uint32_t voff[2][8];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      vrow[kk] = (32 * kk + vr0) * kPDim + (j & 1) * 8;
-      vsw[kk] = kvsw(32 * kk + vr0);
-    }
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        voff[kk][mt] = opaque((32 * kk + vr0) * kPDim + (j & 1) * 8 + ((mt ^ kvsw(32 * kk + vr0)) * 16));
 
     // Blocks b0 .. b0 + STAGES - 2 go out first; each iteration then waits for
     // its own block only and refills the stage the previous block used.
 #pragma unroll
     for (int pb = 0; pb < STAGES - 1; ++pb)
       if (b0 + pb < b1) gather(b0 + pb, pb);
-    for (int kb = b0; kb < b1; ++kb) {
-      const int st = (kb - b0) % STAGES;
+    // One block of keys.  Its stage is a compile-time constant (the loop below is
+    // unrolled over the stages), so every LDS operand address is a loop-invariant
+    // lane offset plus an instruction immediate, with no add of a stage base.
+    auto block = [&](const int kb, auto stage) __attribute__((always_inline)) {
+      constexpr int st = decltype(stage)::value;
       wait_block<STAGES>(min(STAGES - 2, b1 - 1 - kb));   // this wave's share of block kb has landed
       lds_barrier();            // ... and every wave's; block kb - 1 fully read
       if (kb + STAGES - 1 < b1) gather(kb + STAGES - 1, (st + STAGES - 1) % STAGES);
@@ -274,11 +282,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           for (int k = 0; k < 16; ++k) sv[k] = sacc[hh][k >> 2][k & 3];
         } else {
           asm volatile("");
+          // key kb*64 + 16(k >> 2) + 4G + (k & 3) is visible iff its offset in the
+          // lane's keys, 16(k >> 2) + (k & 3), is below lim: compares with constants
+          const int lim = vis - kb * kPKeys - 4 * G;
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const int key = kb * kPKeys + 16 * (k >> 2) + 4 * G + (k & 3);
-            sv[k] = key < vis ? sacc[hh][k >> 2][k & 3] : kPMasked;
-          }
+          for (int k = 0; k < 16; ++k) sv[k] = 16 * (k >> 2) + (k & 3) < lim ? sacc[hh][k >> 2][k & 3] : kPMasked;
         }
         float mr = kPMasked;
 #pragma unroll
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           typedef int i32x2v __attribute__((ext_vector_type(2)));
-          const uint32_t addr = vt + vrow[kk] + ((mt ^ vsw[kk]) * 16);
+          const uint32_t addr = vt + voff[kk][mt];
           const i32x2v r =
               __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2v*)(uintptr_t)addr);
           const f16x8 vf = e4m3x8_to_f16(u32x2{(uint32_t)r[0], (uint32_t)r[1]});
@@ -334,6 +342,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             acc[hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[hh][kk], acc[hh][mt], 0, 0, 0);
         }
       }
+    };
+    for (int kb = b0; kb < b1; kb += STAGES) {
+      block(kb, std::integral_constant<int, 0>{});
+      if (kb + 1 < b1) block(kb + 1, std::integral_constant<int, 1 % STAGES>{});
+      if (STAGES > 2 && kb + 2 < b1) block(kb + 2, std::integral_constant<int, 2 % STAGES>{});
+      if (STAGES > 3 && kb + 3 < b1) block(kb + 3, std::integral_constant<int, 3 % STAGES>{});
     }
   }
 
