@@ -3,10 +3,10 @@
 
 A step is one pass of the whole hot path over one batch: the attention kernel
 over every (token, split) job plus the combine, on inputs already resident in
-HBM.  Steps are replayed from a HIP graph (the pages time their kernels under
-CUDA graphs) and cycle through L distinct "layers" -- independent pools,
-queries and index lists whose pools together exceed the 256 MB last-level
-cache.  At small s_q the rows that all layers gather (0.74 MB per token and
+HBM.  Steps are replayed from HIP graphs of 64 steps (the pages time their
+kernels under CUDA graphs) and cycle through L distinct "layers" --
+independent pools, queries and index lists whose pools together exceed the
+256 MB last-level cache.  At small s_q the rows that all layers gather (0.74 MB per token and
 layer) still fit in that cache and stay there across replays, so the graph
 figure is a warm-cache one there; at s_q = 384 the gathered rows exceed it.
 cold_us_per_step repeats the step with every cache flushed before it (a 1 GiB
@@ -144,12 +144,18 @@ def build_layers(s_q, n_pool, torch, W, seed0=1000, dtype="bf16"):
     return [Layer(s_q, n_pool, seed0 + i, torch, W, dtype) for i in range(n_layers)]
 
 
+GRAPH_STEPS = 64   # steps captured per graph: about the attention calls of one forward of a ~60-layer model
+
+
 def time_steps(layers, S, steps, warmup, torch, smla):
     """Step time from graph replays, exactly `warmup` untimed then `steps` timed steps.
 
-    One graph holds one step of every layer in turn and is replayed whole; a step count
-    that is not a multiple of the layer count ends with the one-step graphs of the first
-    layers.  Returns (wall us/step, event us/step, steps, warmup)."""
+    Step i of a run calls layer i mod L.  The steps are captured in graphs of GRAPH_STEPS
+    steps (rounded up to whole cycles over the layers), plus one graph that holds the
+    remainder of each run.  Launching a graph costs about 5 us of GPU time on this
+    machine whatever its size; a model's decode graph spreads that over its ~60 layers,
+    and so do graphs of this size (one cycle of 8 layers per graph would add about
+    0.7 us to every step).  Returns (wall us/step, event us/step, steps, warmup)."""
     s_q = layers[0].inp.s_q
     scale = layers[0].inp.scale
     o_acc = torch.empty((S, s_q, 64, 512), device="cuda") if S > 1 else None
@@ -169,24 +175,25 @@ def time_steps(layers, S, steps, warmup, torch, smla):
             step(L)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all):
-        for L in layers:
-            step(L)
-    g_one = []
-    for L in layers:
+    n = len(layers)
+    per = n * max(1, -(-GRAPH_STEPS // n))
+
+    def capture(k):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(L)
-        g_one.append(g)
-    n = len(layers)
+            for i in range(k):
+                step(layers[i % n])
+        return g
+
+    g_full = capture(per)
+    g_rem = {r: capture(r) for r in {warmup % per, steps % per} if r}
 
     def replay(k):
-        full, rem = divmod(k, n)
+        full, rem = divmod(k, per)
         for _ in range(full):
-            g_all.replay()
-        for i in range(rem):
-            g_one[i].replay()
+            g_full.replay()
+        if rem:
+            g_rem[rem].replay()
 
     replay(warmup)
     torch.cuda.synchronize()
@@ -279,7 +286,10 @@ def kernel_durations(layers, S, reps, torch, smla):
     """Mean duration (us) of the attention kernel and of the combine, from HIP events on
     the stream they are launched on.  Each figure is a batch of `reps` back-to-back calls
     bracketed by one event pair; a GPU sleep queued first keeps the stream backed up so
-    the launches run without host gaps.  The attention kernel is timed alone (partial-only
+    the launches run without host gaps, and `reps` untimed calls run between the sleep
+    and the batch, so that it is timed at the clock the GPU holds under sustained load
+    (for the first millisecond or so after idling it runs faster: at s_q = 384 a kernel
+    takes about 71 us there and 80-85 us once the load has lasted).  The attention kernel is timed alone (partial-only
     calls); the combine as the difference between whole steps and partial-only calls, so
     it is the combine the step runs (an FP8 output's included: its counters are seeded by
     the attention kernel).  S == 1 times the direct path (one kernel per step)."""
@@ -291,9 +301,11 @@ def kernel_durations(layers, S, reps, torch, smla):
 
     def batch(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cyc = sleep_cycles_for(5 + reps * 0.1, torch)
+        cyc = sleep_cycles_for(5 + reps * 0.2, torch)
         torch.cuda.synchronize()
         torch.cuda._sleep(cyc)
+        for i in range(reps):             # sustained load before the timed calls
+            fn(layers[i % len(layers)])
         e0.record(stream)
         for i in range(reps):
             fn(layers[i % len(layers)])
@@ -430,26 +442,41 @@ def measure_prefill(name, steps, warmup, reps, torch, smla, W):
         step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(warmup):
-        g.replay()
+    per = GRAPH_STEPS // 4            # steps a graph (the graph launch cost spread as in time_steps)
+
+    def capture(k):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(k):
+                step()
+        return g
+
+    g_full = capture(per)
+    g_rem = {r: capture(r) for r in {warmup % per, steps % per} if r}
+
+    def replay(k):
+        for _ in range(k // per):
+            g_full.replay()
+        if k % per:
+            g_rem[k % per].replay()
+
+    replay(warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     e0.record(stream)
-    for _ in range(steps):
-        g.replay()
+    replay(steps)
     e1.record(stream)
     torch.cuda.synchronize()
     step_us = e0.elapsed_time(e1) * 1e3 / steps
 
     def batch(fn):
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cyc = sleep_cycles_for(5 + reps * 0.1, torch)
+        cyc = sleep_cycles_for(5 + reps * 0.2, torch)
         torch.cuda.synchronize()
         torch.cuda._sleep(cyc)
+        for _ in range(reps):             # sustained load before the timed calls (as kernel_durations)
+            fn()
         a0.record(stream)
         for _ in range(reps):
             fn()
@@ -827,7 +854,7 @@ def main():
                                f"num_splits={S}",
                    "global_batch": s_q, "num_splits": S,
                    "timing": f"exactly {args.warmup} untimed then {args.steps} timed steps, HIP graph replay "
-                             "cycling over the layers; warm: the rows all layers gather stay in the 256 MB "
+                             f"cycling over the layers, {GRAPH_STEPS} steps a graph; warm: the rows all layers gather stay in the 256 MB "
                              "last-level cache at this size, so value and roofline are warm-cache figures; "
                              "cold_us_per_step flushes every cache before each step"},
         "hbm_tbps": round(head["step_tbps"], 4),
