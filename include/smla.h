@@ -171,8 +171,8 @@ smla_status combine_splits(const smla_params* p, int32_t num_splits, const float
  * Design", "Adaptive NSPLIT": the split count adapts to the batch).  With
  * x = num_cus / s_q compute units per token: S = x / 8 (rounded down) when
  * x >= 40, 4 when x >= 16, 2 when x >= 8, else 1, capped at the block count
- * (and SMLA_MAX_SPLITS).  Jobs then run as 2, 4, 8 or 16 workgroups each (one
- * per part of the heads or of the output columns).
+ * (and SMLA_MAX_SPLITS).  Jobs then run as up to 16 workgroups each (one per
+ * part of the heads and of the output columns).
  * Deterministic in its arguments, so a captured graph stays valid.  Returns
  * >= 1, or 0 when an argument is non-positive.
  */

@@ -194,17 +194,20 @@ smla_status sparse_mla_decode(const smla_params* p, const void* q, const void* k
   a.n_blocks = n_blocks_of(p->topk);
   a.out_dtype = p->out_dtype;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  // Few jobs leave most compute units idle: then 2, 4 or 8 workgroups share each
-  // job, each owning part of its heads or of its 512 output columns.  Not for a
-  // direct FP8 output, whose scale needs every column of a token.
+  // Few jobs leave most compute units idle: then several workgroups share each
+  // job, each owning part of its heads and of its 512 output columns.  64
+  // heads: 1 to 16 workgroups a job; fewer heads: one per 16-head tile, times
+  // 1, 2 or 4 column parts.  Not for a direct FP8 output, whose scale needs
+  // every head and column of a token.
   const int64_t jobs = (int64_t)p->s_q * (direct ? 1 : num_splits);
   const int32_t cus = device_cus();
-  a.col_parts = (direct && p->out_dtype == SMLA_OUT_FP8_E4M3) ? 1
-                : p->h_q == 64 && 16 * jobs <= cus               ? 16
-                : 8 * jobs <= cus                                ? 8
-                : 4 * jobs <= cus                                ? 4
-                : 2 * jobs <= cus                                ? 2
-                                                                 : 1;
+  const int32_t tiles = p->h_q / 16;
+  if (direct && p->out_dtype == SMLA_OUT_FP8_E4M3)
+    a.col_parts = 1;
+  else if (p->h_q == 64)
+    a.col_parts = 16 * jobs <= cus ? 16 : 8 * jobs <= cus ? 8 : 4 * jobs <= cus ? 4 : 2 * jobs <= cus ? 2 : 1;
+  else
+    a.col_parts = 4 * tiles * jobs <= cus ? 4 * tiles : 2 * tiles * jobs <= cus ? 2 * tiles : tiles;
   a.cus = cus;
 
   if (direct) {        // direct path: one job per token, fused epilogue

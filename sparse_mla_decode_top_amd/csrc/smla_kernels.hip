@@ -7,22 +7,23 @@
 // the largest LSE) and cudnn-frontend PR #768 (near-equal block ranges with
 // the remainder on the leading splits; an empty split is O = 0, LSE = -inf).
 //
-// Kernels, by launch (64 heads unless stated; CS = workgroups a job takes):
-//   * decode_kernel8p (CS = 1, bf16 pool): 8 waves, all heads and columns.
-//   * decode_kernel8h (CS = 2): 8 waves, half of the heads each.
-//   * decode_kernel4t (CS = 4, 8 or 16): 4 waves, one 16-head tile each (CS =
-//     8 or 16: and a half or a quarter of its columns).  The head-part kernels
-//     repeat a head tile's QK^T only across its column parts.
+// Kernels, by launch (CS = workgroups a job takes):
+//   * decode_kernel8p (64 heads, CS = 1, bf16 pool): 8 waves, all heads and
+//     columns.
+//   * decode_kernel8h (64 heads, CS = 2): 8 waves, half of the heads each.
+//   * decode_kernel4t (CS = h_q / 16 head tiles x 1, 2 or 4 column parts): 4
+//     waves, one 16-head tile each (and a half or a quarter of its columns).
+//     The head-part kernels repeat a head tile's QK^T only across its column
+//     parts.
 //   * decode_kernel8m: a mixed launch for more jobs than compute units
 //     (decode_kernel8p's body, then decode_kernel8h's for a short last round).
-//   * decode_kernel (fewer heads, or CS = 1 with an FP8 pool or a direct FP8
-//     output): 4 waves, each workgroup 512 / CS output columns of all heads.
+//   * decode_kernel (CS = 1 where the kernels above do not apply: 64 heads of
+//     an FP8 pool in one part, or a direct FP8 output, whose scale needs every
+//     head and column of a token): 4 waves, all heads and columns.
 // The notes below describe decode_kernel; the others share its tile layout,
 // gather, softmax frame and partial protocol.
 //
-// decode kernel: CS in {1, 2, 4, 8} workgroups of 4 wave64s per (token,
-// split) job, each owning 512 / CS output columns (all of them compute the
-// scores; few jobs then still occupy many compute units).
+// decode kernel: one workgroup of 4 wave64s per (token, split) job.
 //   * The 64 slots of a KV block share one LDS tile, gathered by index with
 //     16-byte direct-to-LDS loads (global_load_lds_dwordx4) in which 8 lanes
 //     fetch one contiguous 128-byte segment of a row (FP8 pool: 4 lanes a
@@ -315,25 +316,22 @@ __device__ __forceinline__ void seed_fp8_combine(float* out_scale, void* out, in
 }
 
 // Job decode shared by every wave.  Job id = token * num_splits + split; a
-// launch covers the jobs from job0 on.  With CS > 1 column parts, the
-// workgroups of a job are 8 block ids apart in groups of 8 * CS (blocks are
-// spread over the 8 XCDs round robin, so all of them land on one XCD and
+// launch covers the jobs from job0 on.  With 2^lg_parts > 1 parts a job, the
+// workgroups of a job are 8 block ids apart in groups of 8 * 2^lg_parts (blocks
+// are spread over the 8 XCDs round robin, so all of them land on one XCD and
 // share its L2 for the job's rows).  Blocks [b0, b1) of split s: near-equal
 // ranges, the remainder on the leading splits, empty past the end.  part:
-// which 512 / CS output columns this workgroup owns.
+// which share of the job's heads and output columns this workgroup owns.
 struct Job {
   int t, s, b0, b1, part;
   bool live;
 };
-template <int CS>
-__device__ __forceinline__ Job decode_job(int block, int num_splits, int n_blocks, int job0, int n_jobs) {
+__device__ __forceinline__ Job decode_job(int block, int lg_parts, int num_splits, int n_blocks, int job0,
+                                          int n_jobs) {
   Job j;
   int id = block;
-  j.part = 0;
-  if (CS > 1) {
-    j.part = (id >> 3) % CS;
-    id = (id / (8 * CS)) * 8 + (id & 7);
-  }
+  j.part = (id >> 3) & ((1 << lg_parts) - 1);
+  id = ((id >> 3) >> lg_parts) * 8 + (id & 7);
   id += job0;
   j.live = id < n_jobs;
   j.t = id / num_splits;
@@ -354,12 +352,12 @@ __device__ __forceinline__ Job decode_job(int block, int num_splits, int n_block
 // The fields that the first instructions need come as leading scalar
 // arguments, which the build asks to be preloaded into SGPRs at wave launch:
 // the index and Q loads then issue without waiting for a kernel-argument load.
-template <bool KV_FP8, bool DIRECT, int CS, bool PREFETCH>
+template <bool KV_FP8, bool DIRECT, bool PREFETCH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
-  constexpr int kCt = 32 / CS;                    // column tiles of 16 owned by this workgroup
-  constexpr int kCols = 512 / CS;
+  constexpr int kCt = 32;                         // column tiles of 16: all 512 columns
+  constexpr int kCols = 512;
   constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
   // bf16 pool: two tiles.  FP8 pool: two code tiles + one bf16 tile.
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
@@ -375,8 +373,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
   const int head = 16 * wave + hl;
 
-  const Job job = decode_job<CS>((int)blockIdx.x, num_splits, n_blocks, job0, s_q * num_splits);
-  if (!job.live) return;                          // padding of the CS > 1 grid (whole workgroup)
+  const Job job = decode_job((int)blockIdx.x, 0, num_splits, n_blocks, job0, s_q * num_splits);
+  if (!job.live) return;
   const int t = job.t;
   const int32_t* idx_row = indices + (int64_t)t * topk;
 
@@ -385,7 +383,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   float l_run = 0.f;                  // this lane's share of the denominator
   if (tid == 0) s_restart = 0;        // ordered before its readers by the loop barriers
   bool restarted = false;
-  f32x4 acc[kCt];                     // O^T: column tile ct -> columns kCols * part + 16ct + 4G + i
+  f32x4 acc[kCt];                     // O^T: column tile ct -> columns 16ct + 4G + i
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -563,24 +561,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       const uint32_t tl = lds_addr(s_tile + cur * kBufBytes);
       // four bases keep every offset within the 16-bit ds_read field
       uint32_t kbase[4], vbase[4];
-      // V^T of this workgroup's columns: column tile ct (local) is global
-      // tile kCt * part + ct; 4 column tiles per 128-byte octet (bf16) or per
-      // 64-byte quartet (FP8 codes)
+      // V^T: 4 column tiles per 128-byte octet (bf16) or per 64-byte quartet
+      // (FP8 codes)
       if constexpr (KV_FP8) {
         kbase[0] = opaque(tl + f8.k[0]);
         kbase[1] = opaque(tl + f8.k[1]);
         kbase[2] = kbase[3] = 0u;
-        const uint32_t tlv = tl + job.part * (kCt / 4) * 4096;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + f8.v[m]);
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tl + f8.v[m]);
       } else {
         kbase[0] = opaque(tl + kb0);
         kbase[1] = opaque(tl + kb1);
         kbase[2] = opaque(tl + kb0 + 65536);
         kbase[3] = opaque(tl + kb1 + 65536);
-        const uint32_t tlv = tl + job.part * (kCt / 4) * 8192;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + vb[m]);
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tl + vb[m]);
       }
       auto kfrag = [&](int ks, int st) -> bf16x8 {
         if constexpr (KV_FP8) return fp8_kfrag(kbase[ks & 1] + (ks >> 1) * 4096 + st * 1024);
@@ -712,10 +707,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           if (kk == 0 && sm_at(ct) >= 0) sm_step(1, sm_at(ct));
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (kk == 0) {                                // steps that did not fit between the MFMAs
-#pragma unroll
-          for (int k = kCt - 1; k < 15; ++k) sm_step(1, k);
-        }
       };
 
       qk_half(0);
@@ -770,12 +761,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) {
     const f32x4 v = acc[ct] * oscale;
-    if (DIRECT && CS == 1 && wave_ok)
+    if (DIRECT && wave_ok)
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     *(f32x4*)(stg + hl * kStagePitch + 64 * ct + 16 * G) = v;
   }
   float qscale = 1.0f;
-  if (DIRECT && CS == 1 && a.out_dtype == kOutFp8) {   // per-token amax over every head
+  if (DIRECT && a.out_dtype == kOutFp8) {       // per-token amax over every head
     amax = warp_max(amax);
     if (lane == 0) s_red[wave] = amax;
     lds_barrier();
@@ -785,9 +776,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   if (wave_ok) {
     const int64_t row0 = (DIRECT ? (int64_t)t * h_q : ((int64_t)job.s * s_q + t) * h_q) + 16 * wave;
-    const int col0 = job.part * kCols;
     if (!DIRECT || a.out_dtype == kOutF32) {     // 1 KB of whole row pieces per instruction
-      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512 + col0;
+      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512;
 #pragma unroll
       for (int j = 0; j < 16 * kCols / 256; ++j) {
         const int f = 256 * j + 4 * lane;          // float index in the wave's 16 x kCols block
@@ -797,7 +787,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     } else if (a.out_dtype == kOutBf16) {        // 1 KB (one or two row pieces) per instruction
       constexpr int kLanesPerRow = kCols / 8, kRowsPer = 64 / kLanesPerRow;
       const int rr = lane / kLanesPerRow, cc = 8 * (lane % kLanesPerRow);
-      uint16_t* dst = (uint16_t*)a.out + row0 * 512 + col0 + cc;
+      uint16_t* dst = (uint16_t*)a.out + row0 * 512 + cc;
 #pragma unroll
       for (int j = 0; j < 16 / kRowsPer; ++j) {
         const int r = kRowsPer * j + rr;
@@ -806,7 +796,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
                                          pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
       }
-    } else if (CS == 1) {                        // e4m3: two 512 B rows per instruction
+    } else {                                     // e4m3: two 512 B rows per instruction
       uint8_t* dst = (uint8_t*)a.out + row0 * 512;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -822,7 +812,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         *(u32x4*)(dst + h * 512 + 16 * (lane & 31)) = w;
       }
     }
-    if (G == 0 && job.part == 0) {               // both column parts hold the same LSE
+    if (G == 0) {
       if (!DIRECT)
         a.lse_accum[row0 + hl] = lse;
       else if (a.lse_out != nullptr)
@@ -832,7 +822,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Split jobs of a decode with an FP8 output: the combine's running amax per
   // token starts from -0.0 (its "an amax, not yet a scale" form), stored here
   // so that the combine needs no launch of its own for it.
-  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && job.part == 0 && tid == 0)
+  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && tid == 0)
     seed_fp8_combine(a.out_scale, a.out, t, h_q);
 }
 
@@ -882,7 +872,7 @@ __device__ __forceinline__ void decode8p_body(
   float* const pex_own = (float*)s_pex[wave];
   const float* const pex_par = (const float*)s_pex[wave ^ 4];
 
-  const Job job = decode_job<1>(block, num_splits, n_blocks, job0, s_q * num_splits);
+  const Job job = decode_job(block, 0, num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the grid (whole workgroup)
   const int t = job.t;
   const int32_t* idx_row = indices + (int64_t)t * topk;
@@ -1256,7 +1246,7 @@ __device__ __forceinline__ void decode8h_body(
   float* const pex_own = (float*)s_pex[wave];
   auto pex_of = [&](int q) -> const float* { return (const float*)s_pex[hq + 2 * q]; };   // quarter q's wave
 
-  const Job job = decode_job<2>(block, num_splits, n_blocks, job0, s_q * num_splits);
+  const Job job = decode_job(block, 1, num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the grid (whole workgroup)
   const int t = job.t;
   const int hbase = 32 * job.part;                // first head of this part
@@ -1622,10 +1612,10 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8h(
 }
 
 // ---------------------------------------------------------------------------
-// decode4t_body: a job in 4 CP workgroups of 4 waves, each owning one head tile
-// (16 heads) and 512 / CP of the output columns (bf16 pool, 64 heads; CP = 1
-// or 2).  None of them repeats another head tile's QK^T, where 4 or 8 column
-// parts would each compute all 64 heads' scores.  Wave w scores slot quarter
+// decode4t_body: a job in (h_q / 16) * CP workgroups of 4 waves, each owning
+// one head tile (16 heads) and 512 / CP of the output columns (CP = 1, 2 or
+// 4).  None of them repeats another head tile's QK^T, where column parts of
+// every head would each compute all of the heads' scores.  Wave w scores slot quarter
 // w (16 slots) of every block; the four waves trade their bf16 weights through
 // LDS (as decode8h_body's head tile) and each accumulates every slot into its
 // quarter of the workgroup's columns.  One frame per head for the four.  The
@@ -1662,11 +1652,13 @@ __device__ __forceinline__ void decode4t_body(
   float* const pex_own = (float*)s_pex[wave];
   auto pex_of = [&](int q) -> const float* { return (const float*)s_pex[q]; };
 
-  const Job job = decode_job<4 * CP>(block, num_splits, n_blocks, job0, s_q * num_splits);
+  constexpr int kLgCP = CP == 4 ? 2 : CP == 2 ? 1 : 0;
+  const int lg_tiles = h_q == 64 ? 2 : h_q == 32 ? 1 : 0;     // h_q / 16 head tiles
+  const Job job = decode_job(block, lg_tiles + kLgCP, num_splits, n_blocks, job0, s_q * num_splits);
   if (!job.live) return;                          // padding of the grid (whole workgroup)
   const int t = job.t;
-  const int htile = job.part / CP;                // head tile: heads [16 htile, +16)
-  const int cpart = job.part % CP;                // columns [kCols cpart, +kCols)
+  const int htile = job.part >> kLgCP;            // head tile: heads [16 htile, +16)
+  const int cpart = job.part & (CP - 1);          // columns [kCols cpart, +kCols)
   const int head = 16 * htile + hl;
   const int32_t* idx_row = indices + (int64_t)t * topk;
 
@@ -2391,42 +2383,13 @@ template <bool DIRECT, bool PREFETCH>
 hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int job1, hipStream_t stream) {
   const unsigned n_jobs = (unsigned)(job1 - job0);
   const dim3 grid(cs == 1 ? n_jobs : (n_jobs + 7) / 8 * 8 * cs);
-#define SMLA_LAUNCH(KERNEL, THREADS, CSV)                                                                 \
-  do {                                                                                                    \
-    if (kv_fp8)                                                                                           \
-      hipLaunchKernelGGL((KERNEL<true, DIRECT, CSV, PREFETCH>), grid, dim3(THREADS), 0, stream, a.indices, \
-                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);                   \
-    else                                                                                                  \
-      hipLaunchKernelGGL((KERNEL<false, DIRECT, CSV, PREFETCH>), grid, dim3(THREADS), 0, stream, a.indices,\
-                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);                   \
-  } while (0)
+  const int tiles = a.h_q / 16;
+  const bool fp8_direct = DIRECT && a.out_dtype == kOutFp8;
   // 64 heads in one column part, bf16 pool, no direct FP8 output: the 8-wave
   // kernel whose wave pairs trade their weights.
-  if (a.h_q == 64 && cs == 1 && !kv_fp8 && !(DIRECT && a.out_dtype == kOutFp8)) {
+  if (a.h_q == 64 && cs == 1 && !kv_fp8 && !fp8_direct) {
     hipLaunchKernelGGL((decode_kernel8p<DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices, a.q,
                        a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
-    return hipGetLastError();
-  }
-  // 64 heads in 4, 8 or 16 parts: one head tile per 4-wave workgroup (8 and 16
-  // parts: and a half or a quarter of its columns), none repeating another
-  // tile's QK^T.
-  if (a.h_q == 64 && (cs == 4 || cs == 8 || cs == 16)) {
-#define SMLA_LAUNCH_4T(FP8, CPV)                                                                             \
-  hipLaunchKernelGGL((decode_kernel4t<FP8, DIRECT, PREFETCH, CPV>), grid, dim3(kThreads), 0, stream, a.indices, \
-                     a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a)
-    if (kv_fp8 && cs == 4)
-      SMLA_LAUNCH_4T(true, 1);
-    else if (kv_fp8 && cs == 8)
-      SMLA_LAUNCH_4T(true, 2);
-    else if (kv_fp8)
-      SMLA_LAUNCH_4T(true, 4);
-    else if (cs == 4)
-      SMLA_LAUNCH_4T(false, 1);
-    else if (cs == 8)
-      SMLA_LAUNCH_4T(false, 2);
-    else
-      SMLA_LAUNCH_4T(false, 4);
-#undef SMLA_LAUNCH_4T
     return hipGetLastError();
   }
   // 64 heads in two parts: head halves that do not repeat QK^T.
@@ -2439,33 +2402,54 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
                          a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
     return hipGetLastError();
   }
-  // Fewer heads, or one part with an FP8 pool or a direct FP8 output: the
-  // 4-wave column-part kernel.
-  if (cs == 8)
-    SMLA_LAUNCH(decode_kernel, kThreads, 8);
-  else if (cs == 4)
-    SMLA_LAUNCH(decode_kernel, kThreads, 4);
-  else if (cs == 2)
-    SMLA_LAUNCH(decode_kernel, kThreads, 2);
+  // One 16-head tile per 4-wave workgroup, whole or in 2 or 4 column parts
+  // (64 heads: 4, 8 or 16 workgroups a job; 32: 2, 4 or 8; 16: 1, 2 or 4),
+  // none repeating another tile's QK^T.
+  if (!fp8_direct && cs >= tiles && cs <= 4 * tiles && (a.h_q < 64 || cs >= 4)) {
+#define SMLA_LAUNCH_4T(FP8, CPV)                                                                             \
+  hipLaunchKernelGGL((decode_kernel4t<FP8, DIRECT, PREFETCH, CPV>), grid, dim3(kThreads), 0, stream, a.indices, \
+                     a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a)
+    const int cp = cs / tiles;
+    if (kv_fp8 && cp == 1)
+      SMLA_LAUNCH_4T(true, 1);
+    else if (kv_fp8 && cp == 2)
+      SMLA_LAUNCH_4T(true, 2);
+    else if (kv_fp8)
+      SMLA_LAUNCH_4T(true, 4);
+    else if (cp == 1)
+      SMLA_LAUNCH_4T(false, 1);
+    else if (cp == 2)
+      SMLA_LAUNCH_4T(false, 2);
+    else
+      SMLA_LAUNCH_4T(false, 4);
+#undef SMLA_LAUNCH_4T
+    return hipGetLastError();
+  }
+  // One part otherwise (64 heads of an FP8 pool, or a direct FP8 output): the
+  // 4-wave kernel over every head and column.
+  if (cs != 1) return hipErrorInvalidValue;
+  if (kv_fp8)
+    hipLaunchKernelGGL((decode_kernel<true, DIRECT, PREFETCH>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
+                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
   else
-    SMLA_LAUNCH(decode_kernel, kThreads, 1);
-#undef SMLA_LAUNCH
+    hipLaunchKernelGGL((decode_kernel<false, DIRECT, PREFETCH>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
+                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
   return hipGetLastError();
 }
 
 // The whole launch plan.  With one column part and more jobs than compute
 // units, the last round would leave CUs idle: when it holds at most half of
-// them, its jobs take 2, 4 or 8 column parts (the largest that keeps it within
-// one round), so it finishes sooner -- in the same launch for a bf16 pool and
-// 64 heads (decode_kernel8m), else in a second one.  A direct FP8 output
-// keeps one part (its scale needs every column).
+// them, its jobs take 2, 4 or 8 parts (the largest that keeps it within one
+// round; 4 at most for 16 heads), so it finishes sooner -- in the same launch
+// for a bf16 pool and 64 heads (decode_kernel8m), else in a second one.  A
+// direct FP8 output keeps one part (its scale needs every column).
 template <bool DIRECT, bool PREFETCH>
 hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
   const int n_jobs = a.s_q * (DIRECT ? 1 : a.num_splits);
   const int cus = a.cus;
   const int tail = cus > 0 ? n_jobs % cus : 0;
   if (a.col_parts == 1 && n_jobs > cus && tail > 0 && 2 * tail <= cus && !(DIRECT && a.out_dtype == kOutFp8)) {
-    const int cs_tail = 8 * tail <= cus ? 8 : 4 * tail <= cus ? 4 : 2;
+    const int cs_tail = min(8 * tail <= cus ? 8 : 4 * tail <= cus ? 4 : 2, 4 * (a.h_q / 16));
     const int n_head = n_jobs - tail;
     if (a.h_q == 64 && !kv_fp8 && n_head % 8 == 0) {     // both bodies in one launch, the tail in 2 parts
       const dim3 grid((unsigned)(n_head + (tail + 7) / 8 * 8 * 2));

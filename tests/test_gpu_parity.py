@@ -177,6 +177,30 @@ def test_fewer_heads(h_q):
         H.assert_lse_close(res["lse"], L_ref)
 
 
+@pytest.mark.parametrize("h_q,s_q,S,kv_dtype", [
+    (16, 300, 1, "bf16"),   # one 16-head tile a job, the last 44 jobs in 4 column parts
+    (16, 100, 1, "fp8"),    # 2 column parts
+    (16, 20, 2, "bf16"),    # 4 column parts
+    (32, 100, 1, "bf16"),   # 2 head tiles
+    (32, 40, 1, "fp8"),     # 2 head tiles x 2 column parts
+    (32, 6, 4, "bf16"),     # 2 head tiles x 4 column parts
+])
+def test_fewer_heads_every_part_count(h_q, s_q, S, kv_dtype):
+    """16 and 32 heads in every workgroup count a job can take: one per 16-head
+    tile times 1, 2 or 4 column parts (the count follows the job count), FP8
+    pools included, every token against the oracle."""
+    print(f"[case] h_q={h_q} s_q={s_q} S={S} {kv_dtype}", flush=True)
+    inp = W.make_inputs(s_q, h_q, 16384, 640, seed=31 + s_q, kv_dtype=kv_dtype, sink=True, pad="random")
+    dev = H.DeviceInputs(inp)
+    O_ref, L_ref = oracle.attend(inp.q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    res = H.run(dev, S, "f32", "direct" if S == 1 else "split")
+    H.assert_o_close(res["O"], O_fin)
+    H.assert_lse_close(res["lse"], L_ref)
+    res = H.run(dev, S, "bf16", "direct" if S == 1 else "split")
+    H.assert_o_close(res["O"], O_fin, rel=2.0 ** -8)
+
+
 def test_score_far_beyond_the_frame_restarts_the_job():
     """A late slot whose log2-unit score exceeds the head's frame (fixed by the
     first block) by far more than the 64-unit slack: the kernel re-runs the job
@@ -197,6 +221,30 @@ def test_score_far_beyond_the_frame_restarts_the_job():
     O_fin = H.oracle_final(inp, O_ref, L_ref)
     assert L_ref[0, 0] > 600 and L_ref[1, 37] > 600
     for S, path in ((1, "direct"), (1, "split"), (2, "split"), (10, "split")):
+        res = H.run(dev, S, "f32", path)
+        H.assert_o_close(res["O"], O_fin)
+        assert H.assert_lse_close_planted(res["lse"], L_ref, planted) >= 2
+
+
+@pytest.mark.parametrize("h_q", [16, 32])
+def test_fewer_heads_restart(h_q):
+    """The restart of a job whose late score exceeds the frame by far, with 16 and 32
+    heads (head-tile workgroups): token 0 head 3 in block 6, token 1 the last head in
+    the second half of block 9."""
+    print(f"[case] h_q={h_q}", flush=True)
+    inp = W.make_inputs(2, h_q, 8192, 640, seed=41, sink=True)
+    q = inp.q
+    planted_rows = []
+    for t, head, slot in ((0, 3, 6 * 64 + 9), (1, h_q - 1, 9 * 64 + 50)):
+        row = int(inp.indices[t, slot])
+        inp.kv_bits[row] = W.f32_to_bf16_bits(20.0 * q[t, head])
+        planted_rows.append(row)
+    planted = H.tokens_gathering(inp.indices, planted_rows)
+    dev = H.DeviceInputs(inp)
+    O_ref, L_ref = oracle.attend(q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    assert L_ref[0, 3] > 400 and L_ref[1, h_q - 1] > 400     # far beyond a frame near 10 (+64 slack)
+    for S, path in ((1, "direct"), (2, "split"), (10, "split")):
         res = H.run(dev, S, "f32", path)
         H.assert_o_close(res["O"], O_fin)
         assert H.assert_lse_close_planted(res["lse"], L_ref, planted) >= 2
