@@ -8,8 +8,7 @@
 // the remainder on the leading splits; an empty split is O = 0, LSE = -inf).
 //
 // Kernels, by launch (CS = workgroups a job takes):
-//   * decode_kernel8p (64 heads, CS = 1, bf16 pool): 8 waves, all heads and
-//     columns.
+//   * decode_kernel8p (64 heads, CS = 1): 8 waves, all heads and columns.
 //   * decode_kernel8h (64 heads, CS = 2): 8 waves, half of the heads each.
 //   * decode_kernel4t (CS = h_q / 16 head tiles x 1, 2 or 4 column parts): 4
 //     waves, one 16-head tile each (and a half or a quarter of its columns).
@@ -17,9 +16,8 @@
 //     parts.
 //   * decode_kernel8m: a mixed launch for more jobs than compute units
 //     (decode_kernel8p's body, then decode_kernel8h's for a short last round).
-//   * decode_kernel (CS = 1 where the kernels above do not apply: 64 heads of
-//     an FP8 pool in one part, or a direct FP8 output, whose scale needs every
-//     head and column of a token): 4 waves, all heads and columns.
+//   * decode_kernel (a direct FP8 output, whose scale needs every head and
+//     column of a token: CS = 1): 4 waves, all heads and columns.
 // The notes below describe decode_kernel; the others share its tile layout,
 // gather, softmax frame and partial protocol.
 //
@@ -59,8 +57,8 @@
 // shared frame per head; the two waves of a SIMD in the 8-wave kernels
 // score different slots, so the hardware overlaps one's softmax and LDS
 // reads with the other's MFMAs.  With more jobs than compute units, a last
-// round that fills at most half of them takes 2, 4 or 8 parts (a bf16 pool
-// and 64 heads: 2, in the same launch, decode_kernel8m).
+// round that fills at most half of them takes 2, 4 or 8 parts (64 heads: 2,
+// in the same launch, decode_kernel8m).
 //
 // combine kernel: split-major partials -> final output (+ sink, cast).
 
@@ -832,7 +830,7 @@ constexpr int kThreads8 = 64 * kWaves8;
 
 // ---------------------------------------------------------------------------
 // decode_kernel8p: one 8-wave workgroup per job that owns all 512 output
-// columns (64 heads, bf16 pool), for launches with a single column part.
+// columns (64 heads, either pool), for launches with a single column part.
 // The two waves on a SIMD own the same 16 heads and each scores one 32-slot
 // half of every block.  Here they trade their bf16
 // weights through LDS, and each wave accumulates every slot of the block into
@@ -842,14 +840,21 @@ constexpr int kThreads8 = 64 * kWaves8;
 // that has a valid slot, so their weights add into one accumulator.
 // LDS: the two tiles and the weight exchange fill the 160 KB exactly; the
 // frame, end-of-pass and denominator exchanges reuse the weight area, and
-// validity comes from a ballot of the block's indices.
+// validity comes from a ballot of the block's indices.  KV_FP8: the two code
+// tiles take the first bf16 tile's space, waves 0-3 gather them (as
+// decode8h_body), the Q rows are staged over the second code tile (free until
+// the first block's look-ahead gather, which follows a barrier) and the
+// block's row scales follow the Q rows.
 // ---------------------------------------------------------------------------
 // LDS of decode_kernel8p: the two tiles, then the weight exchange.
 constexpr int kLds8pBytes = 2 * kTileBytes + kWaves8 * 2048;
+constexpr int kLds8pQFp8 = kCodeTileBytes;                   // FP8: the staged Q rows
+constexpr int kLds8pScaleFp8 = kCodeTileBytes + kTileBytes;  // FP8: [2][kBlk] row scales
+static_assert(kLds8pScaleFp8 + 2 * kBlk * 4 <= 2 * kTileBytes, "the FP8 row scales stay below the weight area");
 
 // The body of decode_kernel8p for workgroup `block` of its launch, on the LDS
 // at `smem` (kLds8pBytes).
-template <bool DIRECT, bool PREFETCH>
+template <bool KV_FP8, bool DIRECT, bool PREFETCH>
 __device__ __forceinline__ void decode8p_body(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, const DecodeArgs& a, int block, uint8_t* smem) {
@@ -860,6 +865,9 @@ __device__ __forceinline__ void decode8p_body(
   // Per wave: its block weights (bf16 hi terms at +0, lo terms at +1024, 16
   // bytes a lane in MFMA operand order), read by the partner wave.
   uint8_t (*const s_pex)[2048] = reinterpret_cast<uint8_t (*)[2048]>(smem + 2 * kTileBytes);
+  float (*const s_scale)[kBlk] = reinterpret_cast<float (*)[kBlk]>(smem + kLds8pScaleFp8);   // FP8
+  constexpr int kQOff = KV_FP8 ? kLds8pQFp8 : kQOffset;     // LDS byte offset of the staged Q rows
+  constexpr int kBufBytes = KV_FP8 ? kCodeTileBytes : kTileBytes;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -896,35 +904,49 @@ __device__ __forceinline__ void decode8p_body(
     const uint32_t tile_lds0 = lds_addr(s_tile);
     bool framed = false;              // workgroup-uniform: the pair frames are set
 
-    // Wave w gathers rows [8w, 8w + 8): lanes 8k..8k+7 one row, chunk
-    // (l & 7) ^ (row & 7) of each octet; a masked row copies the zero row, so a
-    // wave always has exactly 9 DMAs in flight (the first pass counts on it).
-    auto issue_gather = [&](int idx_lane, int buf) {
+    // bf16: wave w gathers rows [8w, 8w + 8), lanes 8k..8k+7 one row, chunk
+    // (l & 7) ^ (row & 7) of each octet.  FP8: waves 0-3 gather rows
+    // [16w, 16w + 16) of the code tile, 4 lanes a row.  A masked row copies the
+    // zero row, so a gathering wave always has exactly 9 DMAs in flight (the
+    // first pass counts on it).
+    const bool gathers = !KV_FP8 || wave < 4;
+    auto row_src = [&](int idx_lane) -> const uint8_t* {
+      if (KV_FP8) {
+        const int row_idx = __shfl(idx_lane, 16 * (wave & 3) + (lane >> 2));
+        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + fp8_gather_chunk(lane);
+      }
       const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
-      const uint32_t lds_base = tile_lds0 + buf * kTileBytes + wave * 1024;
-      const uint8_t* src = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-                           (((lane & 7) ^ rsw(lane >> 3)) * 16);
-      dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
+      return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+             (((lane & 7) ^ rsw(lane >> 3)) * 16);
+    };
+    auto issue_gather = [&](int idx_lane, int buf) {
+      if (!KV_FP8) {
+        dma_octets(row_src(idx_lane), __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kTileBytes + wave * 1024));
+      } else if (gathers) {
+        dma_quartets(row_src(idx_lane),
+                     __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kCodeTileBytes + wave * 1024));
+      }
     };
 
     // per-lane LDS byte offsets of the operand reads (the tile layout above)
     const int sw_k = rsw(hl);
     const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
     const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
+    const Fp8Offsets f8 = fp8_offsets(lane);                  // FP8 pool: K and V^T reads of the codes
     const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
     const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
     int vb[4];                                                  // column tile ct & 3
 #pragma unroll
     for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
 
-    // ---- prologue: Q rows (heads) [8w, 8w + 8) into LDS by wave w, at kQOffset
+    // ---- prologue: Q rows (heads) [8w, 8w + 8) into LDS by wave w, at kQOff
     int idx_cur;
     {
       const int r0 = 8 * wave + (lane >> 3);
       const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
       const uint8_t* qbase = (const uint8_t*)(q_ptr + (int64_t)t * h_q * 576);
       idx_cur = load_idx_and_q1(idx_row + min(job.b0 * kBlk + lane, topk - 1), qbase + (int64_t)r0 * 1152 + chunk,
-                                __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + wave * 1024));
+                                __builtin_amdgcn_readfirstlane(tile_lds0 + kQOff + wave * 1024));
     }
 
     auto run_pass = [&](const bool first) __attribute__((always_inline)) -> bool {
@@ -935,24 +957,34 @@ __device__ __forceinline__ void decode8p_body(
     int idx_nxt = load_idx(job.b0 + 1);
     bool valid_cur = valid_of(idx_cur);
     if (first) {
-      // Q rows landed (issued first; block b0's 9 DMAs and, with the
-      // look-ahead, the next index load stay in flight).
-      if (PREFETCH)
-        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      // Q rows landed (issued first; block b0's 9 DMAs of a gathering wave
+      // and, with the look-ahead, the next index load stay in flight).
+      if (gathers) {
+        if (PREFETCH)
+          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else {
+        if (PREFETCH)
+          asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       lds_barrier();
-      const uint32_t qt = lds_addr(s_tile) + kQOffset + hq * 2048;
+      const uint32_t qt = lds_addr(s_tile) + kQOff + hq * 2048;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
         const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
         qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
       }
     }
+    // FP8: block b0's row scales (stored by wave 0 at the top of the block loop).
+    float sc_cur = (KV_FP8 && wave == 0 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
 
     for (int b = job.b0; b < job.b1; ++b) {
       const int cur = (b - job.b0) & 1;
       wait_vmem_all();          // this wave's share of block b has landed
+      if (KV_FP8 && wave == 0) s_scale[cur][lane] = sc_cur;
       lds_barrier();            // ... and every wave's; block b-1 and its weights fully consumed
       // slot s of the block is valid iff bit s is set (the same in every wave)
       const uint32_t vhalf = (uint32_t)(__ballot(valid_cur) >> (32 * sg));
@@ -961,42 +993,59 @@ __device__ __forceinline__ void decode8p_body(
       // Block b+1: one DMA per QK^T k-step pair (masked rows and rows past the
       // job's last block copy the zero row).
       bool valid_nxt = false;
+      float sc_nxt = 0.f;
       const uint8_t* gsrc = g_zero_row;
       uint32_t gbase = 0u;
       if (PREFETCH) {
         idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
         valid_nxt = valid_of(idx_nxt);
-        const int row_idx = __shfl(idx_nxt, 8 * wave + (lane >> 3));
-        gsrc = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-               (((lane & 7) ^ rsw(lane >> 3)) * 16);
-        gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kTileBytes + wave * 1024);
+        if (KV_FP8 && wave == 0 && valid_nxt) sc_nxt = a.kv_scale[idx_nxt];
+        gsrc = row_src(idx_nxt);
+        gbase = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + (KV_FP8 ? (wave & 3) : wave) * 1024);
       }
       auto gather_dma = [&](const int d) __attribute__((always_inline)) {
-        if (!PREFETCH) return;
+        if (!PREFETCH || !gathers) return;
+        constexpr int L = KV_FP8 ? 4096 : 8192, Gs = KV_FP8 ? 64 : 128;
         switch (d) {
-          case 0: dma_one<8192, 128, 0>(gsrc, gbase); break;
-          case 1: dma_one<8192, 128, 1>(gsrc, gbase); break;
-          case 2: dma_one<8192, 128, 2>(gsrc, gbase); break;
-          case 3: dma_one<8192, 128, 3>(gsrc, gbase); break;
-          case 4: dma_one<8192, 128, 4>(gsrc, gbase); break;
-          case 5: dma_one<8192, 128, 5>(gsrc, gbase); break;
-          case 6: dma_one<8192, 128, 6>(gsrc, gbase); break;
-          case 7: dma_one<8192, 128, 7>(gsrc, gbase); break;
-          default: dma_one<8192, 128, 8>(gsrc, gbase); break;
+          case 0: dma_one<L, Gs, 0>(gsrc, gbase); break;
+          case 1: dma_one<L, Gs, 1>(gsrc, gbase); break;
+          case 2: dma_one<L, Gs, 2>(gsrc, gbase); break;
+          case 3: dma_one<L, Gs, 3>(gsrc, gbase); break;
+          case 4: dma_one<L, Gs, 4>(gsrc, gbase); break;
+          case 5: dma_one<L, Gs, 5>(gsrc, gbase); break;
+          case 6: dma_one<L, Gs, 6>(gsrc, gbase); break;
+          case 7: dma_one<L, Gs, 7>(gsrc, gbase); break;
+          default: dma_one<L, Gs, 8>(gsrc, gbase); break;
         }
       };
       const int idx_after = load_idx(b + 2);
 
-      const uint32_t tl = lds_addr(s_tile + cur * kTileBytes);
-      const uint32_t kbase[4] = {opaque(tl + kb0), opaque(tl + kb1), opaque(tl + kb0 + 65536),
-                                 opaque(tl + kb1 + 65536)};
+      // Block b's operands: bf16 rows, or the e4m3 codes converted in registers.
+      const uint32_t tl = lds_addr(s_tile + cur * kBufBytes);
+      uint32_t kbase[4], vbase[4];
+      if constexpr (KV_FP8) {
+        kbase[0] = opaque(tl + f8.k[0]);
+        kbase[1] = opaque(tl + f8.k[1]);
+        kbase[2] = kbase[3] = 0u;
+        const uint32_t tlv = tl + sg * 4 * 4096;     // this wave's 256 columns
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + f8.v[m]);
+      } else {
+        kbase[0] = opaque(tl + kb0);
+        kbase[1] = opaque(tl + kb1);
+        kbase[2] = opaque(tl + kb0 + 65536);
+        kbase[3] = opaque(tl + kb1 + 65536);
+        const uint32_t tlv = tl + sg * 4 * 8192;     // this wave's 256 columns
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tlv + vb[m]);
+      }
       auto kfrag = [&](int ks, int st) -> bf16x8 {
+        if constexpr (KV_FP8) return fp8_kfrag(kbase[ks & 1] + (ks >> 1) * 4096 + st * 1024);
         const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
         return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
       };
-      const uint32_t tlv = tl + sg * 4 * 8192;     // this wave's 256 columns
-      const uint32_t vbase[4] = {opaque(tlv + vb[0]), opaque(tlv + vb[1]), opaque(tlv + vb[2]), opaque(tlv + vb[3])};
       auto vfrag = [&](int ct, int kk) -> bf16x8 {
+        if constexpr (KV_FP8) return fp8_vfrag(vbase[ct & 3] + (ct >> 2) * 4096 + kk * 2048);
         const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
         const i16x4 v1 =
@@ -1044,12 +1093,19 @@ __device__ __forceinline__ void decode8p_body(
 #pragma unroll
       for (int a0 = 0; a0 < kAheadV; ++a0) vf[a0] = vfrag(a0, sg);
       const uint32_t vbits = vhalf >> (4 * G);
+      f32x4 rsc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if (KV_FP8) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) rsc[u] = *(const f32x4*)&s_scale[cur][32 * sg + 16 * u + 4 * G];
+      }
       float tv[8];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          tv[4 * u + i] = fmaf(sacc[u][i], scale_log2, ((vbits >> (16 * u + i)) & 1u) ? 0.f : kMaskedScore);
+        for (int i = 0; i < 4; ++i) {
+          const float bias = ((vbits >> (16 * u + i)) & 1u) ? 0.f : kMaskedScore;
+          tv[4 * u + i] = KV_FP8 ? fmaf(sacc[u][i] * scale_log2, rsc[u][i], bias) : fmaf(sacc[u][i], scale_log2, bias);
+        }
       float m = fmaxf(fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3])), fmaxf(fmaxf(tv[4], tv[5]), fmaxf(tv[6], tv[7])));
       m = rows_max(m);
       m_seen = fmaxf(m_seen, m);
@@ -1067,8 +1123,9 @@ __device__ __forceinline__ void decode8p_body(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float tt = tv[e];
-        const float p = __builtin_amdgcn_exp2f(tt - M_run);
+        float p = __builtin_amdgcn_exp2f(tt - M_run);
         l_run += p;
+        if (KV_FP8) p *= rsc[e >> 2][e & 3];
         pv[e] = p;
       }
       uint32_t ph[4], pl[4];
@@ -1108,6 +1165,7 @@ __device__ __forceinline__ void decode8p_body(
       }
 
       valid_cur = valid_nxt;
+      sc_cur = sc_nxt;
       idx_nxt = idx_after;
     }
     wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
@@ -1195,13 +1253,13 @@ __device__ __forceinline__ void decode8p_body(
   if (!DIRECT && a.out_scale != nullptr && job.s == 0 && tid == 0) seed_fp8_combine(a.out_scale, a.out, t, h_q);
 }
 
-template <bool DIRECT, bool PREFETCH>
+template <bool KV_FP8, bool DIRECT, bool PREFETCH>
 __global__ __launch_bounds__(kThreads8) void decode_kernel8p(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds8pBytes];
-  decode8p_body<DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a, (int)blockIdx.x,
-                                  smem);
+  decode8p_body<KV_FP8, DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, job0, a,
+                                          (int)blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2071,7 +2129,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel4t(
 // The tail's workgroups start as soon as compute units free up, with no kernel
 // boundary in between.  n_head is a multiple of 8, so the tail keeps the XCD
 // grouping of a job's parts.
-template <bool DIRECT, bool PREFETCH>
+template <bool KV_FP8, bool DIRECT, bool PREFETCH>
 __global__ __launch_bounds__(kThreads8) void decode_kernel8m(
     const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
     int32_t s_q, int32_t topk, int32_t h_q, int32_t n_head, DecodeArgs a) {
@@ -2079,10 +2137,11 @@ __global__ __launch_bounds__(kThreads8) void decode_kernel8m(
   const int block = (int)blockIdx.x;
   static_assert(kLds8pBytes >= kLds8hBytes, "the mixed launch's LDS holds either body");
   if (block < n_head)
-    decode8p_body<DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, 0, a, block, smem);
+    decode8p_body<KV_FP8, DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, 0, a, block,
+                                            smem);
   else
-    decode8h_body<false, DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, n_head, a,
-                                           block - n_head, smem);
+    decode8h_body<KV_FP8, DIRECT, PREFETCH>(indices, q_ptr, num_splits, n_blocks, s_q, topk, h_q, n_head, a,
+                                            block - n_head, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2385,11 +2444,15 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
   const dim3 grid(cs == 1 ? n_jobs : (n_jobs + 7) / 8 * 8 * cs);
   const int tiles = a.h_q / 16;
   const bool fp8_direct = DIRECT && a.out_dtype == kOutFp8;
-  // 64 heads in one column part, bf16 pool, no direct FP8 output: the 8-wave
-  // kernel whose wave pairs trade their weights.
-  if (a.h_q == 64 && cs == 1 && !kv_fp8 && !fp8_direct) {
-    hipLaunchKernelGGL((decode_kernel8p<DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices, a.q,
-                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
+  // 64 heads in one column part, no direct FP8 output: the 8-wave kernel
+  // whose wave pairs trade their weights.
+  if (a.h_q == 64 && cs == 1 && !fp8_direct) {
+    if (kv_fp8)
+      hipLaunchKernelGGL((decode_kernel8p<true, DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices,
+                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
+    else
+      hipLaunchKernelGGL((decode_kernel8p<false, DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices,
+                         a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
     return hipGetLastError();
   }
   // 64 heads in two parts: head halves that do not repeat QK^T.
@@ -2425,8 +2488,8 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
 #undef SMLA_LAUNCH_4T
     return hipGetLastError();
   }
-  // One part otherwise (64 heads of an FP8 pool, or a direct FP8 output): the
-  // 4-wave kernel over every head and column.
+  // One part otherwise (a direct FP8 output): the 4-wave kernel over every
+  // head and column.
   if (cs != 1) return hipErrorInvalidValue;
   if (kv_fp8)
     hipLaunchKernelGGL((decode_kernel<true, DIRECT, PREFETCH>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
@@ -2441,7 +2504,7 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
 // units, the last round would leave CUs idle: when it holds at most half of
 // them, its jobs take 2, 4 or 8 parts (the largest that keeps it within one
 // round; 4 at most for 16 heads), so it finishes sooner -- in the same launch
-// for a bf16 pool and 64 heads (decode_kernel8m), else in a second one.  A
+// for 64 heads (decode_kernel8m), else in a second one.  A
 // direct FP8 output keeps one part (its scale needs every column).
 template <bool DIRECT, bool PREFETCH>
 hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream) {
@@ -2451,10 +2514,14 @@ hipError_t launch_decode_cs(const DecodeArgs& a, bool kv_fp8, hipStream_t stream
   if (a.col_parts == 1 && n_jobs > cus && tail > 0 && 2 * tail <= cus && !(DIRECT && a.out_dtype == kOutFp8)) {
     const int cs_tail = min(8 * tail <= cus ? 8 : 4 * tail <= cus ? 4 : 2, 4 * (a.h_q / 16));
     const int n_head = n_jobs - tail;
-    if (a.h_q == 64 && !kv_fp8 && n_head % 8 == 0) {     // both bodies in one launch, the tail in 2 parts
+    if (a.h_q == 64 && n_head % 8 == 0) {     // both bodies in one launch, the tail in 2 parts
       const dim3 grid((unsigned)(n_head + (tail + 7) / 8 * 8 * 2));
-      hipLaunchKernelGGL((decode_kernel8m<DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices, a.q,
-                         a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, n_head, a);
+      if (kv_fp8)
+        hipLaunchKernelGGL((decode_kernel8m<true, DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices,
+                           a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, n_head, a);
+      else
+        hipLaunchKernelGGL((decode_kernel8m<false, DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices,
+                           a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, n_head, a);
       return hipGetLastError();
     }
     const hipError_t e = launch_jobs<DIRECT, PREFETCH>(a, kv_fp8, 1, 0, n_jobs - tail, stream);

@@ -201,6 +201,24 @@ def test_fewer_heads_every_part_count(h_q, s_q, S, kv_dtype):
     H.assert_o_close(res["O"], O_fin, rel=2.0 ** -8)
 
 
+@pytest.mark.parametrize("s_q,S", [(160, 1), (300, 1), (90, 2)])
+def test_fp8_pool_large_batch_every_token(s_q, S):
+    """An FP8 pool in one part a job (the 8-wave paired workgroups), alone (s_q = 160,
+    direct; 90 x 2 splits) and with a short last round in head halves in the same
+    launch (s_q = 300, direct), every token against the oracle."""
+    print(f"[case] fp8 s_q={s_q} S={S}", flush=True)
+    inp = W.make_inputs(s_q, 64, 131072, 640, seed=51 + s_q, kv_dtype="fp8", sink=True, pad="random")
+    dev = H.DeviceInputs(inp)
+    O_ref, L_ref = oracle.attend(inp.q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    path = "direct" if S == 1 else "split"
+    res = H.run(dev, S, "f32", path)
+    H.assert_o_close(res["O"], O_fin)
+    H.assert_lse_close(res["lse"], L_ref)
+    res = H.run(dev, S, "bf16", path)
+    H.assert_o_close(res["O"], O_fin, rel=2.0 ** -8)
+
+
 def test_score_far_beyond_the_frame_restarts_the_job():
     """A late slot whose log2-unit score exceeds the head's frame (fixed by the
     first block) by far more than the 64-unit slack: the kernel re-runs the job
