@@ -660,10 +660,9 @@ def pmc_summary(dirs):
 
 def kernel_label(s_q, S, pool, cus=256):
     """Which attention kernel(s) a launch runs (mirrors sparse_mla_decode's choice for 64
-    heads): the head-tile kernel at 4, 8 or 16 parts, the head-half kernel at 2; with one part,
-    the paired 8-wave kernel (bf16 pool) or the 4-wave kernel (FP8 pool); a last round
-    that would fill at most half of the CUs takes more column parts, in the same launch
-    (bf16 pool: the mixed kernel) or a second one."""
+    heads): the head-tile kernel at 4, 8 or 16 parts, the head-half kernel at 2, the paired
+    8-wave kernel at one part; a last round that would fill at most half of the CUs takes
+    two head halves in the same launch (the mixed kernel)."""
     jobs = s_q * S
     cs = 16 if 16 * jobs <= cus else 8 if 8 * jobs <= cus else 4 if 4 * jobs <= cus else 2 if 2 * jobs <= cus else 1
     mode = "partial" if S > 1 else "direct"
@@ -674,16 +673,12 @@ def kernel_label(s_q, S, pool, cus=256):
             return f"decode_kernel4t<{pool} pool, {mode}, {c} parts: head tiles{cols}>"
         if c == 2:
             return f"decode_kernel8h<{pool} pool, {mode}, 2 head halves>"
-        name = "decode_kernel8p" if pool == "bf16" else "decode_kernel"
-        return f"{name}<{pool} pool, {mode}, 1 column part>"
+        return f"decode_kernel8p<{pool} pool, {mode}, 1 column part>"
 
     tail = jobs % cus
-    if cs == 1 and jobs > cus and 0 < tail and 2 * tail <= cus:
-        ct = 8 if 8 * tail <= cus else 4 if 4 * tail <= cus else 2
-        if pool == "bf16" and (jobs - tail) % 8 == 0:
-            return (f"decode_kernel8m<bf16 pool, {mode}: decode_kernel8p's body over {jobs - tail} jobs, "
-                    f"decode_kernel8h's in 2 head halves over the last {tail}>")
-        return f"{one(1)} over {jobs - tail} jobs + {one(ct)} over the last {tail}"
+    if cs == 1 and jobs > cus and 0 < tail and 2 * tail <= cus and (jobs - tail) % 8 == 0:
+        return (f"decode_kernel8m<{pool} pool, {mode}: decode_kernel8p's body over {jobs - tail} jobs, "
+                f"decode_kernel8h's in 2 head halves over the last {tail}>")
     return one(cs)
 
 

@@ -8,7 +8,9 @@
 // the remainder on the leading splits; an empty split is O = 0, LSE = -inf).
 //
 // Kernels, by launch (CS = workgroups a job takes):
-//   * decode_kernel8p (64 heads, CS = 1): 8 waves, all heads and columns.
+//   * decode_kernel8p (CS = 1: 64 heads, or a direct FP8 output, whose scale
+//     needs every head and column of a token; fewer heads are then padded to
+//     64): 8 waves, all heads and columns.
 //   * decode_kernel8h (64 heads, CS = 2): 8 waves, half of the heads each.
 //   * decode_kernel4t (CS = h_q / 16 head tiles x 1, 2 or 4 column parts): 4
 //     waves, one 16-head tile each (and a half or a quarter of its columns).
@@ -16,32 +18,29 @@
 //     parts.
 //   * decode_kernel8m: a mixed launch for more jobs than compute units
 //     (decode_kernel8p's body, then decode_kernel8h's for a short last round).
-//   * decode_kernel (a direct FP8 output, whose scale needs every head and
-//     column of a token: CS = 1): 4 waves, all heads and columns.
-// The notes below describe decode_kernel; the others share its tile layout,
-// gather, softmax frame and partial protocol.
-//
-// decode kernel: one workgroup of 4 wave64s per (token, split) job.
+// What they share:
 //   * The 64 slots of a KV block share one LDS tile, gathered by index with
 //     16-byte direct-to-LDS loads (global_load_lds_dwordx4) in which 8 lanes
 //     fetch one contiguous 128-byte segment of a row (FP8 pool: 4 lanes a
 //     64-byte segment of e4m3 codes, converted to bf16 in registers as the
-//     MFMA operands are read); two tiles double-buffer
-//     the gather of block b+1 behind the compute of block b, its DMAs spread
-//     over block b's QK^T MFMAs.  Masked slots are never read: their tile
-//     rows are zero-filled, or copied from a zero row.
-//   * Wave w owns heads [16w, 16w+16) end to end, so the waves share nothing
-//     but the tile (one barrier per block).  S^T[slot][head] = K . Q^T and
-//     O^T[col][head] = V^T . P^T use v_mfma_f32_16x16x32_bf16; every lane
-//     holds one head's scores and accumulators.  Q is staged through LDS and
-//     kept in VGPRs (72 per lane); V^T is read from the row-major tile with
-//     the gfx950 transpose load ds_read_b64_tr_b16.  A block runs as two
-//     32-slot halves so that the softmax of one half is issued between the
-//     MFMAs of the other.
-//   * Softmax in log2 units against an integer frame M per head: each weight
-//     is p = 2^(t - M), one v_exp_f32.  M is the floor of the head's first
-//     non-empty half-block maximum and never moves inside a pass, so the
-//     accumulators are touched by MFMAs only (they stay in AGPRs).  A
+//     MFMA operands are read); two tiles double-buffer the gather of block
+//     b+1 behind the compute of block b, its DMAs spread over block b's QK^T
+//     MFMAs.  Masked slots are never read: their tile rows are copied from a
+//     zero row.
+//   * S^T[slot][head] = K . Q^T and O^T[col][head] = V^T . P^T use
+//     v_mfma_f32_16x16x32_bf16; every lane holds one head's scores and
+//     accumulators.  Q is staged through LDS and kept in VGPRs (72 per lane);
+//     V^T is read from the row-major tile with the gfx950 transpose load
+//     ds_read_b64_tr_b16.
+//   * The waves that share a head tile score a part of each block's slots
+//     each, trade their bf16 weights through LDS and accumulate every slot
+//     into their own part of the columns; the two waves of a SIMD in the
+//     8-wave kernels score different slots, so the hardware overlaps one's
+//     softmax and LDS reads with the other's MFMAs.
+//   * Softmax in log2 units against an integer frame M per head, shared by
+//     the waves of the head: each weight is p = 2^(t - M), one v_exp_f32.  M
+//     is the floor of the head's first non-empty block maximum and never
+//     moves inside a pass, so the accumulators are touched by MFMAs only.  A
 //     later score above M + 64 would risk overflow: the job then runs once
 //     more with M = floor of the largest score seen, which bounds every p by
 //     2.  The denominator sums the unrounded fp32 weights.
@@ -50,15 +49,9 @@
 //     leaves O errors near 4e-3 when a few slots dominate (one 64-slot block);
 //     hi + lo carries p to about 2^-17 relative.
 //   * Outputs are staged through LDS and stored in whole-line pieces.
-//
-// decode_kernel8p / 8h / 4t: the waves that share a head tile score a part
-// of each block's slots each, trade their bf16 weights through LDS and
-// accumulate every slot into their own part of the columns, under one
-// shared frame per head; the two waves of a SIMD in the 8-wave kernels
-// score different slots, so the hardware overlaps one's softmax and LDS
-// reads with the other's MFMAs.  With more jobs than compute units, a last
-// round that fills at most half of them takes 2, 4 or 8 parts (64 heads: 2,
-// in the same launch, decode_kernel8m).
+//   * With more jobs than compute units, a last round that fills at most half
+//     of them takes 2, 4 or 8 parts (64 heads: 2, in the same launch,
+//     decode_kernel8m).
 //
 // combine kernel: split-major partials -> final output (+ sink, cast).
 
@@ -219,37 +212,11 @@ __device__ __forceinline__ void dma_quartets(const void* gptr, uint32_t lds_base
       : "memory");
 }
 // First index of a job and its Q rows in one block: the index load is issued,
-// then the 2 x 9 Q-row DMAs of this wave (two groups of 8 rows, as a KV
-// gather), and only the index is waited for (vmcnt counts completions in issue
-// order, so the 18 DMAs stay in flight).  One asm statement, so that the
-// compiler neither reads the index register before it has landed nor adds a
-// wait of its own that would cover the DMAs.
-__device__ __forceinline__ int load_idx_and_q(const int32_t* idx_ptr, const void* q0, const void* q1,
-                                              uint32_t lds0_uniform, uint32_t lds1_uniform) {
-  int idx;
-  uint32_t saved;
-  asm volatile(
-      "global_load_dword %0, %2, off\n\t"
-      "s_mov_b32 %1, m0\n\t"
-      "s_mov_b32 m0, %5\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, off\n\t"
-      SMLA_DMA_OP(3, 8064, 128) SMLA_DMA_OP(3, 8064, 256) SMLA_DMA_OP(3, 8064, 384) SMLA_DMA_OP(3, 8064, 512)
-      SMLA_DMA_OP(3, 8064, 640) SMLA_DMA_OP(3, 8064, 768) SMLA_DMA_OP(3, 8064, 896) SMLA_DMA_OP(3, 8064, 1024)
-      "s_mov_b32 m0, %6\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, off\n\t"
-      SMLA_DMA_OP(4, 8064, 128) SMLA_DMA_OP(4, 8064, 256) SMLA_DMA_OP(4, 8064, 384) SMLA_DMA_OP(4, 8064, 512)
-      SMLA_DMA_OP(4, 8064, 640) SMLA_DMA_OP(4, 8064, 768) SMLA_DMA_OP(4, 8064, 896) SMLA_DMA_OP(4, 8064, 1024)
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_waitcnt vmcnt(18)"
-      : "=&v"(idx), "=&s"(saved)
-      : "v"(idx_ptr), "v"(q0), "v"(q1), "s"(lds0_uniform), "s"(lds1_uniform)
-      : "memory");
-  return idx;
-}
-// The same for one group of 8 Q rows (the 8-wave kernel: 9 DMAs per wave).
+// then the 9 DMAs of this wave's 8 Q rows (as a KV gather), and only the index
+// is waited for (vmcnt counts completions in issue order, so the 9 DMAs stay
+// in flight).  One asm statement, so that the compiler neither reads the index
+// register before it has landed nor adds a wait of its own that would cover
+// the DMAs.
 __device__ __forceinline__ int load_idx_and_q1(const int32_t* idx_ptr, const void* q0, uint32_t lds0_uniform) {
   int idx;
   uint32_t saved;
@@ -272,11 +239,6 @@ __device__ __forceinline__ int load_idx_and_q1(const int32_t* idx_ptr, const voi
 #undef SMLA_DMA
 #undef SMLA_DMA_OP
 
-__device__ __forceinline__ float warp_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
 
 // e4m3fn code of a finite fp32 value, round to nearest even, saturating at
 // +-448, sign kept (also for values that round to zero).
@@ -341,488 +303,15 @@ __device__ __forceinline__ Job decode_job(int block, int lg_parts, int num_split
 }
 
 // ---------------------------------------------------------------------------
-// The attention kernel.  KV_FP8: pool rows are e4m3 codes + a row scale.
-// DIRECT: single-split job writing the final output (sink + cast fused).
+// The attention kernels' template flags.  KV_FP8: pool rows are e4m3 codes +
+// a row scale.  DIRECT: single-split job writing the final output (sink +
+// cast fused).  PREFETCH: some job has more than one block, so each block
+// gathers the next one (for a job's last block the gather copies the zero row
+// into the idle buffer, keeping the loop free of branches).  The fields that
+// the first instructions need come as leading scalar arguments, which the
+// build asks to be preloaded into SGPRs at wave launch: the index and Q loads
+// then issue without waiting for a kernel-argument load.
 // ---------------------------------------------------------------------------
-// PREFETCH: some job has more than one block, so each block gathers the next
-// one (for a job's last block the gather copies the zero row into the idle
-// buffer, keeping the loop free of branches).
-// The fields that the first instructions need come as leading scalar
-// arguments, which the build asks to be preloaded into SGPRs at wave launch:
-// the index and Q loads then issue without waiting for a kernel-argument load.
-template <bool KV_FP8, bool DIRECT, bool PREFETCH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(
-    const int32_t* __restrict__ indices, const uint16_t* __restrict__ q_ptr, int32_t num_splits, int32_t n_blocks,
-    int32_t s_q, int32_t topk, int32_t h_q, int32_t job0, DecodeArgs a) {
-  constexpr int kCt = 32;                         // column tiles of 16: all 512 columns
-  constexpr int kCols = 512;
-  constexpr int kStagePitch = kCols * 4 + 16;     // LDS pitch of a staged fp32 output row
-  // bf16 pool: two tiles.  FP8 pool: two code tiles + one bf16 tile.
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2 * kTileBytes];
-  __shared__ __attribute__((aligned(16))) float s_scale[2][kBlk];
-  __shared__ __attribute__((aligned(16))) float s_bias[2][kBlk];   // 0: valid slot, kMaskedScore: masked
-  __shared__ float s_red[kWaves];
-  __shared__ int s_restart;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int hl = lane & 15;               // head within the wave (MFMA column)
-  const int G = lane >> 4;                // k-group of the 16x16x32 operand layout
-  const int head = 16 * wave + hl;
-
-  const Job job = decode_job((int)blockIdx.x, 0, num_splits, n_blocks, job0, s_q * num_splits);
-  if (!job.live) return;
-  const int t = job.t;
-  const int32_t* idx_row = indices + (int64_t)t * topk;
-
-  float M_run = kNoFrame;             // integer frame of this lane's head (log2 units)
-  float m_seen = kMaskedScore;        // largest score seen so far
-  float l_run = 0.f;                  // this lane's share of the denominator
-  if (tid == 0) s_restart = 0;        // ordered before its readers by the loop barriers
-  bool restarted = false;
-  f32x4 acc[kCt];                     // O^T: column tile ct -> columns 16ct + 4G + i
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (job.b0 < job.b1) {
-    // Lane l holds the index of slot l of a block.  The load address is clamped
-    // into the token's list so that it is issued unconditionally (no divergent
-    // branch, hence no early wait on it); slots past the split or the list are
-    // masked where the index is used.
-    auto load_idx = [&](int b) -> int {
-      return idx_row[min(b * kBlk + lane, topk - 1)];
-    };
-    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
-    auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
-    const float scale_log2 = a.scale_log2;
-    // Q fragments (B operand of S^T = K . Q^T): head, dims 32ks + 8G .. +8.
-    bf16x8 qf[18];
-
-    const uint32_t tile_lds0 = lds_addr(s_tile);
-    constexpr int kBufBytes = KV_FP8 ? kCodeTileBytes : kTileBytes;
-
-    // Gather a job's first block into buffer `buf` in one burst (nothing to
-    // overlap it with yet).  bf16: wave w fills rows [16w, 16w+16) as two
-    // groups of 8 rows; lane l gathers rows 16w + (l >> 3) and
-    // 16w + 8 + (l >> 3), chunk (l & 7) ^ (row & 7) of each octet.  FP8: wave w
-    // fills rows [16w, 16w+16); lane l gathers row 16w + (l >> 2), chunk l & 3
-    // of each quartet.  Masked rows are zero-filled.
-    auto issue_gather = [&](int idx_lane, int buf) {
-      if (!KV_FP8) {
-#pragma unroll
-        for (int hgrp = 0; hgrp < 2; ++hgrp) {
-          const int rg = 2 * wave + hgrp;                  // group of 8 rows
-          const int row_idx = __shfl(idx_lane, 8 * rg + (lane >> 3));
-          const uint32_t lds_base = tile_lds0 + buf * kBufBytes + rg * 1024;
-          if (valid_of(row_idx)) {
-            const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + (((lane & 7) ^ rsw(lane >> 3)) * 16);
-            dma_octets(src, __builtin_amdgcn_readfirstlane(lds_base));
-          } else {
-            uint8_t* dst = s_tile + buf * kBufBytes + rg * 1024 + lane * 16;
-#pragma unroll
-            for (int o = 0; o < 9; ++o) *(u32x4*)(dst + 8192 * o) = u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-      } else {
-        const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
-        const uint32_t lds_base = tile_lds0 + buf * kBufBytes + wave * 1024;
-        if (valid_of(row_idx)) {
-          const uint8_t* src = a.kv + (int64_t)row_idx * a.row_stride_bytes + fp8_gather_chunk(lane);
-          dma_quartets(src, __builtin_amdgcn_readfirstlane(lds_base));
-        } else {
-          uint8_t* dst = s_tile + buf * kBufBytes + wave * 1024 + lane * 16;
-#pragma unroll
-          for (int q = 0; q < 9; ++q) *(u32x4*)(dst + 4096 * q) = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    };
-
-    // per-lane LDS byte offsets of the operand reads (see the layout above)
-    const int sw_k = rsw(hl);
-    const int kb0 = hl * 128 + ((G ^ sw_k) * 16);              // K chunk 4ks + G, ks even
-    const int kb1 = hl * 128 + (((4 + G) ^ sw_k) * 16);        // ks odd
-    const Fp8Offsets f8 = fp8_offsets(lane);                  // FP8 pool: K and V^T reads of the codes
-    const int sw_v = rsw(4 * G + ((lane >> 2) & 3));
-    const int vrow = (4 * G + ((lane >> 2) & 3)) * 128 + (lane & 1) * 8;
-    int vb[4];                                                  // column tile ct & 3
-#pragma unroll
-    for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
-
-    // ---- prologue -----------------------------------------------------------
-    // Q rows are copied into LDS (at kQOffset, a region the first block does not
-    // use) by the same 128-byte-per-row DMA as a KV gather, rows = heads, and
-    // read back in operand order: whole-line requests instead of 64-byte
-    // pieces of 16 rows per load.  Rows of heads >= h_q copy head 0 (their
-    // results are never stored).  The first block's index is waited for alone.
-    int idx_cur;
-    {
-      const int r0 = 16 * wave + (lane >> 3), r1 = r0 + 8;
-      const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
-      const uint8_t* qbase = (const uint8_t*)(q_ptr + (int64_t)t * h_q * 576);
-      idx_cur = load_idx_and_q(idx_row + min(job.b0 * kBlk + lane, topk - 1),
-                               qbase + (int64_t)(r0 < h_q ? r0 : 0) * 1152 + chunk,
-                               qbase + (int64_t)(r1 < h_q ? r1 : 0) * 1152 + chunk,
-                               __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + (2 * wave) * 1024),
-                               __builtin_amdgcn_readfirstlane(tile_lds0 + kQOffset + (2 * wave + 1) * 1024));
-    }
-
-    // One pass over the job's blocks; returns whether a score left the frame.
-    // Inlined twice (first pass, rare restart) rather than looped, so that the
-    // first pass's prologue shares no wait counts with a loop back edge.
-    auto run_pass = [&](const bool first) __attribute__((always_inline)) -> bool {
-    bool overflow = false;
-    if (!first) idx_cur = load_idx(job.b0);
-    // block b0 in flight; the next block's indices are requested behind it
-    idx_cur = slot_in(job.b0) ? idx_cur : -1;
-    issue_gather(idx_cur, 0);
-    int idx_nxt = load_idx(job.b0 + 1);
-    bool valid_cur = valid_of(idx_cur);
-    float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
-    if (first) {
-      wait_vmem_all();        // Q rows (and block b0) have landed
-      lds_barrier();
-      const uint32_t qt = lds_addr(s_tile) + kQOffset + wave * 2048;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
-        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
-      }
-      // The first iteration's barrier orders these reads before the block b0+1
-      // prefetch overwrites the Q rows.
-    }
-
-    for (int b = job.b0; b < job.b1; ++b) {
-      const int cur = (b - job.b0) & 1;
-      wait_vmem_all();          // this wave's share of block b has landed
-      if (wave == 0) {
-        s_bias[cur][lane] = valid_cur ? 0.f : kMaskedScore;
-        if (KV_FP8) s_scale[cur][lane] = sc_cur;
-      }
-      lds_barrier();            // ... and every wave's; block b-1 fully consumed
-
-      // Block b+1 (indices loaded one block ahead) is gathered one DMA at a
-      // time between the MFMAs of block b's QK^T (see qk_half): a burst of 18
-      // stalls at issue when the memory pipeline is busy, and the MFMAs
-      // queued before each DMA keep running meanwhile.  Masked rows (and
-      // every row past the job's last block) copy the zero row.
-      bool valid_nxt = false;
-      float sc_nxt = 0.f;
-      const uint8_t* gsrc[2] = {g_zero_row, g_zero_row};
-      uint32_t gbase[2] = {0u, 0u};
-      if (PREFETCH) {
-        idx_nxt = slot_in(b + 1) ? idx_nxt : -1;
-        valid_nxt = valid_of(idx_nxt);
-        if (KV_FP8 && wave == 0 && valid_nxt) sc_nxt = a.kv_scale[idx_nxt];
-        if (!KV_FP8) {
-#pragma unroll
-          for (int hgrp = 0; hgrp < 2; ++hgrp) {
-            const int rg = 2 * wave + hgrp;
-            const int row_idx = __shfl(idx_nxt, 8 * rg + (lane >> 3));
-            gsrc[hgrp] = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-                         (((lane & 7) ^ rsw(lane >> 3)) * 16);
-            gbase[hgrp] = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + rg * 1024);
-          }
-        } else {
-          const int row_idx = __shfl(idx_nxt, 16 * wave + (lane >> 2));
-          gsrc[0] = (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-                    fp8_gather_chunk(lane);
-          gbase[0] = __builtin_amdgcn_readfirstlane(tile_lds0 + (cur ^ 1) * kBufBytes + wave * 1024);
-        }
-      }
-      // DMA d of the next block: bf16 d = 0..17 (row group d / 9, octet d % 9);
-      // FP8 d = 0..8 (quartet d).
-      auto gather_dma = [&](const int d) __attribute__((always_inline)) {
-        if (!PREFETCH) return;
-        const int g = KV_FP8 ? 0 : d / 9, o = KV_FP8 ? d : d % 9;
-        constexpr int L = KV_FP8 ? 4096 : 8192, Gs = KV_FP8 ? 64 : 128;
-        switch (o) {
-          case 0: dma_one<L, Gs, 0>(gsrc[g], gbase[g]); break;
-          case 1: dma_one<L, Gs, 1>(gsrc[g], gbase[g]); break;
-          case 2: dma_one<L, Gs, 2>(gsrc[g], gbase[g]); break;
-          case 3: dma_one<L, Gs, 3>(gsrc[g], gbase[g]); break;
-          case 4: dma_one<L, Gs, 4>(gsrc[g], gbase[g]); break;
-          case 5: dma_one<L, Gs, 5>(gsrc[g], gbase[g]); break;
-          case 6: dma_one<L, Gs, 6>(gsrc[g], gbase[g]); break;
-          case 7: dma_one<L, Gs, 7>(gsrc[g], gbase[g]); break;
-          default: dma_one<L, Gs, 8>(gsrc[g], gbase[g]); break;
-        }
-      };
-      constexpr int kDmas = KV_FP8 ? 9 : 18;
-      const int idx_after = load_idx(b + 2);
-
-      // The block is processed as two halves of 32 slots (slot tiles 0-1 and
-      // 2-3).  The softmax of one half is independent of the MFMAs that run
-      // next to it, so its VALU work is issued in small steps between them:
-      //   QK(h0) | QK(h1) + softmax(h0) | PV(h0) + softmax(h1) | PV(h1)
-      // The first half with a valid slot fixes a head's frame.
-      const uint32_t tl = lds_addr(s_tile + cur * kBufBytes);
-      // four bases keep every offset within the 16-bit ds_read field
-      uint32_t kbase[4], vbase[4];
-      // V^T: 4 column tiles per 128-byte octet (bf16) or per 64-byte quartet
-      // (FP8 codes)
-      if constexpr (KV_FP8) {
-        kbase[0] = opaque(tl + f8.k[0]);
-        kbase[1] = opaque(tl + f8.k[1]);
-        kbase[2] = kbase[3] = 0u;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tl + f8.v[m]);
-      } else {
-        kbase[0] = opaque(tl + kb0);
-        kbase[1] = opaque(tl + kb1);
-        kbase[2] = opaque(tl + kb0 + 65536);
-        kbase[3] = opaque(tl + kb1 + 65536);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) vbase[m] = opaque(tl + vb[m]);
-      }
-      auto kfrag = [&](int ks, int st) -> bf16x8 {
-        if constexpr (KV_FP8) return fp8_kfrag(kbase[ks & 1] + (ks >> 1) * 4096 + st * 1024);
-        const uint32_t kp = kbase[(ks & 1) + (ks >= 16 ? 2 : 0)] + ((ks >> 1) & 7) * 8192 + st * 2048;
-        return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)kp;
-      };
-      auto vfrag = [&](int ct, int kk) -> bf16x8 {
-        if constexpr (KV_FP8) return fp8_vfrag(vbase[ct & 3] + (ct >> 2) * 4096 + kk * 2048);
-        const uint32_t vp = vbase[ct & 3] + (ct >> 2) * 8192 + kk * 4096;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)vp);
-        const i16x4 v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)(vp + 2048));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, v0);
-        const u32x2 w1 = __builtin_bit_cast(u32x2, v1);
-        return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-      };
-
-      // bias (and FP8 row scale) of this lane's 16 slots: slots 16st + 4G + i
-      f32x4 bias[4], rsc[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        bias[st] = *(const f32x4*)&s_bias[cur][16 * st + 4 * G];
-        if (KV_FP8) rsc[st] = *(const f32x4*)&s_scale[cur][16 * st + 4 * G];
-      }
-
-      f32x4 sacc[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      // Softmax of half hh in 15 steps (called with constant hh and k):
-      //   0: scores (log2 units, masked slots at kMaskedScore)   1-2: head max, frame
-      //   3-10: one weight each (2^(t - M), p = 0 for a masked slot or a head
-      //   without a frame)   11-14: one bf16 hi/lo pair each.
-      float tv[2][8], pv[2][8], mh[2];
-      uint32_t ph[2][4], pl[2][4];
-      auto sm_step = [&](const int hh, const int k) __attribute__((always_inline)) {
-        if (k == 0) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int st = 2 * hh + (e >> 2), i = e & 3;
-            tv[hh][e] = KV_FP8 ? fmaf(sacc[st][i] * scale_log2, rsc[st][i], bias[st][i])
-                               : fmaf(sacc[st][i], scale_log2, bias[st][i]);
-          }
-        } else if (k == 1) {
-          float m = fmaxf(fmaxf(fmaxf(tv[hh][0], tv[hh][1]), fmaxf(tv[hh][2], tv[hh][3])),
-                          fmaxf(fmaxf(tv[hh][4], tv[hh][5]), fmaxf(tv[hh][6], tv[hh][7])));
-          auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-          mh[hh] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        } else if (k == 2) {
-          auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mh[hh]), __float_as_uint(mh[hh]), false, false);
-          const float m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-          m_seen = fmaxf(m_seen, m);
-          if (M_run == kNoFrame && m > kMaskedScore) M_run = floorf(m);
-          overflow |= m > M_run + kFrameSlack;
-        } else if (k <= 10) {
-          const int e = k - 3;
-          const float tt = tv[hh][e];
-          float p = __builtin_amdgcn_exp2f(tt - M_run);
-          l_run += p;
-          if (KV_FP8) p *= rsc[2 * hh + (e >> 2)][e & 3];
-          pv[hh][e] = p;
-        } else {
-          const int j = k - 11;
-          const uint32_t h2 = pack_bf16x2(pv[hh][2 * j], pv[hh][2 * j + 1]);
-          ph[hh][j] = h2;
-          pl[hh][j] = pack_bf16x2(pv[hh][2 * j] - __uint_as_float(h2 << 16),
-                                  pv[hh][2 * j + 1] - __uint_as_float(h2 & 0xFFFF0000u));
-        }
-      };
-      // step of the softmax placed after MFMA group g (-1: none)
-      auto sm_at = [](int g) -> int { return (g >= 1 && g <= 15) ? g - 1 : -1; };
-
-      // ---- QK^T of one half: 2 slot tiles x 18 k-steps; the K fragments of
-      // k-step ks+kAheadK are requested before the MFMAs of ks.  hh = 1
-      // carries the softmax of half 0.
-      // MFMAs on one accumulator are issued back to back in pairs (k-steps
-      // 2j and 2j+1): on gfx950 alternating accumulators from one MFMA to the
-      // next measured about 21 cycles per 16x16x32 MFMA, pairs about 16.5.
-      constexpr int kAheadK = 4, kAheadV = 4, kRing = kAheadK + 2;
-      auto qk_half = [&](const int hh) __attribute__((always_inline)) {
-        bf16x8 kf[kRing][2];
-#pragma unroll
-        for (int a0 = 0; a0 < kAheadK; ++a0)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) kf[a0][u] = kfrag(a0, 2 * hh + u);
-#pragma unroll
-        for (int j = 0; j < 9; ++j) {
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int ka = 2 * j + e + kAheadK;
-            if (ka < 18) {
-#pragma unroll
-              for (int u = 0; u < 2; ++u) kf[ka % kRing][u] = kfrag(ka, 2 * hh + u);
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int ks = 2 * j + e;
-              sacc[2 * hh + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % kRing][u], qf[ks],
-                                                                         sacc[2 * hh + u], 0, 0, 0);
-            }
-            const int ks = 2 * j + u;              // the VALU / DMA slot of k-step ks
-            if (hh == 1 && sm_at(ks) >= 0) sm_step(0, sm_at(ks));
-            // the next block's gather: DMAs 0..8 in half 0, 9..17 in half 1
-            if (ks < 9 && 9 * hh + ks < kDmas) gather_dma(9 * hh + ks);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      };
-      // ---- O^T += V^T . P^T over one half (k-step kk): the kCt column tiles
-      // of this workgroup x (hi, lo); V^T fragments kAheadV column tiles
-      // ahead.  kk = 0 carries the softmax of half 1 (its 15 steps fit in the
-      // first 16 column tiles).
-      auto pv_half = [&](const int kk) __attribute__((always_inline)) {
-        const bf16x8 pfh = __builtin_bit_cast(bf16x8, u32x4{ph[kk][0], ph[kk][1], ph[kk][2], ph[kk][3]});
-        const bf16x8 pfl = __builtin_bit_cast(bf16x8, u32x4{pl[kk][0], pl[kk][1], pl[kk][2], pl[kk][3]});
-        bf16x8 vf[kAheadV + 1];
-#pragma unroll
-        for (int a0 = 0; a0 < kAheadV; ++a0) vf[a0] = vfrag(a0, kk);
-#pragma unroll
-        for (int ct = 0; ct < kCt; ++ct) {
-          if (ct + kAheadV < kCt) vf[(ct + kAheadV) % (kAheadV + 1)] = vfrag(ct + kAheadV, kk);
-          __builtin_amdgcn_sched_barrier(0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfh, acc[ct], 0, 0, 0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % (kAheadV + 1)], pfl, acc[ct], 0, 0, 0);
-          if (kk == 0 && sm_at(ct) >= 0) sm_step(1, sm_at(ct));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-
-      qk_half(0);
-      qk_half(1);      // + softmax(h0)
-      pv_half(0);      // + softmax(h1)
-      pv_half(1);
-
-      valid_cur = valid_nxt;
-      sc_cur = sc_nxt;
-      idx_nxt = idx_after;
-    }
-    wait_vmem_all();            // the last block's look-ahead gather lands before LDS is reused
-    return overflow;
-    };
-
-    const bool overflow = run_pass(true);
-    // A score beyond the frame anywhere in the workgroup: run the job again
-    // from zero with every head's frame at the largest score it has seen.
-    if (__any(overflow) && lane == 0) s_restart = 1;
-    lds_barrier();              // also: every wave is past its last tile read
-    if (s_restart != 0) {
-      restarted = true;
-      M_run = floorf(m_seen);   // a restart implies a valid score was seen
-      l_run = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      run_pass(false);
-    }
-  }
-
-  // ---- epilogue -------------------------------------------------------------
-  const float l_head = rows_sum(l_run);          // full denominator of this lane's head
-  const bool any = l_head > 0.f;
-  const float lse = any ? M_run + __builtin_amdgcn_logf(l_head) : kNegInf;
-  float oscale = any ? 1.0f / l_head : 0.f;
-  const bool wave_ok = 16 * wave < h_q;        // h_q is a multiple of 16
-  if (DIRECT && a.sink != nullptr && any && wave_ok) {
-    const float z = a.sink[head] * kLog2e - lse;
-    oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
-  }
-
-  // The scaled rows go through LDS so that each global store instruction
-  // writes whole lines of one or two rows (a lane's accumulators hold 4
-  // columns of each column tile, i.e. 64-byte pieces of 16 rows per store).
-  // Wave w stages its 16 heads x kCols fp32 at s_tile + w * 16 * kStagePitch;
-  // the 16-byte row padding keeps the 16-lane writes bank-conflict free.  A
-  // wave reads back only its own rows, and LDS keeps a wave's accesses in
-  // order, so no barrier is needed between the two.
-  if (restarted) lds_barrier();                  // a restarted pass ends with tiles in use
-  uint8_t* stg = s_tile + wave * 16 * kStagePitch;
-  float amax = 0.f;
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) {
-    const f32x4 v = acc[ct] * oscale;
-    if (DIRECT && wave_ok)
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-    *(f32x4*)(stg + hl * kStagePitch + 64 * ct + 16 * G) = v;
-  }
-  float qscale = 1.0f;
-  if (DIRECT && a.out_dtype == kOutFp8) {       // per-token amax over every head
-    amax = warp_max(amax);
-    if (lane == 0) s_red[wave] = amax;
-    lds_barrier();
-    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    qscale = amax > 0.f ? amax / 448.0f : 1.0f;
-    if (tid == 0) a.out_scale[t] = qscale;
-  }
-  if (wave_ok) {
-    const int64_t row0 = (DIRECT ? (int64_t)t * h_q : ((int64_t)job.s * s_q + t) * h_q) + 16 * wave;
-    if (!DIRECT || a.out_dtype == kOutF32) {     // 1 KB of whole row pieces per instruction
-      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512;
-#pragma unroll
-      for (int j = 0; j < 16 * kCols / 256; ++j) {
-        const int f = 256 * j + 4 * lane;          // float index in the wave's 16 x kCols block
-        const int r = f / kCols, c = f % kCols;
-        *(f32x4*)(dst + r * 512 + c) = *(const f32x4*)(stg + r * kStagePitch + 4 * c);
-      }
-    } else if (a.out_dtype == kOutBf16) {        // 1 KB (one or two row pieces) per instruction
-      constexpr int kLanesPerRow = kCols / 8, kRowsPer = 64 / kLanesPerRow;
-      const int rr = lane / kLanesPerRow, cc = 8 * (lane % kLanesPerRow);
-      uint16_t* dst = (uint16_t*)a.out + row0 * 512 + cc;
-#pragma unroll
-      for (int j = 0; j < 16 / kRowsPer; ++j) {
-        const int r = kRowsPer * j + rr;
-        const f32x4 v0 = *(const f32x4*)(stg + r * kStagePitch + 4 * cc);
-        const f32x4 v1 = *(const f32x4*)(stg + r * kStagePitch + 4 * cc + 16);
-        *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
-                                         pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
-      }
-    } else {                                     // e4m3: two 512 B rows per instruction
-      uint8_t* dst = (uint8_t*)a.out + row0 * 512;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int h = 2 * j + (lane >> 5);
-        const uint8_t* src = stg + h * kStagePitch + 64 * (lane & 31);
-        u32x4 w;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x4 v = *(const f32x4*)(src + 16 * k);
-          w[k] = e4m3_encode(v[0] / qscale) | (e4m3_encode(v[1] / qscale) << 8) |
-                 (e4m3_encode(v[2] / qscale) << 16) | (e4m3_encode(v[3] / qscale) << 24);
-        }
-        *(u32x4*)(dst + h * 512 + 16 * (lane & 31)) = w;
-      }
-    }
-    if (G == 0) {
-      if (!DIRECT)
-        a.lse_accum[row0 + hl] = lse;
-      else if (a.lse_out != nullptr)
-        a.lse_out[row0 + hl] = lse;
-    }
-  }
-  // Split jobs of a decode with an FP8 output: the combine's running amax per
-  // token starts from -0.0 (its "an amax, not yet a scale" form), stored here
-  // so that the combine needs no launch of its own for it.
-  if (!DIRECT && a.out_scale != nullptr && job.s == 0 && tid == 0)
-    seed_fp8_combine(a.out_scale, a.out, t, h_q);
-}
 
 // The 8-wave kernels below (two waves per SIMD): 64 heads, 512 threads.
 constexpr int kWaves8 = 8;
@@ -940,12 +429,14 @@ __device__ __forceinline__ void decode8p_body(
     for (int m = 0; m < 4; ++m) vb[m] = vrow + (((2 * m + ((lane & 3) >> 1)) ^ sw_v) * 16);
 
     // ---- prologue: Q rows (heads) [8w, 8w + 8) into LDS by wave w, at kQOff
+    // (rows of heads >= h_q copy head 0; their results are never stored)
     int idx_cur;
     {
       const int r0 = 8 * wave + (lane >> 3);
       const int chunk = ((lane & 7) ^ rsw(lane >> 3)) * 16;
       const uint8_t* qbase = (const uint8_t*)(q_ptr + (int64_t)t * h_q * 576);
-      idx_cur = load_idx_and_q1(idx_row + min(job.b0 * kBlk + lane, topk - 1), qbase + (int64_t)r0 * 1152 + chunk,
+      idx_cur = load_idx_and_q1(idx_row + min(job.b0 * kBlk + lane, topk - 1),
+                                qbase + (int64_t)(r0 < h_q ? r0 : 0) * 1152 + chunk,
                                 __builtin_amdgcn_readfirstlane(tile_lds0 + kQOff + wave * 1024));
     }
 
@@ -1205,16 +696,17 @@ __device__ __forceinline__ void decode8p_body(
   }
 
   // ---- epilogue: l = both halves' denominators (one frame), O = acc / l ----
+  const bool head_ok = head < h_q;                // fewer heads (a direct FP8 output): rows past h_q are padding
   const float l = l_run + l_par;
   const bool any = l > 0.f;
   const float lse = any ? M_run + __builtin_amdgcn_logf(l) : kNegInf;
   float oscale = any ? 1.0f / l : 0.f;
-  if (DIRECT && a.sink != nullptr && any) {
+  if (DIRECT && a.sink != nullptr && any && head_ok) {
     const float z = a.sink[head] * kLog2e - lse;
     oscale = oscale / (1.0f + __builtin_amdgcn_exp2f(z));
   }
   const int64_t rowt = DIRECT ? (int64_t)t * h_q : ((int64_t)job.s * s_q + t) * h_q;
-  if (sg == 0 && G == 0) {
+  if (sg == 0 && G == 0 && head_ok) {
     if (!DIRECT)
       a.lse_accum[rowt + head] = lse;
     else if (a.lse_out != nullptr)
@@ -1223,30 +715,68 @@ __device__ __forceinline__ void decode8p_body(
 
   // Staging (row = head, the tiles are free): wave (hq, sg) writes its 16
   // heads x 256 columns; after the barrier wave w stores heads [8w, 8w + 8)
-  // in whole rows.
+  // in whole rows.  A direct FP8 output takes the token's amax over every
+  // head and column on the way (through a word of the weight area that the
+  // end-of-pass exchange does not read).
+  const bool fp8_out = DIRECT && a.out_dtype == kOutFp8;
+  float* const s_red = (float*)(s_pex[0] + 1024);  // [kWaves8]
+  float amax = 0.f;
   {
     uint8_t* stg = s_tile + head * kStagePitch + (256 * sg + 4 * G) * 4;
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct) *(f32x4*)(stg + 64 * ct) = acc[ct] * oscale;
+    for (int ct = 0; ct < kCt; ++ct) {
+      const f32x4 v = acc[ct] * oscale;
+      if (fp8_out && head_ok)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      *(f32x4*)(stg + 64 * ct) = v;
+    }
+  }
+  if (fp8_out) {
+    amax = wave_max(amax);
+    if (lane == 0) s_red[wave] = amax;
   }
   lds_barrier();
+  float qscale = 1.0f;
+  if (fp8_out) {
+    amax = fmaxf(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])),
+                 fmaxf(fmaxf(s_red[4], s_red[5]), fmaxf(s_red[6], s_red[7])));
+    qscale = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (tid == 0) a.out_scale[t] = qscale;
+  }
   const uint8_t* st = s_tile + 8 * wave * kStagePitch;
   const int64_t row0 = rowt + 8 * wave;
-  if (!DIRECT || a.out_dtype == kOutF32) {       // 1 KB of one row per instruction
-    float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512;
+  if (8 * wave < h_q) {                          // (h_q is a multiple of 16)
+    if (!DIRECT || a.out_dtype == kOutF32) {     // 1 KB of one row per instruction
+      float* dst = (DIRECT ? (float*)a.out : a.o_accum) + row0 * 512;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = j >> 1, c = 256 * (j & 1) + 4 * lane;
-      *(f32x4*)(dst + r * 512 + c) = *(const f32x4*)(st + r * kStagePitch + 4 * c);
-    }
-  } else {                                       // bf16 (a direct FP8 output never takes this kernel)
-    uint16_t* dst = (uint16_t*)a.out + row0 * 512 + 8 * lane;
+      for (int j = 0; j < 16; ++j) {
+        const int r = j >> 1, c = 256 * (j & 1) + 4 * lane;
+        *(f32x4*)(dst + r * 512 + c) = *(const f32x4*)(st + r * kStagePitch + 4 * c);
+      }
+    } else if (a.out_dtype == kOutBf16) {        // 1 KB of one row per instruction
+      uint16_t* dst = (uint16_t*)a.out + row0 * 512 + 8 * lane;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const f32x4 v0 = *(const f32x4*)(st + r * kStagePitch + 32 * lane);
-      const f32x4 v1 = *(const f32x4*)(st + r * kStagePitch + 32 * lane + 16);
-      *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
-                                       pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+      for (int r = 0; r < 8; ++r) {
+        const f32x4 v0 = *(const f32x4*)(st + r * kStagePitch + 32 * lane);
+        const f32x4 v1 = *(const f32x4*)(st + r * kStagePitch + 32 * lane + 16);
+        *(u32x4*)(dst + r * 512) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                         pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+      }
+    } else {                                     // e4m3: two 512 B rows per instruction
+      uint8_t* dst = (uint8_t*)a.out + row0 * 512;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 2 * j + (lane >> 5);
+        const uint8_t* src = st + r * kStagePitch + 64 * (lane & 31);
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x4 v = *(const f32x4*)(src + 16 * k);
+          w[k] = e4m3_encode(v[0] / qscale) | (e4m3_encode(v[1] / qscale) << 8) |
+                 (e4m3_encode(v[2] / qscale) << 16) | (e4m3_encode(v[3] / qscale) << 24);
+        }
+        *(u32x4*)(dst + r * 512 + 16 * (lane & 31)) = w;
+      }
     }
   }
   // Split jobs of a decode with an FP8 output: seed the combine's amax and counters.
@@ -2444,9 +1974,10 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
   const dim3 grid(cs == 1 ? n_jobs : (n_jobs + 7) / 8 * 8 * cs);
   const int tiles = a.h_q / 16;
   const bool fp8_direct = DIRECT && a.out_dtype == kOutFp8;
-  // 64 heads in one column part, no direct FP8 output: the 8-wave kernel
-  // whose wave pairs trade their weights.
-  if (a.h_q == 64 && cs == 1 && !fp8_direct) {
+  // 64 heads in one column part, or a direct FP8 output (one part; fewer
+  // heads are padded to 64): the 8-wave kernel whose wave pairs trade their
+  // weights.
+  if (cs == 1 && (a.h_q == 64 || fp8_direct)) {
     if (kv_fp8)
       hipLaunchKernelGGL((decode_kernel8p<true, DIRECT, PREFETCH>), grid, dim3(kThreads8), 0, stream, a.indices,
                          a.q, a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
@@ -2488,16 +2019,7 @@ hipError_t launch_jobs(const DecodeArgs& a, bool kv_fp8, int cs, int job0, int j
 #undef SMLA_LAUNCH_4T
     return hipGetLastError();
   }
-  // One part otherwise (a direct FP8 output): the 4-wave kernel over every
-  // head and column.
-  if (cs != 1) return hipErrorInvalidValue;
-  if (kv_fp8)
-    hipLaunchKernelGGL((decode_kernel<true, DIRECT, PREFETCH>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
-                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<false, DIRECT, PREFETCH>), grid, dim3(kThreads), 0, stream, a.indices, a.q,
-                       a.num_splits, a.n_blocks, a.s_q, a.topk, a.h_q, job0, a);
-  return hipGetLastError();
+  return hipErrorInvalidValue;                  // no other part count is planned
 }
 
 // The whole launch plan.  With one column part and more jobs than compute

@@ -67,6 +67,16 @@ def test_random_large_batch_matches_oracle(i):
     _check(i, _case_large(i))
 
 
+@pytest.mark.parametrize("h_q,s_q,kv_dtype", [(16, 5, "bf16"), (32, 40, "fp8"), (64, 3, "fp8"), (16, 300, "fp8"),
+                                               (32, 260, "bf16"), (64, 300, "bf16")])
+def test_direct_fp8_output(h_q, s_q, kv_dtype):
+    """The direct path with an FP8 output (one workgroup a token, every head and column
+    for the token's scale; fewer heads padded), small and larger than the compute units."""
+    c = dict(s_q=s_q, h_q=h_q, topk=640, n_pool=20000, kv_dtype=kv_dtype, pad="random", sink=True, S=1,
+             path="direct", out="fp8", seed=7000 + s_q + h_q)
+    _check(f"fp8-direct-{h_q}-{s_q}", c)
+
+
 def _check(i, c):
     print(f"[case] {i}: {c}", flush=True)
     inp = W.make_inputs(c["s_q"], c["h_q"], c["n_pool"], c["topk"], c["seed"], kv_dtype=c["kv_dtype"],
