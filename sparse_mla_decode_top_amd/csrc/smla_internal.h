@@ -25,7 +25,7 @@ struct DecodeArgs {
   int32_t s_q, h_q, topk, num_splits, n_blocks;
   int32_t out_dtype;          // smla_out_dtype (direct mode)
   float scale_log2;           // softmax_scale * log2(e)
-  int32_t col_parts;          // workgroups per job: 1 to 16 for 64 heads; else (h_q / 16) x 1, 2 or 4 (head tiles x column parts)
+  int32_t col_parts;          // workgroups per job: 1 to 16 for 64 heads, else (h_q / 16) x 1, 2 or 4; 1 for a direct FP8 output
   int32_t cus;                // compute units of the device (the launch plan's round size)
 };
 
