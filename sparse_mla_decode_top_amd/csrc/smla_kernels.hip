@@ -302,6 +302,30 @@ __device__ __forceinline__ Job decode_job(int block, int lg_parts, int num_split
   return j;
 }
 
+// A job's index list: lane l holds slot l of a 64-slot block.  The load
+// address is clamped into the token's list so that it is issued
+// unconditionally (no divergent branch, hence no early wait on it); slots past
+// the split or the list are masked where the index is used, and so is an
+// index outside the pool.
+struct JobIndices {
+  const int32_t* row;                 // the token's top-k list
+  int topk, b1;                       // list length; end of the job's block range
+  int64_t n_pool;
+  __device__ __forceinline__ int load(int b, int lane) const { return row[min(b * kBlk + lane, topk - 1)]; }
+  __device__ __forceinline__ bool slot_in(int b, int lane) const { return b < b1 && b * kBlk + lane < topk; }
+  __device__ __forceinline__ bool valid(int idx) const { return idx >= 0 && (int64_t)idx < n_pool; }
+};
+
+// The global address a lane's gather DMAs start from: its piece of pool row
+// `row_idx`, or of the zero row when the row is masked.  bf16: 8 lanes a row,
+// chunk (l & 7) ^ (row & 7) of each 128-byte octet; FP8 codes: 4 lanes a row,
+// the quartet chunk of fp8_gather_chunk.
+template <bool KV_FP8>
+__device__ __forceinline__ const uint8_t* gather_src(const DecodeArgs& a, int row_idx, bool valid, int lane) {
+  return (valid ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
+         (KV_FP8 ? fp8_gather_chunk(lane) : (((lane & 7) ^ rsw(lane >> 3)) * 16));
+}
+
 // ---------------------------------------------------------------------------
 // The attention kernels' template flags.  KV_FP8: pool rows are e4m3 codes +
 // a row scale.  DIRECT: single-split job writing the final output (sink +
@@ -383,11 +407,10 @@ __device__ __forceinline__ void decode8p_body(
   for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (job.b0 < job.b1) {
-    auto load_idx = [&](int b) -> int {
-      return idx_row[min(b * kBlk + lane, topk - 1)];
-    };
-    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
-    auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
+    const JobIndices ji{idx_row, topk, job.b1, a.n_pool};
+    auto load_idx = [&](int b) -> int { return ji.load(b, lane); };
+    auto slot_in = [&](int b) -> bool { return ji.slot_in(b, lane); };
+    auto valid_of = [&](int idx) -> bool { return ji.valid(idx); };
     const float scale_log2 = a.scale_log2;
     bf16x8 qf[18];                    // Q fragments: head, dims 32ks + 8G .. +8
     const uint32_t tile_lds0 = lds_addr(s_tile);
@@ -400,13 +423,8 @@ __device__ __forceinline__ void decode8p_body(
     // first pass counts on it).
     const bool gathers = !KV_FP8 || wave < 4;
     auto row_src = [&](int idx_lane) -> const uint8_t* {
-      if (KV_FP8) {
-        const int row_idx = __shfl(idx_lane, 16 * (wave & 3) + (lane >> 2));
-        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + fp8_gather_chunk(lane);
-      }
-      const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
-      return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-             (((lane & 7) ^ rsw(lane >> 3)) * 16);
+      const int row_idx = __shfl(idx_lane, KV_FP8 ? 16 * (wave & 3) + (lane >> 2) : 8 * wave + (lane >> 3));
+      return gather_src<KV_FP8>(a, row_idx, valid_of(row_idx), lane);
     };
     auto issue_gather = [&](int idx_lane, int buf) {
       if (!KV_FP8) {
@@ -851,11 +869,10 @@ __device__ __forceinline__ void decode8h_body(
   for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (job.b0 < job.b1) {
-    auto load_idx = [&](int b) -> int {
-      return idx_row[min(b * kBlk + lane, topk - 1)];
-    };
-    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
-    auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
+    const JobIndices ji{idx_row, topk, job.b1, a.n_pool};
+    auto load_idx = [&](int b) -> int { return ji.load(b, lane); };
+    auto slot_in = [&](int b) -> bool { return ji.slot_in(b, lane); };
+    auto valid_of = [&](int idx) -> bool { return ji.valid(idx); };
     const float scale_log2 = a.scale_log2;
     bf16x8 qf[18];                    // Q fragments: head, dims 32ks + 8G .. +8
     const uint32_t tile_lds0 = lds_addr(s_tile);
@@ -866,13 +883,8 @@ __device__ __forceinline__ void decode8h_body(
     // a gathering wave, a masked row copying the zero row.
     const bool gathers = !KV_FP8 || wave < 4;
     auto row_src = [&](int idx_lane) -> const uint8_t* {
-      if (KV_FP8) {
-        const int row_idx = __shfl(idx_lane, 16 * (wave & 3) + (lane >> 2));
-        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + fp8_gather_chunk(lane);
-      }
-      const int row_idx = __shfl(idx_lane, 8 * wave + (lane >> 3));
-      return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-             (((lane & 7) ^ rsw(lane >> 3)) * 16);
+      const int row_idx = __shfl(idx_lane, KV_FP8 ? 16 * (wave & 3) + (lane >> 2) : 8 * wave + (lane >> 3));
+      return gather_src<KV_FP8>(a, row_idx, valid_of(row_idx), lane);
     };
     auto issue_gather = [&](int idx_lane, int buf) {
       if (!KV_FP8) {
@@ -1259,11 +1271,10 @@ __device__ __forceinline__ void decode4t_body(
   for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (job.b0 < job.b1) {
-    auto load_idx = [&](int b) -> int {
-      return idx_row[min(b * kBlk + lane, topk - 1)];
-    };
-    auto slot_in = [&](int b) -> bool { return b < job.b1 && b * kBlk + lane < topk; };
-    auto valid_of = [&](int idx) -> bool { return idx >= 0 && (int64_t)idx < a.n_pool; };
+    const JobIndices ji{idx_row, topk, job.b1, a.n_pool};
+    auto load_idx = [&](int b) -> int { return ji.load(b, lane); };
+    auto slot_in = [&](int b) -> bool { return ji.slot_in(b, lane); };
+    auto valid_of = [&](int idx) -> bool { return ji.valid(idx); };
     const float scale_log2 = a.scale_log2;
     bf16x8 qf[18];                    // Q fragments: head, dims 32ks + 8G .. +8
     const uint32_t tile_lds0 = lds_addr(s_tile);
@@ -1274,13 +1285,8 @@ __device__ __forceinline__ void decode4t_body(
     // of each octet), 18 DMAs a wave.  FP8: 4 lanes a row (chunk l & 3 of each
     // quartet), 9 DMAs a wave.
     auto row_src = [&](int idx_lane, int grp) -> const uint8_t* {
-      if (KV_FP8) {
-        const int row_idx = __shfl(idx_lane, 16 * wave + (lane >> 2));
-        return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) + fp8_gather_chunk(lane);
-      }
-      const int row_idx = __shfl(idx_lane, 16 * wave + 8 * grp + (lane >> 3));
-      return (valid_of(row_idx) ? a.kv + (int64_t)row_idx * a.row_stride_bytes : g_zero_row) +
-             (((lane & 7) ^ rsw(lane >> 3)) * 16);
+      const int row_idx = __shfl(idx_lane, KV_FP8 ? 16 * wave + (lane >> 2) : 16 * wave + 8 * grp + (lane >> 3));
+      return gather_src<KV_FP8>(a, row_idx, valid_of(row_idx), lane);
     };
     auto issue_gather = [&](int idx_lane, int buf) {
       if (KV_FP8) {
