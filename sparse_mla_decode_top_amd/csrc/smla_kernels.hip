@@ -326,6 +326,36 @@ __device__ __forceinline__ const uint8_t* gather_src(const DecodeArgs& a, int ro
          (KV_FP8 ? fp8_gather_chunk(lane) : (((lane & 7) ^ rsw(lane >> 3)) * 16));
 }
 
+// The first block's wait for this wave's Q rows, which were issued first:
+// vector memory operations complete in issue order, so the block's DMAS
+// gather DMAs and, with the look-ahead, the next index load stay in flight.
+template <bool PREFETCH, int DMAS>
+__device__ __forceinline__ void wait_q_rows() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMAS + (PREFETCH ? 1 : 0)) : "memory");
+}
+
+// A head tile's 18 Q fragments (B operand of S^T = K . Q^T: head, dims
+// 32 ks + 8 G .. +8) from the staged Q rows at LDS address qt, kb0 / kb1 being
+// the lane's offsets for even / odd k-steps.
+__device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[18], uint32_t qt, int kb0, int kb1) {
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
+    qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
+  }
+}
+
+// One block's gather in the 8-wave kernels, the lane's source from gather_src.
+// bf16: wave w fills rows [8w, 8w + 8) of the tile; FP8: waves 0-3 fill rows
+// [16w, 16w + 16) of the code tile.  9 DMAs a gathering wave.
+template <bool KV_FP8>
+__device__ __forceinline__ void gather_block8(const uint8_t* src, uint32_t tile_lds0, int buf, int wave) {
+  if (!KV_FP8)
+    dma_octets(src, __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kTileBytes + wave * 1024));
+  else if (wave < 4)
+    dma_quartets(src, __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kCodeTileBytes + wave * 1024));
+}
+
 // ---------------------------------------------------------------------------
 // The attention kernels' template flags.  KV_FP8: pool rows are e4m3 codes +
 // a row scale.  DIRECT: single-split job writing the final output (sink +
@@ -426,14 +456,7 @@ __device__ __forceinline__ void decode8p_body(
       const int row_idx = __shfl(idx_lane, KV_FP8 ? 16 * (wave & 3) + (lane >> 2) : 8 * wave + (lane >> 3));
       return gather_src<KV_FP8>(a, row_idx, valid_of(row_idx), lane);
     };
-    auto issue_gather = [&](int idx_lane, int buf) {
-      if (!KV_FP8) {
-        dma_octets(row_src(idx_lane), __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kTileBytes + wave * 1024));
-      } else if (gathers) {
-        dma_quartets(row_src(idx_lane),
-                     __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kCodeTileBytes + wave * 1024));
-      }
-    };
+    auto issue_gather = [&](int idx_lane, int buf) { gather_block8<KV_FP8>(row_src(idx_lane), tile_lds0, buf, wave); };
 
     // per-lane LDS byte offsets of the operand reads (the tile layout above)
     const int sw_k = rsw(hl);
@@ -468,24 +491,12 @@ __device__ __forceinline__ void decode8p_body(
     if (first) {
       // Q rows landed (issued first; block b0's 9 DMAs of a gathering wave
       // and, with the look-ahead, the next index load stay in flight).
-      if (gathers) {
-        if (PREFETCH)
-          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      } else {
-        if (PREFETCH)
-          asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+      if (gathers)
+        wait_q_rows<PREFETCH, 9>();
+      else
+        wait_q_rows<PREFETCH, 0>();
       lds_barrier();
-      const uint32_t qt = lds_addr(s_tile) + kQOff + hq * 2048;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
-        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
-      }
+      load_q_frags(qf, lds_addr(s_tile) + kQOff + hq * 2048, kb0, kb1);
     }
     // FP8: block b0's row scales (stored by wave 0 at the top of the block loop).
     float sc_cur = (KV_FP8 && wave == 0 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
@@ -886,14 +897,7 @@ __device__ __forceinline__ void decode8h_body(
       const int row_idx = __shfl(idx_lane, KV_FP8 ? 16 * (wave & 3) + (lane >> 2) : 8 * wave + (lane >> 3));
       return gather_src<KV_FP8>(a, row_idx, valid_of(row_idx), lane);
     };
-    auto issue_gather = [&](int idx_lane, int buf) {
-      if (!KV_FP8) {
-        dma_octets(row_src(idx_lane), __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kTileBytes + wave * 1024));
-      } else if (gathers) {
-        dma_quartets(row_src(idx_lane),
-                     __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kCodeTileBytes + wave * 1024));
-      }
-    };
+    auto issue_gather = [&](int idx_lane, int buf) { gather_block8<KV_FP8>(row_src(idx_lane), tile_lds0, buf, wave); };
 
     // per-lane LDS byte offsets of the operand reads (the tile layout above)
     const int sw_k = rsw(hl);
@@ -928,24 +932,12 @@ __device__ __forceinline__ void decode8h_body(
     if (first) {
       // Q rows landed (issued first; block b0's 9 DMAs of a gathering wave
       // and, with the look-ahead, the next index load stay in flight).
-      if (gathers) {
-        if (PREFETCH)
-          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      } else {
-        if (PREFETCH)
-          asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+      if (gathers)
+        wait_q_rows<PREFETCH, 9>();
+      else
+        wait_q_rows<PREFETCH, 0>();
       lds_barrier();
-      const uint32_t qt = lds_addr(s_tile) + kQOffset + hq * 2048;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
-        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
-      }
+      load_q_frags(qf, lds_addr(s_tile) + kQOffset + hq * 2048, kb0, kb1);
     }
     // FP8: block b0's row scales (stored at the top of the block loop).
     float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
@@ -1341,24 +1333,9 @@ __device__ __forceinline__ void decode4t_body(
     if (first) {
       // Q rows landed (issued first; block b0's 18 DMAs (FP8: 9) and, with the
       // look-ahead, the next index load stay in flight).
-      if (KV_FP8) {
-        if (PREFETCH)
-          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      } else {
-        if (PREFETCH)
-          asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-      }
+      wait_q_rows<PREFETCH, KV_FP8 ? 9 : 18>();
       lds_barrier();
-      const uint32_t qt = lds_addr(s_tile) + kQOffset;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const uint32_t qp = qt + ((ks & 1) ? kb1 : kb0) + (ks >> 1) * 8192;
-        qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)qp;
-      }
+      load_q_frags(qf, lds_addr(s_tile) + kQOffset, kb0, kb1);
     }
     // FP8: block b0's row scales (stored at the top of the block loop).
     float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
