@@ -219,6 +219,32 @@ def test_fp8_pool_large_batch_every_token(s_q, S):
     H.assert_o_close(res["O"], O_fin, rel=2.0 ** -8)
 
 
+def test_fp8_pool_restart_in_one_part():
+    """The restart of a job whose late score exceeds the frame by far, on an FP8 pool in
+    one part a job (the 8-wave paired workgroups; split: the mixed launch): token 0 head
+    5 in block 7, token 129 head 50 in the second half of block 9, each planted row
+    quantised like the pool's."""
+    inp = W.make_inputs(130, 64, 32768, 640, seed=61, kv_dtype="fp8", sink=True)
+    q = inp.q
+    planted_rows = []
+    for t, head, slot in ((0, 5, 7 * 64 + 3), (129, 50, 9 * 64 + 44)):
+        row = int(inp.indices[t, slot])
+        x = (20.0 * q[t, head]).astype(np.float32)
+        scale = np.float32(np.abs(x).max() / np.float32(448.0))
+        inp.kv_codes[row] = W._e4m3_codes_of(np.clip(x / scale, -448.0, 448.0).astype(np.float32))
+        inp.kv_scale[row] = scale
+        planted_rows.append(row)
+    planted = H.tokens_gathering(inp.indices, planted_rows)
+    dev = H.DeviceInputs(inp)
+    O_ref, L_ref = oracle.attend(q.astype(np.float64), H.oracle_pool(inp), inp.indices, inp.n_pool, inp.scale)
+    O_fin = H.oracle_final(inp, O_ref, L_ref)
+    assert L_ref[0, 5] > 400 and L_ref[129, 50] > 400     # far beyond a frame near 10 (+64 slack)
+    for S, path in ((1, "direct"), (2, "split")):
+        res = H.run(dev, S, "f32", path)
+        H.assert_o_close(res["O"], O_fin)
+        assert H.assert_lse_close_planted(res["lse"], L_ref, planted) >= 2
+
+
 def test_score_far_beyond_the_frame_restarts_the_job():
     """A late slot whose log2-unit score exceeds the head's frame (fixed by the
     first block) by far more than the 64-unit slack: the kernel re-runs the job
