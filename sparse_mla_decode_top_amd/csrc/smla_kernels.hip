@@ -356,6 +356,31 @@ __device__ __forceinline__ void gather_block8(const uint8_t* src, uint32_t tile_
     dma_quartets(src, __builtin_amdgcn_readfirstlane(tile_lds0 + buf * kCodeTileBytes + wave * 1024));
 }
 
+// End of a pass, in every wave of the workgroup: posts the wave's largest
+// score, its denominator (the row sum of l_run, which l_run becomes) and its
+// overflow flag in its weight-exchange slot (floats [0, 16), [16, 32), int 32)
+// and returns whether any of the NW waves overflowed.  The two barriers order
+// the posts after every wave's last reads of the tiles and the weights, and
+// before the reads of the other waves' posts.
+template <int NW>
+__device__ __forceinline__ bool post_pass(bool overflow, float m_seen, float& l_run, float* pex_own,
+                                          const uint8_t* pex0, int slot_bytes, int hl, int G, int lane) {
+  const float l_w = rows_sum(l_run);
+  const bool ov = __any(overflow);
+  lds_barrier();
+  if (G == 0) {
+    pex_own[hl] = m_seen;
+    pex_own[16 + hl] = l_w;
+  }
+  if (lane == 0) ((int*)pex_own)[32] = ov ? 1 : 0;
+  lds_barrier();
+  l_run = l_w;
+  int any_ov = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) any_ov |= ((const int*)(pex0 + v * slot_bytes))[32];
+  return any_ov != 0;
+}
+
 // ---------------------------------------------------------------------------
 // The attention kernels' template flags.  KV_FP8: pool rows are e4m3 codes +
 // a row scale.  DIRECT: single-split job writing the final output (sink +
@@ -695,21 +720,9 @@ __device__ __forceinline__ void decode8p_body(
     // End of a pass: every wave posts its largest score, its denominator and
     // its overflow flag; returns whether any wave of the workgroup overflowed.
     auto end_exchange = [&](const bool overflow) __attribute__((always_inline)) -> bool {
-      const float l_w = rows_sum(l_run);
-      const bool ov = __any(overflow);
-      lds_barrier();            // every wave is past its last reads of the tiles and the weights
-      if (G == 0) {
-        pex_own[hl] = m_seen;
-        pex_own[16 + hl] = l_w;
-      }
-      if (lane == 0) ((int*)pex_own)[32] = ov ? 1 : 0;
-      lds_barrier();
-      l_run = l_w;
+      const bool any_ov = post_pass<kWaves8>(overflow, m_seen, l_run, pex_own, s_pex[0], 2048, hl, G, lane);
       l_par = pex_par[16 + hl];
-      int any_ov = 0;
-#pragma unroll
-      for (int v = 0; v < kWaves8; ++v) any_ov |= ((const int*)s_pex[v])[32];
-      return any_ov != 0;
+      return any_ov;
     };
 
     if (end_exchange(run_pass(true))) {
@@ -1114,22 +1127,10 @@ __device__ __forceinline__ void decode8h_body(
     // End of a pass: every wave posts its largest score, its denominator and
     // its overflow flag; returns whether any wave of the workgroup overflowed.
     auto end_exchange = [&](const bool overflow) __attribute__((always_inline)) -> bool {
-      const float l_w = rows_sum(l_run);
-      const bool ov = __any(overflow);
-      lds_barrier();            // every wave is past its last reads of the tiles and the weights
-      if (G == 0) {
-        pex_own[hl] = m_seen;
-        pex_own[16 + hl] = l_w;
-      }
-      if (lane == 0) ((int*)pex_own)[32] = ov ? 1 : 0;
-      lds_barrier();
-      l_run = l_w;
+      const bool any_ov = post_pass<kWaves8>(overflow, m_seen, l_run, pex_own, s_pex[0], 1024, hl, G, lane);
       // the same sum, in the same order, in each of the head tile's four waves
       l_tot = ((pex_of(0)[16 + hl] + pex_of(1)[16 + hl]) + pex_of(2)[16 + hl]) + pex_of(3)[16 + hl];
-      int any_ov = 0;
-#pragma unroll
-      for (int v = 0; v < kWaves8; ++v) any_ov |= ((const int*)s_pex[v])[32];
-      return any_ov != 0;
+      return any_ov;
     };
 
     if (end_exchange(run_pass(true))) {
@@ -1542,22 +1543,10 @@ __device__ __forceinline__ void decode4t_body(
     // End of a pass: every wave posts its largest score, its denominator and
     // its overflow flag; returns whether any wave of the workgroup overflowed.
     auto end_exchange = [&](const bool overflow) __attribute__((always_inline)) -> bool {
-      const float l_w = rows_sum(l_run);
-      const bool ov = __any(overflow);
-      lds_barrier();            // every wave is past its last reads of the tiles and the weights
-      if (G == 0) {
-        pex_own[hl] = m_seen;
-        pex_own[16 + hl] = l_w;
-      }
-      if (lane == 0) ((int*)pex_own)[32] = ov ? 1 : 0;
-      lds_barrier();
-      l_run = l_w;
+      const bool any_ov = post_pass<kWaves>(overflow, m_seen, l_run, pex_own, s_pex[0], 1024, hl, G, lane);
       // the same sum, in the same order, in each of the four waves
       l_tot = ((pex_of(0)[16 + hl] + pex_of(1)[16 + hl]) + pex_of(2)[16 + hl]) + pex_of(3)[16 + hl];
-      int any_ov = 0;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) any_ov |= ((const int*)s_pex[v])[32];
-      return any_ov != 0;
+      return any_ov;
     };
 
     if (end_exchange(run_pass(true))) {
