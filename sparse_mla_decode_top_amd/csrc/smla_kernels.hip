@@ -89,9 +89,11 @@ constexpr float kNoFrame = 3.0e38f;
 
 enum OutDtype { kOutBf16 = 0, kOutF32 = 1, kOutFp8 = 2 };
 
-// A zero pool row: the spread-out gather copies it for masked slots, so each of
-// its DMA instructions is issued by every lane, branch free.
-__device__ __attribute__((aligned(256))) uint8_t g_zero_row[1152];
+// Zeros: a pool row that the spread-out gather copies for masked slots, so
+// each of its DMA instructions is issued by every lane, branch free (its first
+// 1152 bytes), and an fp32 partial row that the combine loads for the split
+// slots of a chunk past the split count (all 2048).
+__device__ __attribute__((aligned(256))) uint8_t g_zero_row[2048];
 
 // ---------------------------------------------------------------------------
 // LDS tile layout ("octet-major").  A bf16 row is 72 chunks of 16 bytes (8
@@ -1670,7 +1672,9 @@ __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h,
   const int S = a.num_splits;
   const int64_t row = (int64_t)t * a.h_q + h;
   const int64_t ostride = (int64_t)a.s_q * a.h_q * 512;
-  const float* op = a.o_accum + row * 512 + col0 + (PARTS == 4 ? 2 : 4) * lane;
+  const int lane_off = col0 + (PARTS == 4 ? 2 : 4) * lane;     // the lane's columns within a row
+  const float* op = a.o_accum + row * 512 + lane_off;
+  const float* zp = (const float*)g_zero_row + lane_off;        // a zero row for the slots past S
   auto piece = [&](const float* src) -> f32x4 {
     if (PARTS == 4) {
       const f32x2 x = *(const f32x2*)src;
@@ -1679,13 +1683,14 @@ __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h,
     return *(const f32x4*)src;
   };
   const float ls = lane < S ? a.lse_accum[lane * (int64_t)a.s_q * a.h_q + row] : kNegInf;
-  // Split indices past S are clamped to S - 1 (an L1 hit on a row already
-  // requested) so the loads are unconditional and the LSE wait leaves them
-  // in flight; their terms are skipped below.
+  // Split slots past S load the zero row (a cache hit after the first
+  // workgroup, and no second request for a line already in flight) so the
+  // loads are unconditional and the LSE wait leaves them in flight; their
+  // terms are skipped below.
   f32x4 v[kMergeChunk][NV];
 #pragma unroll
   for (int c = 0; c < kMergeChunk; ++c) {
-    const float* src = op + min(c, S - 1) * ostride;
+    const float* src = c < S ? op + c * ostride : zp;
     v[c][0] = piece(src);
     if (NV == 2) v[c][NV - 1] = *(const f32x4*)(src + 256);
   }
@@ -1711,7 +1716,7 @@ __device__ __forceinline__ Merged merge_head(const CombineArgs& a, int t, int h,
   for (int s0 = kMergeChunk; s0 < S; s0 += kMergeChunk) {
 #pragma unroll
     for (int c = 0; c < kMergeChunk; ++c) {
-      const float* src = op + min(s0 + c, S - 1) * ostride;
+      const float* src = s0 + c < S ? op + (s0 + c) * ostride : zp;
       v[c][0] = piece(src);
       if (NV == 2) v[c][NV - 1] = *(const f32x4*)(src + 256);
     }
@@ -2109,7 +2114,10 @@ hipError_t noalloc_scratch(void** ptr) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.num_splits <= 4) return launch_combine_chunk<4>(a, stream);
+  if (a.num_splits == 5) return launch_combine_chunk<5>(a, stream);
+  if (a.num_splits == 6) return launch_combine_chunk<6>(a, stream);
   if (a.num_splits <= 8) return launch_combine_chunk<8>(a, stream);
+  if (a.num_splits <= 10) return launch_combine_chunk<10>(a, stream);
   if (a.num_splits <= 12) return launch_combine_chunk<12>(a, stream);
   return launch_combine_chunk<16>(a, stream);
 }
