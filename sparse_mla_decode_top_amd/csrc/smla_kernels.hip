@@ -1343,11 +1343,18 @@ __device__ __forceinline__ void decode4t_body(
     // FP8: block b0's row scales (stored at the top of the block loop).
     float sc_cur = (KV_FP8 && valid_cur) ? a.kv_scale[idx_cur] : 0.f;
 
+    // One block a job and a bf16 pool: a wave scores the rows it gathered
+    // itself, so QK^T waits for its own DMAs only, and the weight exchange's
+    // barrier orders the other waves' rows before the V^T reads.
+    constexpr bool kOwnRows = !PREFETCH && !KV_FP8;
     for (int b = job.b0; b < job.b1; ++b) {
       const int cur = (b - job.b0) & 1;
       wait_vmem_all();          // this wave's share of block b has landed
       if (KV_FP8 && wave == 0) s_scale[cur][lane] = sc_cur;
-      lds_barrier();            // ... and every wave's; block b-1 and its weights fully consumed
+      if (kOwnRows)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      else
+        lds_barrier();          // ... and every wave's; block b-1 and its weights fully consumed
       // slot s of the block is valid iff bit s is set (the same in every wave)
       const uint64_t vmask = __ballot(valid_cur);
       const uint32_t vquart = (uint32_t)(vmask >> (16 * wave));
@@ -1469,8 +1476,10 @@ __device__ __forceinline__ void decode4t_body(
       // ---- softmax of this wave's 16 slots (lane: slots 16 wave + 4G + i)
       constexpr int kAV = kAheadV < 2 * kCt ? kAheadV : 2 * kCt;
       bf16x8 vf[kAV + 1];
+      if (!kOwnRows) {
 #pragma unroll
-      for (int a0 = 0; a0 < kAV; ++a0) vf[a0] = vfrag(a0 % kCt, a0 / kCt);
+        for (int a0 = 0; a0 < kAV; ++a0) vf[a0] = vfrag(a0 % kCt, a0 / kCt);
+      }
       const uint32_t vbits = vquart >> (4 * G);
       f32x4 rsc = f32x4{0.f, 0.f, 0.f, 0.f};
       if (KV_FP8) rsc = *(const f32x4*)&s_scale[cur][16 * wave + 4 * G];
@@ -1511,7 +1520,11 @@ __device__ __forceinline__ void decode4t_body(
       }
       *(u32x2*)(s_pex[wave] + 8 * lane) = u32x2{ph[0], ph[1]};
       *(u32x2*)(s_pex[wave] + 512 + 8 * lane) = u32x2{pl[0], pl[1]};
-      lds_barrier();            // every wave's weights are in LDS
+      lds_barrier();            // every wave's weights (and, one block a job, rows) are in LDS
+      if (kOwnRows) {
+#pragma unroll
+        for (int a0 = 0; a0 < kAV; ++a0) vf[a0] = vfrag(a0 % kCt, a0 / kCt);
+      }
 
       // ---- O^T += V^T . P^T over the block: k-step kk takes the weights of
       // quarters 2kk (the first 4 k-indices of each lane's group) and 2kk + 1.
